@@ -1,0 +1,340 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a library routine, a closed form, an
+invariant of the mathematics, or brute force, so that a plausible slip in the
+oracle (a dropped gain, a wrong sign or pairing in RoPE, a transposed weight,
+a wrong GQA head mapping, a wrong slot formula, a misplaced residual) fails
+at least one of them.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from decode_step_06_amd.configs import TINY, ModelShape, Workload
+from decode_step_06_amd.inputs import gen_batch, gen_weights
+from oracle import decoder as od
+from oracle import kvcache as okv
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+# ---------------------------------------------------------------- bf16 rounding
+def test_round_bf16_matches_torch_conversion():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),       # float32 subnormals
+        (rng.standard_normal(2000) * 1e37).astype(np.float32),        # near overflow
+        np.array([0.0, -0.0, 1.0, -1.0, 3.3895314e38, np.float32(1.0 + 2 ** -8),
+                  np.float32(1.0 + 3 * 2 ** -8), np.float32(1.0 + 2 ** -8 + 2 ** -20),
+                  np.inf, -np.inf], dtype=np.float32),
+    ])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+    got = od.round_bf16(vals.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    assert np.isnan(od.round_bf16(np.array([np.nan])))[0]
+
+
+def test_round_bf16_ties_to_even():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties go to the even mantissa (1.0).
+    assert od.round_bf16(np.array([1.0 + 2 ** -8]))[0] == 1.0
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6: goes to 1 + 2^-6.
+    assert od.round_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rmsnorm_matches_torch_rms_norm():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((7, 96))
+    g = 1 + 0.1 * rng.standard_normal(96)
+    ref = F.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(od.rmsnorm(x, g, 1e-6), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_rmsnorm_closed_form_constant_row():
+    # A constant row c: mean(x^2) = c^2, so y = sign(c) * g / sqrt(1 + eps / c^2).
+    c, eps = -0.5, 1e-6
+    g = np.linspace(0.5, 1.5, 16)
+    y = od.rmsnorm(np.full((1, 16), c), g, eps)[0]
+    np.testing.assert_allclose(y, -g / np.sqrt(1 + eps / c ** 2), rtol=1e-15)
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(2).standard_normal((3, 2, 64))
+    ang = od.rope_angles(np.zeros(3), 64, 10000.0)
+    np.testing.assert_array_equal(od.apply_rope(x, ang), x)
+
+
+def test_rope_preserves_pair_norms_and_is_relative():
+    rng = np.random.default_rng(3)
+    d = 64
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((1, 1, d))
+    half = d // 2
+    for p in (1, 17, 1000):
+        r = od.apply_rope(q, od.rope_angles(np.array([p]), d, 1e4))
+        n0 = q[0, 0, :half] ** 2 + q[0, 0, half:] ** 2
+        n1 = r[0, 0, :half] ** 2 + r[0, 0, half:] ** 2
+        np.testing.assert_allclose(n1, n0, rtol=1e-12)
+
+    # <R_m q, R_n k> depends only on m - n.
+    def dot(m, n):
+        a = od.apply_rope(q, od.rope_angles(np.array([m]), d, 1e4))
+        b = od.apply_rope(k, od.rope_angles(np.array([n]), d, 1e4))
+        return float(np.sum(a * b))
+    np.testing.assert_allclose(dot(10, 3), dot(107, 100), rtol=1e-10)
+    np.testing.assert_allclose(dot(3, 10), dot(503, 510), rtol=1e-10)
+    assert abs(dot(10, 3) - dot(3, 10)) > 1e-6  # not symmetric: the rotation has a sign
+
+
+def test_rope_matches_transformers_llama_rotary():
+    from transformers import LlamaConfig
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding, apply_rotary_pos_emb
+    d, base = 64, 10000.0
+    cfg = LlamaConfig(hidden_size=4 * d, num_attention_heads=4, head_dim=d, rope_theta=base,
+                      max_position_embeddings=4096)
+    rot = LlamaRotaryEmbedding(cfg)
+    pos = np.array([0, 1, 5, 511, 2047])
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((len(pos), 3, d))
+    k = rng.standard_normal((len(pos), 2, d))
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]  # [1, heads, T, d]
+    tk = torch.from_numpy(k).permute(1, 0, 2)[None]
+    cos, sin = rot(tq, torch.from_numpy(pos)[None])
+    rq, rk = apply_rotary_pos_emb(tq, tk, cos.to(torch.float64), sin.to(torch.float64))
+    ang = od.rope_angles(pos, d, base)
+    # The library builds its table in float32; compare at float32 accuracy of the angles.
+    np.testing.assert_allclose(od.apply_rope(q, ang), rq[0].permute(1, 0, 2).numpy(), atol=3e-4)
+    np.testing.assert_allclose(od.apply_rope(k, ang), rk[0].permute(1, 0, 2).numpy(), atol=3e-4)
+
+
+# ---------------------------------------------------------------- attention
+def test_attention_single_token_returns_v():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((8, 32))
+    k = rng.standard_normal((1, 2, 32))
+    v = rng.standard_normal((1, 2, 32))
+    o, p = od.attention_row(q, k, v, 4)
+    for h in range(8):
+        np.testing.assert_array_equal(o[h], v[0, h // 4])
+    np.testing.assert_array_equal(p, np.ones((8, 1)))
+
+
+def test_attention_constant_v_and_probabilities_sum_to_one():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((4, 16)) * 3
+    k = rng.standard_normal((37, 1, 16))
+    v = np.full((37, 1, 16), 0.75)
+    o, p = od.attention_row(q, k, v, 4)
+    np.testing.assert_allclose(o, 0.75, rtol=1e-14)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-14)
+    assert (p > 0).all()
+
+
+def test_paged_attention_matches_sdpa_with_gqa_on_dense_copy():
+    """Brute force: the oracle reads K/V through shuffled block tables; the
+    reference gets a dense per-sequence copy built straight from (seq, pos)
+    and torch's SDPA with grouped KV heads (contiguous groups)."""
+    rng = np.random.default_rng(7)
+    nq, nkv, d, nb = 6, 2, 16, 24
+    lens = [1, 5, 16, 17, 40]
+    alloc = okv.BlockAllocator(nb, rng.permutation(nb), len(lens), 4)
+    for s, n in enumerate(lens):
+        alloc.alloc(s, n)
+    tables = alloc.table_rows()
+    cache = od.OracleKV(1, nb, nkv, d)
+    dense = {}
+    for s, n in enumerate(lens):
+        kk = rng.standard_normal((n, nkv, d))
+        vv = rng.standard_normal((n, nkv, d))
+        dense[s] = (kk, vv)
+        cache.write(0, [okv.slot_of(tables[s], p) for p in range(n)], kk, vv)
+    model = ModelShape("t", 1, 0, nq, nkv, d, 0, 0, False, "f32")
+    orc = od.Oracle(model, {"layers": [{}]})
+    q = rng.standard_normal((len(lens), nq, d))
+    row_seq = np.arange(len(lens))
+    row_pos = np.array(lens) - 1
+    o = orc.attend(0, cache, tables, q, row_seq, row_pos).reshape(len(lens), nq, d)
+    for s, n in enumerate(lens):
+        kk, vv = dense[s]
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q[s])[None, :, None, :],
+            torch.from_numpy(kk).permute(1, 0, 2)[None],
+            torch.from_numpy(vv).permute(1, 0, 2)[None], enable_gqa=True)
+        np.testing.assert_allclose(o[s], ref[0, :, 0, :].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_silu_matches_torch():
+    x = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(od.silu(x), F.silu(torch.from_numpy(x)).numpy(), rtol=1e-14, atol=1e-300)
+
+
+# ---------------------------------------------------------------- whole layer / step vs transformers
+def _hf_model(model, weights, n_layers, vocab):
+    from transformers import LlamaConfig, LlamaForCausalLM
+    cfg = LlamaConfig(vocab_size=vocab, hidden_size=model.hidden, intermediate_size=model.ffn,
+                      num_hidden_layers=n_layers, num_attention_heads=model.n_q_heads,
+                      num_key_value_heads=model.n_kv_heads, head_dim=model.head_dim,
+                      rms_norm_eps=model.rms_eps, rope_theta=model.rope_base, attention_bias=False,
+                      mlp_bias=False, tie_word_embeddings=True, max_position_embeddings=4096)
+    cfg._attn_implementation = "eager"
+    hf = LlamaForCausalLM(cfg).to(torch.float64).eval()
+    nq, nkv, d, Fd = model.n_q_heads, model.n_kv_heads, model.head_dim, model.ffn
+    with torch.no_grad():
+        for i, lw in enumerate(weights["layers"]):
+            L = hf.model.layers[i]
+            w = torch.from_numpy(lw["wqkv"].astype(np.float64))
+            L.self_attn.q_proj.weight.copy_(w[: nq * d])
+            L.self_attn.k_proj.weight.copy_(w[nq * d: (nq + nkv) * d])
+            L.self_attn.v_proj.weight.copy_(w[(nq + nkv) * d:])
+            L.self_attn.o_proj.weight.copy_(torch.from_numpy(lw["wo"].astype(np.float64)))
+            gu = torch.from_numpy(lw["wgu"].astype(np.float64))
+            L.mlp.gate_proj.weight.copy_(gu[:Fd])
+            L.mlp.up_proj.weight.copy_(gu[Fd:])
+            L.mlp.down_proj.weight.copy_(torch.from_numpy(lw["wdown"].astype(np.float64)))
+            L.input_layernorm.weight.copy_(torch.from_numpy(lw["attn_norm"].astype(np.float64)))
+            L.post_attention_layernorm.weight.copy_(torch.from_numpy(lw["mlp_norm"].astype(np.float64)))
+        hf.model.norm.weight.copy_(torch.from_numpy(weights["final_norm"].astype(np.float64)))
+        hf.model.embed_tokens.weight.copy_(torch.from_numpy(weights["embed"].astype(np.float64)))
+    return hf, cfg
+
+
+def test_step_matches_transformers_llama_with_supplied_cache():
+    """Two-layer tied-head model: each decode row against the library's LLaMA
+    forward with a DynamicCache holding that sequence's (already rotated) past
+    keys and values; a fresh prefill chunk against the library's causal
+    forward over the chunk."""
+    from transformers.cache_utils import DynamicCache
+    model = ModelShape("t2", 2, 64, 4, 2, 16, 96, 50, True, "f32")
+    weights = gen_weights(model, seed=11)
+    w = Workload("t2", model, 3, ctx_range=(2, 30), prefill_chunks=(9,), num_blocks=12)
+    b = gen_batch(w)
+    alloc = okv.BlockAllocator(b.num_blocks, b.free_order, b.n_seqs, 4)
+    for s, n in enumerate(b.seq_lens):
+        alloc.alloc(s, int(n))
+    tables = alloc.table_rows()
+    cache = od.OracleKV(model.n_layers, b.num_blocks, model.n_kv_heads, model.head_dim)
+    od.fill_past(cache, tables, b.past_seq, b.past_pos, b.past_k, b.past_v)
+    orc = od.Oracle(model, weights)
+    logits = orc.step(cache, tables, b.row_seq, b.row_pos, tokens=b.tokens)
+
+    hf, cfg = _hf_model(model, weights, model.n_layers, model.vocab)
+    with torch.no_grad():
+        for s in range(w.n_decode):
+            n_past = int(b.seq_lens[s]) - 1
+            sel = b.past_seq == s
+            order = np.argsort(b.past_pos[sel])
+            c = DynamicCache(config=cfg)
+            for layer in range(model.n_layers):
+                kk = torch.from_numpy(b.past_k[layer][sel][order].astype(np.float64)).permute(1, 0, 2)[None]
+                vv = torch.from_numpy(b.past_v[layer][sel][order].astype(np.float64)).permute(1, 0, 2)[None]
+                c.update(kk, vv, layer)
+            out = hf(input_ids=torch.tensor([[int(b.tokens[s])]]), position_ids=torch.tensor([[n_past]]),
+                     past_key_values=c, use_cache=True)
+            # the library's float32 cos/sin table limits agreement to ~1e-7 relative
+            np.testing.assert_allclose(logits[s], out.logits[0, 0].numpy(), rtol=2e-5, atol=2e-6)
+        rows = np.where(b.row_seq == w.n_decode)[0]
+        out = hf(input_ids=torch.from_numpy(b.tokens[rows].astype(np.int64))[None],
+                 position_ids=torch.from_numpy(b.row_pos[rows].astype(np.int64))[None])
+        np.testing.assert_allclose(logits[rows], out.logits[0].numpy(), rtol=2e-5, atol=2e-6)
+
+
+def test_single_layer_hidden_path_matches_transformers_decoder_layer():
+    """The tiny fp32 layer (no vocabulary: hidden in, hidden out) against one
+    library decoder layer with the same supplied cache."""
+    from transformers.cache_utils import DynamicCache
+    w = Workload("tiny_b4", TINY, 4, ctx_range=(5, 40), num_blocks=16)
+    weights = gen_weights(TINY, seed=0)
+    b = gen_batch(w)
+    alloc = okv.BlockAllocator(b.num_blocks, b.free_order, b.n_seqs, 4)
+    for s, n in enumerate(b.seq_lens):
+        alloc.alloc(s, int(n))
+    tables = alloc.table_rows()
+    cache = od.OracleKV(1, b.num_blocks, TINY.n_kv_heads, TINY.head_dim)
+    od.fill_past(cache, tables, b.past_seq, b.past_pos, b.past_k, b.past_v)
+    y = od.Oracle(TINY, weights).step(cache, tables, b.row_seq, b.row_pos, x=b.x)
+
+    fake = dict(weights, final_norm=np.ones(TINY.hidden), embed=np.zeros((2, TINY.hidden)))
+    hf, cfg = _hf_model(TINY, fake, 1, 2)
+    layer = hf.model.layers[0]
+    with torch.no_grad():
+        for s in range(4):
+            sel = b.past_seq == s
+            order = np.argsort(b.past_pos[sel])
+            c = DynamicCache(config=cfg)
+            kk = torch.from_numpy(b.past_k[0][sel][order].astype(np.float64)).permute(1, 0, 2)[None]
+            vv = torch.from_numpy(b.past_v[0][sel][order].astype(np.float64)).permute(1, 0, 2)[None]
+            c.update(kk, vv, 0)
+            pos = torch.tensor([[int(b.row_pos[s])]])
+            hs = torch.from_numpy(b.x[s].astype(np.float64))[None, None]
+            pe = hf.model.rotary_emb(hs, pos)
+            pe = (pe[0].to(torch.float64), pe[1].to(torch.float64))
+            out = layer(hs, attention_mask=None, position_ids=pos, past_key_values=c, use_cache=True,
+                        cache_position=pos[0], position_embeddings=pe)
+            out = out[0] if isinstance(out, tuple) else out
+            # the library's float32 cos/sin table limits agreement to ~1e-6
+            np.testing.assert_allclose(y[s], out[0, 0].numpy(), rtol=2e-5, atol=2e-5)
+
+
+# ---------------------------------------------------------------- nano split, bf16 storage points
+def _small_bf16_case():
+    model = ModelShape("b", 2, 64, 4, 2, 16, 96, 0, False, "bf16")
+    weights = gen_weights(model, seed=3)
+    w = Workload("b", model, 5, ctx_range=(3, 50), prefill_chunks=(11, 7), num_blocks=40)
+    b = gen_batch(w)
+    alloc = okv.BlockAllocator(b.num_blocks, b.free_order, b.n_seqs, 8)
+    for s, n in enumerate(b.seq_lens):
+        alloc.alloc(s, int(n))
+    return model, weights, b, alloc.table_rows()
+
+
+def _run(model, weights, b, tables, **kw):
+    cache = od.OracleKV(model.n_layers, b.num_blocks, model.n_kv_heads, model.head_dim)
+    od.fill_past(cache, tables, b.past_seq, b.past_pos, b.past_k, b.past_v)
+    return od.Oracle(model, weights).step(cache, tables, b.row_seq, b.row_pos, x=b.x, **kw)
+
+
+def test_nano_split_equals_unsplit():
+    # A split inside a prefill chunk: rows after the split read keys written
+    # by rows before it.
+    model, weights, b, tables = _small_bf16_case()
+    full = _run(model, weights, b, tables)
+    for splits in ([8, 15], [5, 6, 12], [1] * 23):
+        np.testing.assert_allclose(_run(model, weights, b, tables, nano_splits=splits), full,
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_emulation_rounds_only_at_storage_points():
+    model, weights, b, tables = _small_bf16_case()
+    orc = od.Oracle(model, weights)
+    x = b.x.astype(np.float64)
+    q, k, v = orc.qkv(0, x, b.row_pos)
+    for a in (q, k, v):
+        np.testing.assert_array_equal(od.round_bf16(a), a)
+    wide = od.Oracle(model, weights, emulate_bf16=False)
+    qw, _, _ = wide.qkv(0, x, b.row_pos)
+    # two roundings (normalised input, rotated q) of relative size <= 2^-8 each
+    rel_l2 = np.linalg.norm(q - qw) / np.linalg.norm(qw)
+    assert 1e-4 < rel_l2 < 2 * 2.0 ** -8
+    assert (q != qw).mean() > 0.9                 # and it did round
+
+
+def test_padding_row_changes_nothing_and_writes_nothing():
+    model, weights, b, tables = _small_bf16_case()
+    full = _run(model, weights, b, tables)
+    seq = np.concatenate([b.row_seq, [-1]]).astype(np.int32)
+    pos = np.concatenate([b.row_pos, [0]]).astype(np.int32)
+    x = np.concatenate([b.x, np.ones((1, model.hidden), np.float32)])
+    cache = od.OracleKV(model.n_layers, b.num_blocks, model.n_kv_heads, model.head_dim)
+    od.fill_past(cache, tables, b.past_seq, b.past_pos, b.past_k, b.past_v)
+    before = [c.copy() for c in cache.k]
+    y = od.Oracle(model, weights).step(cache, tables, seq, pos, x=x)
+    np.testing.assert_allclose(y[:-1], full, rtol=1e-12, atol=1e-12)
+    # only the batch's own slots changed
+    for layer in range(model.n_layers):
+        changed = ~((cache.k[layer] == before[layer]) | (np.isnan(cache.k[layer]) & np.isnan(before[layer])))
+        rows = np.unique(np.where(changed)[0])
+        expect = sorted(okv.slot_map(tables, b.row_seq, b.row_pos))
+        assert sorted(rows.tolist()) == expect
