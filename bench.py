@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched GQA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line.  The timed workload is the Qwen2.5-0.5B-shaped 24-layer
+decode step at batch 32, context 512 (KV blocks of 16, tied LM head), bf16,
+replayed as one captured hipGraph per step: ``value`` is decode tokens/s
+(batch x steps / seconds) with every input already resident in HBM.
+
+Also reported (each kernel timed live with HIP events on the stream it runs
+on, behind a queued busy-wait kernel so host launch gaps do not count):
+  * ``roofline``: the step's dominant kernel against the HBM peak;
+  * ``kernels``: per-kernel achieved GB/s or TFLOP/s for the step's kernels;
+  * ``dense_batch``: the LLaMA-2-70B-shaped layer at the 2048-token dense
+    batch -- decode attention (512 rows x context 1024) against the HBM peak,
+    the four projections against the bf16 MFMA peak, and the layer step with
+    and without the nano-batch overlap;
+  * ``cpu_baseline``: the CPU oracle timed on the host (bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from decode_step_06_amd import ns  # noqa: E402
+from decode_step_06_amd import roofline as rf  # noqa: E402
+from decode_step_06_amd.configs import WORKLOADS  # noqa: E402
+from decode_step_06_amd.inputs import gen_batch, gen_weights  # noqa: E402
+from decode_step_06_amd.runner import (DeviceWeights, alloc_sequences, blocks_for, create_engine,  # noqa: E402
+                                       fill_past, fill_past_random_on_device)
+
+WORKLOAD = "qwen05b_b32_ctx512"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def busy(stream, ms=30):
+    """Queue a bounded busy-wait kernel so the launches after it are all
+    enqueued before the GPU reaches them."""
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(ms * 1e-3 * 2.0e9))
+
+
+def time_launches(fn, n, stream, reps=3):
+    """Average device time per launch of fn(i) over n back-to-back launches
+    (HIP events on `stream`); median over reps."""
+    out = []
+    for _ in range(reps):
+        busy(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) / n * 1e-3)
+    return statistics.median(out)
+
+
+# ---------------------------------------------------------------- the timed step
+def setup_step(wname):
+    w = WORKLOADS[wname]
+    shape = w.model
+    log(f"[bench] generating {wname} inputs (seeded)")
+    weights = gen_weights(shape, seed=w.seeds["weights"])
+    b = gen_batch(w)
+    maxb = blocks_for(b.seq_lens)
+    h = create_engine(shape, DeviceWeights.from_numpy(shape, weights), b.num_blocks, b.n_seqs, maxb, b.n_rows,
+                      b.free_order, None)
+    alloc_sequences(h, b.seq_lens)
+    fill_past(h, b.past_seq, b.past_pos, b.past_k, b.past_v)
+    return w, weights, b, h, maxb
+
+
+def run_step_bench(h, b, steps, warmup, warm_seconds, stream):
+    shape = h.shape
+    out = torch.empty((b.n_rows, shape.vocab or shape.hidden), device="cuda")
+    nb = ns.Batch(b.row_seq, b.row_pos, b.tokens)
+    g = ns.ns_graph_capture(h.eng, b.n_rows, out.data_ptr(), stream)
+    try:
+        # eager step once (launch count), then sustained warm-up for the clock
+        ns.ns_decode_step(h.eng, nb, out.data_ptr(), stream)
+        stream.synchronize()
+        launches = ns.ns_engine_last_launches(h.eng)
+        t_end = time.time() + warm_seconds
+        while time.time() < t_end:
+            for _ in range(20):
+                ns.ns_graph_replay(g, nb, stream)
+            stream.synchronize()
+        for _ in range(warmup):
+            ns.ns_graph_replay(g, nb, stream)
+        stream.synchronize()
+        runs = []
+        for _ in range(2):  # timed twice; disagreement over 15% is flagged
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                ns.ns_graph_replay(g, nb, stream)
+            stream.synchronize()
+            torch.cuda.synchronize()
+            runs.append((time.perf_counter() - t0) / steps)
+        # eager steps for the fixed per-step cost (eager - graph)
+        for _ in range(3):
+            ns.ns_decode_step(h.eng, nb, out.data_ptr(), stream)
+        stream.synchronize()
+        t0 = time.perf_counter()
+        n_eager = max(5, steps // 4)
+        for _ in range(n_eager):
+            ns.ns_decode_step(h.eng, nb, out.data_ptr(), stream)
+        stream.synchronize()
+        eager = (time.perf_counter() - t0) / n_eager
+    finally:
+        ns.ns_graph_destroy(g)
+    return runs, eager, launches
+
+
+# ---------------------------------------------------------------- kernels of the step
+def step_kernels(h, b, stream, reps=5):
+    """Per-kernel device time inside the real step: an eager serial step with
+    the engine's profiling on records a HIP event after every launch on the
+    step's stream (a busy-wait kernel queued first keeps host launch gaps out
+    of the timing).  Returns per class: launches per step, mean us per
+    launch, algorithmic bytes (and FLOPs) per launch."""
+    s = h.shape
+    L, H, F, V, T = s.n_layers, s.hidden, s.ffn, s.vocab, b.n_rows
+    DQ = s.n_q_heads * s.head_dim
+    out = torch.empty((T, V or H), device="cuda")
+    nb = ns.Batch(b.row_seq, b.row_pos, b.tokens)
+    ns.ns_engine_profile(h.eng, True)
+    per = {}
+    try:
+        for _ in range(reps):
+            busy(stream)
+            ns.ns_decode_step(h.eng, nb, out.data_ptr(), stream)
+            kinds, us = ns.ns_engine_profile_read(h.eng)
+            for k, u in zip(kinds, us):
+                per.setdefault(k, []).append(u)
+    finally:
+        ns.ns_engine_profile(h.eng, False)
+    ctx = (b.row_pos + 1).astype(np.int64)
+    work = {  # algorithmic bytes (and FLOPs) per launch
+        "qkv_proj": (rf.gemm_bytes(T, s.qkv_dim, H, 2, "store"), rf.gemm_flops(T, s.qkv_dim, H)),
+        "o_proj": (rf.gemm_bytes(T, H, DQ, 2, "resid"), rf.gemm_flops(T, H, DQ)),
+        "gate_up_proj": (rf.gemm_bytes(T, F, H, 2, "silu"), rf.gemm_flops(T, F, H, True)),
+        "down_proj": (rf.gemm_bytes(T, H, F, 2, "resid"), rf.gemm_flops(T, H, F)),
+        "lm_head": (rf.gemm_bytes(T, V, H, 2, "store"), rf.gemm_flops(T, V, H)),
+        "attention": (int(rf.attention_bytes(s, ctx)), int(rf.attention_flops(s, ctx))),
+    }
+    res = {}
+    for k, us in per.items():
+        n = len(us) // reps
+        mean = float(np.mean(us))
+        r = {"launches_per_step": n, "us_per_launch": mean, "us_per_step": mean * n}
+        if k in work:
+            nbytes, fl = work[k]
+            r.update(bytes_per_launch=nbytes, gbs=nbytes / (mean * 1e-6) / 1e9,
+                     tflops=fl / (mean * 1e-6) / 1e12)
+        res[k] = r
+    return res
+
+
+# ---------------------------------------------------------------- the dense-batch layer
+def dense_batch(stream, steps=10):
+    """LLaMA-2-70B-shaped layer at the 2048-token dense batch (device-drawn
+    weights and cache): attention and projection roofline fractions, and the
+    layer step serial vs nano-batch overlapped (graph replays)."""
+    w = WORKLOADS["llama70b_layer_t2048"]
+    s = w.model
+    log("[bench] dense batch: llama70b layer, 2048 rows")
+    b = gen_batch(w, with_past=False)
+    maxb = blocks_for(b.seq_lens)
+    dw = DeviceWeights.random_on_device(s, seed=0)
+    h = create_engine(s, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, None, nan_poison=False)
+    res = {}
+    try:
+        alloc_sequences(h, b.seq_lens)
+        fill_past_random_on_device(h, b.past_seq, b.past_pos, seed=4)
+        H, F, DQ, T = s.hidden, s.ffn, s.n_q_heads * s.head_dim, b.n_rows
+        lw = dw.t["layers"][0]
+        A = torch.randn((T, max(H, F, DQ)), device="cuda").to(torch.bfloat16)
+        C32 = torch.empty((T, max(s.qkv_dim, H)), device="cuda")
+        Cb = torch.empty((T, F), device="cuda", dtype=torch.bfloat16)
+        gem = {}
+        for name, epi, N, K, Bw, C in (("qkv_proj", ns.NS_EPI_STORE, s.qkv_dim, H, lw["wqkv"], C32),
+                                       ("o_proj", ns.NS_EPI_RESID, H, DQ, lw["wo"], C32),
+                                       ("gate_up_proj", ns.NS_EPI_SILU, F, H, lw["wgu"], Cb),
+                                       ("down_proj", ns.NS_EPI_RESID, H, F, lw["wdown"], C32)):
+            Ak = A[:, :K].contiguous()
+            t = time_launches(lambda i: ns.ns_op_gemm(ns.NS_BF16, epi, T, N, K, Ak.data_ptr(), Bw.data_ptr(),
+                                                      C.data_ptr(), stream), 5, stream)
+            fl = rf.gemm_flops(T, N, K, epi == ns.NS_EPI_SILU)
+            gem[name] = dict(us=t * 1e6, tflops=fl / t / 1e12, frac=fl / t / 1e12 / rf.BF16_PEAK_TFLOPS)
+        tot_fl = sum(rf.gemm_flops(T, N, K, sw) for N, K, sw in ((s.qkv_dim, H, False), (H, DQ, False),
+                                                                 (F, H, True), (H, F, False)))
+        tot_t = sum(v["us"] for v in gem.values()) * 1e-6
+        res["gemm"] = gem
+        res["gemm_tflops"] = tot_fl / tot_t / 1e12
+        res["gemm_mfma_frac"] = res["gemm_tflops"] / rf.BF16_PEAK_TFLOPS
+        # decode attention: the 512 decode rows at context 1024
+        nd = w.n_decode
+        rowb = torch.arange(nd, dtype=torch.int32, device="cuda")
+        pos = torch.from_numpy(b.row_pos[:nd].astype(np.int32)).cuda()
+        bt = torch.from_numpy(ns.ns_kv_block_table(h.kv, b.n_seqs, maxb)[:nd].copy()).cuda()
+        q_att = torch.randn((nd, s.n_kv_heads, s.head_dim // 8, s.group, 8), device="cuda").to(torch.bfloat16)
+        o = torch.empty((nd, DQ), device="cuda", dtype=torch.bfloat16)
+        wsb = ns.ns_op_attention_ws_bytes(h.desc, nd, maxb)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        t = time_launches(lambda i: ns.ns_op_attention(h.desc, nd, q_att.data_ptr(), h.kv_mem.data_ptr(),
+                                                       h.num_blocks, rowb.data_ptr(), pos.data_ptr(), bt.data_ptr(),
+                                                       maxb, o.data_ptr(), ws.data_ptr(), wsb, 0, stream), 5, stream)
+        ab = rf.attention_bytes(s, [w.decode_ctx] * nd)
+        res["attention"] = dict(us=t * 1e6, gbs=ab / t / 1e9, hbm_frac=ab / t / 1e9 / rf.HBM_PEAK_GBS, bytes=ab)
+        # the whole layer step: serial vs nano-batched with overlap
+        x = torch.randn((T, H), device="cuda")
+        out = torch.empty((T, H), device="cuda")
+        nb = ns.Batch(b.row_seq, b.row_pos, None, x)
+        for label, sched in (("serial", ns.make_sched()),
+                             ("nano_overlap", ns.make_sched(nano_rows=w.nano_splits,
+                                                            qkv_rows=(512,) * w.qkv_splits, overlap=True))):
+            ns.ns_engine_set_sched(h.eng, sched)
+            g = ns.ns_graph_capture(h.eng, T, out.data_ptr(), stream)
+            try:
+                for _ in range(3):
+                    ns.ns_graph_replay(g, nb, stream)
+                stream.synchronize()
+                t = time_launches(lambda i: ns.ns_graph_replay(g, nb, stream), steps, stream)
+            finally:
+                ns.ns_graph_destroy(g)
+            res[f"layer_step_ms_{label}"] = t * 1e3
+        res["layer_tokens_per_s_nano"] = T / (res["layer_step_ms_nano_overlap"] * 1e-3)
+    finally:
+        h.destroy()
+        torch.cuda.synchronize()
+    return res
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_baseline(w, weights, b, maxb, n_steps=3):
+    from oracle import decoder as od
+    from oracle import kvcache as okv
+    log("[bench] cpu_baseline: timing the oracle")
+    alloc = okv.BlockAllocator(b.num_blocks, b.free_order, b.n_seqs, maxb)
+    for s, n in enumerate(b.seq_lens):
+        alloc.alloc(s, int(n))
+    tables = alloc.table_rows()
+    cache = od.OracleKV(w.model.n_layers, b.num_blocks, w.model.n_kv_heads, w.model.head_dim)
+    od.fill_past(cache, tables, b.past_seq, b.past_pos, b.past_k, b.past_v)
+    orc = od.Oracle(w.model, weights)
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        orc.step(cache, tables, b.row_seq, b.row_pos, tokens=b.tokens)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": b.n_rows * n_steps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_steps} full steps of {w.name} (24 layers, batch {b.n_rows}, float64 numpy), "
+                      f"{dt:.1f} s", "threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _jsonable(o):
+    if isinstance(o, (np.integer,)):
+        return int(o)
+    if isinstance(o, (np.floating,)):
+        return float(o)
+    raise TypeError(type(o))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warm-seconds", type=float, default=3.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the decode step is built and measured on a single MI355X "
+              "(no sharding, no collectives); --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ns.lib()
+    stream = torch.cuda.Stream()
+    w, weights, b, h, maxb = setup_step(WORKLOAD)
+    try:
+        runs, eager, launches = run_step_bench(h, b, args.steps, args.warmup, args.warm_seconds, stream)
+        kern = step_kernels(h, b, stream)
+    finally:
+        h.destroy()
+    step_s = runs[-1]
+    value = b.n_rows / step_s
+    ctx = (b.row_pos + 1).tolist()
+    sb = rf.step_bytes(w.model, ctx)
+    # dominant kernel: the class with the largest share of the step's device time
+    dom = max((k for k in kern if "gbs" in kern[k]), key=lambda k: kern[k]["us_per_step"])
+    dk = kern[dom]
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(dk["gbs"], 1), "peak": rf.HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(dk["gbs"] / rf.HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": dk["bytes_per_launch"], "avg_launch_us": round(dk["us_per_launch"], 3),
+            "share_of_step": round(dk["us_per_step"] / sum(v["us_per_step"] for v in kern.values()), 3)}
+    result = {
+        "metric": "decode tokens/s @1 GPU; attn HBM GB/s and GEMM MFMA % of peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and cached context)",
+        "config": {"workload": w.name, "batch": b.n_rows, "context": int(w.decode_ctx), "layers": w.model.n_layers,
+                   "kv_block": 16, "mode": "hipGraph replay", "parallelism": "single GPU"},
+        "roofline": roof,
+        "step": {"runs_ms": [round(r * 1e3, 4) for r in runs],
+                 "runs_disagree_over_15pct": bool(max(runs) > 1.15 * min(runs)),
+                 "eager_ms": round(eager * 1e3, 4), "fixed_cost_ms": round((eager - step_s) * 1e3, 4),
+                 "kernels_per_step": launches, "algorithmic_bytes": sb,
+                 "hbm_floor_ms": round(rf.floor_seconds(sb) * 1e3, 4),
+                 "step_hbm_frac": round(sb / step_s / 1e9 / rf.HBM_PEAK_GBS, 4)},
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kern.items()},
+    }
+    if not args.no_dense:
+        try:
+            result["dense_batch"] = json.loads(json.dumps(dense_batch(stream), default=_jsonable))
+        except Exception as e:  # report, do not hide
+            result["dense_batch"] = {"error": repr(e)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, weights, b, maxb)
+    print(json.dumps(result, default=_jsonable), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,711 @@
+// Engine of the decode step: workspace plan, step metadata, the kernel
+// sequence of one step (shared by eager execution and graph capture), the
+// nano-batch schedule over two streams, and graph capture / replay.
+//
+// Sources: page "gpu-waiting-not-working" (nanoserve notes) -- changes table
+// (one pinned host-to-device copy of the step metadata; RoPE cos/sin built
+// once per step) and section "Where this leaves nanoserve" (capture the
+// decode step once and replay it); page "NanoFlow: LLM Serving Is Compute
+// Bound, and Your GPU Is Half Idle" -- section "Nano-batching: manufacturing
+// independence" (split rows into nano-batches so projections of one overlap
+// attention of another) and its implementation note (events order the
+// nano-ops across streams); page "The chef who calls out every order: SMs,
+// CUDA streams and CUDA graphs" -- streams as in-order queues that overlap
+// each other, and one graph per batch size.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "ns_internal.h"
+#include "ns_kernels.h"
+
+namespace ns {
+int check_desc(const ns_model_desc* d);
+size_t kv_layer_bytes(const ns_model_desc* d, int32_t num_blocks);
+}  // namespace ns
+
+#define HIP_TRY(expr)                                                                                  \
+  do {                                                                                                 \
+    hipError_t _e = (expr);                                                                            \
+    if (_e != hipSuccess) NS_FAIL(NS_EHIP, "%s failed: %s", #expr, hipGetErrorString(_e));             \
+  } while (0)
+
+namespace {
+
+constexpr int kAttnTargetWaves = 2048;  // attention wavefronts to aim for (8 per CU)
+constexpr int kMaxParts = 4;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int elem_size(int32_t dtype) { return dtype == NS_BF16 ? 2 : 4; }
+
+// Context partition size (tokens, a multiple of 64) and partition count for
+// a batch of n_rows rows when sequences hold at most cap_tokens tokens.  It
+// depends only on the whole batch's row count, so a nano-batched step and an
+// unsplit step, eager and captured, partition identically.
+void attn_partition(int n_rows, int nkv, int cap_tokens, int* part_tokens, int* n_parts) {
+  const int chunks = std::max(1, (cap_tokens + 63) / 64);
+  const long items = std::max(1L, (long)n_rows * nkv);
+  int want = (int)std::max(1L, (kAttnTargetWaves + items - 1) / items);
+  want = std::min(want, chunks);
+  const int per = (chunks + want - 1) / want;
+  *part_tokens = 64 * per;
+  *n_parts = (chunks + per - 1) / per;
+}
+
+struct Plan {
+  size_t x, h, qkv, q_att, o, act, cosb, sinb, meta, part_acc, part_ml, total;
+  size_t meta_ints;  // int32 entries of the metadata block
+};
+
+Plan make_plan(const ns_model_desc* d, int T, int maxb) {
+  Plan p{};
+  const size_t es = elem_size(d->dtype);
+  const int G = d->n_q_heads / d->n_kv_heads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  p.x = take((size_t)T * d->hidden * 4);
+  p.h = take((size_t)T * d->hidden * es);
+  p.qkv = take((size_t)T * (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim * 4);
+  p.q_att = take((size_t)T * d->n_q_heads * d->head_dim * es);
+  p.o = take((size_t)T * d->n_q_heads * d->head_dim * es);
+  p.act = take((size_t)T * d->ffn * es);
+  p.cosb = take((size_t)T * d->head_dim / 2 * 4);
+  p.sinb = take((size_t)T * d->head_dim / 2 * 4);
+  p.meta_ints = 4 * (size_t)T + (size_t)T * maxb;
+  p.meta = take(p.meta_ints * 4);
+  long items = 0;
+  for (int n = 1; n <= T; ++n) {
+    int P, np;
+    attn_partition(n, d->n_kv_heads, maxb * NS_BLOCK_SIZE, &P, &np);
+    if (np > 1) items = std::max(items, (long)n * d->n_kv_heads * np);
+  }
+  p.part_acc = take((size_t)items * G * d->head_dim * 4);
+  p.part_ml = take((size_t)items * G * 2 * 4);
+  p.total = off;
+  return p;
+}
+
+// Row ranges of a split: up to 4 consecutive parts; the last takes the rest.
+std::vector<std::pair<int, int>> row_parts(int n_tok, int n, const int32_t* rows) {
+  std::vector<std::pair<int, int>> out;
+  if (n <= 1) {
+    out.push_back({0, n_tok});
+    return out;
+  }
+  int r = 0;
+  for (int i = 0; i < n && r < n_tok; ++i) {
+    int len = (i == n - 1) ? n_tok - r : std::min(std::max(rows[i], 0), n_tok - r);
+    if (len <= 0) continue;
+    out.push_back({r, r + len});
+    r += len;
+  }
+  if (r < n_tok) {
+    if (out.empty()) out.push_back({r, n_tok});
+    else out.back().second = n_tok;
+  }
+  return out;
+}
+
+}  // namespace
+
+struct ns_engine {
+  ns_model_desc d{};
+  int es = 2;
+  int G = 1;
+  std::vector<const void*> attn_norm, wqkv, wo, mlp_norm, wgu, wdown;
+  const void* final_norm = nullptr;
+  const void* embed = nullptr;
+  const void* lm_head = nullptr;
+  ns_kv* kv = nullptr;
+  char* kv_dev = nullptr;
+  size_t kv_layer = 0;
+  int num_blocks = 0;
+  int max_tokens = 0;
+  int maxb = 0;
+  char* ws = nullptr;
+  Plan plan{};
+  ns_sched sched{};
+  hipStream_t s2 = nullptr;
+  hipEvent_t ev_qkv[kMaxParts] = {};
+  hipEvent_t ev_att[kMaxParts] = {};
+  int32_t* staging[2] = {nullptr, nullptr};
+  hipEvent_t staging_ev[2] = {};
+  bool staging_used[2] = {false, false};
+  int staging_next = 0;
+  int last_launches = 0;
+  // profiling: an event after every launch of an eager serial step
+  bool prof = false;
+  hipEvent_t prof_start = nullptr;
+  std::vector<hipEvent_t> prof_ev;
+  std::vector<int32_t> prof_kind;
+  int prof_n = 0;
+
+  float* x() const { return (float*)(ws + plan.x); }
+  void* h() const { return ws + plan.h; }
+  float* qkv() const { return (float*)(ws + plan.qkv); }
+  void* q_att() const { return ws + plan.q_att; }
+  void* o() const { return ws + plan.o; }
+  void* act() const { return ws + plan.act; }
+  float* cosb() const { return (float*)(ws + plan.cosb); }
+  float* sinb() const { return (float*)(ws + plan.sinb); }
+  int32_t* meta() const { return (int32_t*)(ws + plan.meta); }
+  // metadata block: tokens[T] | row_bseq[T] | pos[T] | slot[T] | btab[T][maxb]
+  int32_t* m_tok() const { return meta(); }
+  int32_t* m_rowb() const { return meta() + max_tokens; }
+  int32_t* m_pos() const { return meta() + 2 * max_tokens; }
+  int32_t* m_slot() const { return meta() + 3 * max_tokens; }
+  int32_t* m_btab() const { return meta() + 4 * max_tokens; }
+  char* k_layer(int l) const { return kv_dev + (size_t)l * kv_layer; }
+  char* v_layer(int l) const { return kv_dev + (size_t)l * kv_layer + kv_layer / 2; }
+};
+
+struct ns_graph {
+  ns_engine* e = nullptr;
+  int bucket = 0;
+  void* out = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+int check_sched(const ns_sched* s) {
+  if (!s) return NS_OK;
+  if (s->n_nano < 0 || s->n_nano > kMaxParts || s->n_qkv < 0 || s->n_qkv > kMaxParts)
+    NS_FAIL(NS_EINVAL, "at most %d nano-batches", kMaxParts);
+  if (s->attn_wg_cap < 0) NS_FAIL(NS_EINVAL, "attn_wg_cap must be >= 0");
+  if (s->cu_mask_frac < 0.f || s->cu_mask_frac > 1.f) NS_FAIL(NS_EINVAL, "cu_mask_frac must be in [0, 1]");
+  return NS_OK;
+}
+
+// Validate a batch against the engine and the KV manager; no side effects.
+int check_batch(const ns_engine* e, const ns_batch* b, int max_rows) {
+  if (!b) NS_FAIL(NS_EINVAL, "null batch");
+  if (b->n_tok <= 0) NS_FAIL(NS_EINVAL, "batch must have at least one row");
+  if (b->n_tok > max_rows) NS_FAIL(NS_ESHAPE, "batch of %d rows exceeds %d", b->n_tok, max_rows);
+  if (!b->seq || !b->pos) NS_FAIL(NS_EINVAL, "null seq/pos arrays");
+  if (e->d.vocab > 0 && !b->token_ids) NS_FAIL(NS_EINVAL, "model has a vocabulary: token_ids required");
+  if (e->d.vocab == 0 && !b->hidden_in) NS_FAIL(NS_EINVAL, "model has no vocabulary: hidden_in required");
+  const ns_kv* kv = e->kv;
+  std::vector<int32_t> last_pos(kv->max_seqs, -1);
+  for (int i = 0; i < b->n_tok; ++i) {
+    const int32_t s = b->seq[i], p = b->pos[i];
+    if (s == -1) continue;
+    if (s < 0 || s >= kv->max_seqs) NS_FAIL(NS_EINVAL, "row %d: sequence %d out of range", i, s);
+    if (p < 0 || (int64_t)p >= (int64_t)kv->tables[s].size() * NS_BLOCK_SIZE)
+      NS_FAIL(NS_ESHAPE, "row %d: position %d not covered by sequence %d's blocks", i, p, s);
+    if ((int)kv->tables[s].size() > e->maxb)
+      NS_FAIL(NS_ESHAPE, "sequence %d holds more blocks than the engine's table rows", s);
+    if (p <= last_pos[s]) NS_FAIL(NS_EINVAL, "rows of sequence %d must have increasing positions", s);
+    last_pos[s] = p;
+    if (e->d.vocab > 0 && (b->token_ids[i] < 0 || b->token_ids[i] >= e->d.vocab))
+      NS_FAIL(NS_EINVAL, "row %d: token id %d out of range", i, b->token_ids[i]);
+  }
+  return NS_OK;
+}
+
+// Pack the step metadata for `rows` rows (rows >= n_tok are padding) into
+// pinned staging and copy it to the device with one transfer.
+int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
+  const int k = e->staging_next;
+  e->staging_next ^= 1;
+  if (e->staging_used[k]) HIP_TRY(hipEventSynchronize(e->staging_ev[k]));
+  int32_t* m = e->staging[k];
+  const int T = e->max_tokens;
+  int32_t* tok = m;
+  int32_t* rowb = m + T;
+  int32_t* pos = m + 2 * T;
+  int32_t* slot = m + 3 * T;
+  int32_t* btab = m + 4 * T;
+  std::vector<int32_t> bseq_of(e->kv->max_seqs, -1);
+  int n_bseq = 0;
+  for (int i = 0; i < rows; ++i) {
+    const bool real = i < b->n_tok && b->seq[i] != -1;
+    tok[i] = (i < b->n_tok && b->token_ids) ? b->token_ids[i] : 0;
+    pos[i] = real ? b->pos[i] : 0;
+    if (!real) {
+      rowb[i] = -1;
+      slot[i] = -1;
+      continue;
+    }
+    const int32_t s = b->seq[i];
+    if (bseq_of[s] < 0) {
+      bseq_of[s] = n_bseq;
+      const auto& tab = e->kv->tables[s];
+      int32_t* row = btab + (size_t)n_bseq * e->maxb;
+      for (int j = 0; j < e->maxb; ++j) row[j] = j < (int)tab.size() ? tab[j] : -1;
+      ++n_bseq;
+    }
+    rowb[i] = bseq_of[s];
+    const int32_t p = b->pos[i];
+    slot[i] = e->kv->tables[s][p / NS_BLOCK_SIZE] * NS_BLOCK_SIZE + p % NS_BLOCK_SIZE;
+  }
+  const size_t head = 4 * (size_t)T * sizeof(int32_t);
+  const size_t bytes = head + (size_t)n_bseq * e->maxb * sizeof(int32_t);
+  HIP_TRY(hipMemcpyAsync(e->meta(), m, bytes, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(e->staging_ev[k], st));
+  e->staging_used[k] = true;
+  return NS_OK;
+}
+
+void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::AttnArgs* a) {
+  a->dtype = e->d.dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
+  a->q_att = e->q_att();
+  a->kc = e->k_layer(layer);
+  a->vc = e->v_layer(layer);
+  a->row_bseq = e->m_rowb();
+  a->row_pos = e->m_pos();
+  a->btab = e->m_btab();
+  a->maxb = e->maxb;
+  a->out = e->o();
+  a->part_acc = (float*)(e->ws + e->plan.part_acc);
+  a->part_ml = (float*)(e->ws + e->plan.part_ml);
+  a->row0 = r0;
+  a->n_rows = r1 - r0;
+  a->nq = e->d.n_q_heads;
+  a->nkv = e->d.n_kv_heads;
+  a->d = e->d.head_dim;
+  attn_partition(n_tok, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, &a->part_tokens, &a->n_parts);
+  a->wg_cap = e->sched.attn_wg_cap;
+}
+
+// The kernel sequence of one step over n_tok rows (metadata already on the
+// device, x already holding the hidden input for models without a
+// vocabulary).  Used unchanged by eager steps and by graph capture.
+// Kernel classes reported by the profiling mode.
+enum { K_EMBED = 0, K_ROPE_TABLE, K_NORM, K_QKV, K_ROPE_KV, K_ATTN, K_O, K_GU, K_DOWN, K_LM_HEAD, K_COPY };
+
+int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStream_t st, bool capturing) {
+  const ns_model_desc& d = e->d;
+  const int dt = d.dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
+  const int H = d.hidden, nq = d.n_q_heads, nkv = d.n_kv_heads, hd = d.head_dim, F = d.ffn;
+  const int QKV = (nq + 2 * nkv) * hd, DQ = nq * hd;
+  const size_t es = e->es;
+  const bool overlap = sc.overlap != 0;
+  auto nano = row_parts(n_tok, sc.n_nano, sc.nano_rows);
+  auto qparts = sc.n_qkv > 1 ? row_parts(n_tok, sc.n_qkv, sc.qkv_rows) : nano;
+  int launches = 0;
+  hipStream_t sa = overlap ? e->s2 : st;
+  const bool prof = e->prof && !capturing && !overlap;
+  e->prof_n = 0;
+  if (prof) HIP_TRY(hipEventRecord(e->prof_start, st));
+  auto mark = [&](int kind) -> int {
+    if (!prof) return NS_OK;
+    if (e->prof_n >= (int)e->prof_ev.size()) {
+      hipEvent_t ev;
+      HIP_TRY(hipEventCreate(&ev));
+      e->prof_ev.push_back(ev);
+      e->prof_kind.push_back(0);
+    }
+    HIP_TRY(hipEventRecord(e->prof_ev[e->prof_n], st));
+    e->prof_kind[e->prof_n++] = kind;
+    return NS_OK;
+  };
+#define MARK(k)                 \
+  do {                          \
+    int _rc = mark(k);          \
+    if (_rc) return _rc;        \
+  } while (0)
+
+  if (d.vocab > 0) {
+    ns::launch_embed(dt, e->embed, e->m_tok(), e->x(), n_tok, H, d.vocab, st);
+    ++launches;
+    MARK(K_EMBED);
+  }
+  ns::launch_rope_table(e->m_pos(), e->cosb(), e->sinb(), n_tok, hd, d.rope_base, st);
+  ++launches;
+  MARK(K_ROPE_TABLE);
+
+  char* h = (char*)e->h();
+  char* o = (char*)e->o();
+  char* act = (char*)e->act();
+  float* x = e->x();
+  float* qkv = e->qkv();
+  for (int l = 0; l < d.n_layers; ++l) {
+    for (size_t j = 0; j < qparts.size(); ++j) {
+      const int r0 = qparts[j].first, n = qparts[j].second - r0;
+      ns::launch_rmsnorm(dt, x + (size_t)r0 * H, e->attn_norm[l], h + r0 * H * es, n, H, d.rms_eps, st);
+      MARK(K_NORM);
+      if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n, QKV, H, h + r0 * H * es, H, e->wqkv[l], H,
+                          qkv + (size_t)r0 * QKV, QKV, st))
+        NS_FAIL(NS_ESHAPE, "unsupported QKV projection shape");
+      MARK(K_QKV);
+      ns::launch_rope_kv(dt, qkv + (size_t)r0 * QKV, e->cosb() + (size_t)r0 * hd / 2,
+                         e->sinb() + (size_t)r0 * hd / 2, e->m_slot() + r0,
+                         (char*)e->q_att() + (size_t)r0 * DQ * es, e->k_layer(l), e->v_layer(l), n, nq, nkv, hd,
+                         st);
+      MARK(K_ROPE_KV);
+      launches += 3;
+      ns::AttnArgs a;
+      attn_args(e, l, r0, r0 + n, n_tok, &a);
+      if (overlap) {
+        HIP_TRY(hipEventRecord(e->ev_qkv[j], st));
+        HIP_TRY(hipStreamWaitEvent(sa, e->ev_qkv[j], 0));
+      }
+      ns::launch_attention(a, sa);
+      launches += a.n_parts > 1 ? 2 : 1;
+      MARK(K_ATTN);
+      if (overlap) HIP_TRY(hipEventRecord(e->ev_att[j], sa));
+    }
+    for (size_t i = 0; i < nano.size(); ++i) {
+      const int r0 = nano[i].first, r1 = nano[i].second, n = r1 - r0;
+      if (overlap)
+        for (size_t j = 0; j < qparts.size(); ++j)
+          if (qparts[j].first < r1 && qparts[j].second > r0) HIP_TRY(hipStreamWaitEvent(st, e->ev_att[j], 0));
+      if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, DQ, o + r0 * DQ * es, DQ, e->wo[l], DQ, x + (size_t)r0 * H,
+                          H, st))
+        NS_FAIL(NS_ESHAPE, "unsupported O projection shape");
+      MARK(K_O);
+      ns::launch_rmsnorm(dt, x + (size_t)r0 * H, e->mlp_norm[l], h + r0 * H * es, n, H, d.rms_eps, st);
+      MARK(K_NORM);
+      if (ns::launch_gemm(dt, ns::EPI_SILU_MUL, n, F, H, h + r0 * H * es, H, e->wgu[l], H, act + r0 * F * es, F,
+                          st))
+        NS_FAIL(NS_ESHAPE, "unsupported gate-up projection shape");
+      MARK(K_GU);
+      if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, F, act + r0 * F * es, F, e->wdown[l], F,
+                          x + (size_t)r0 * H, H, st))
+        NS_FAIL(NS_ESHAPE, "unsupported down projection shape");
+      MARK(K_DOWN);
+      launches += 4;
+    }
+  }
+  if (d.vocab > 0) {
+    ns::launch_rmsnorm(dt, x, e->final_norm, h, n_tok, H, d.rms_eps, st);
+    MARK(K_NORM);
+    if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n_tok, d.vocab, H, h, H, e->lm_head, H, out, d.vocab, st))
+      NS_FAIL(NS_ESHAPE, "unsupported LM head shape");
+    MARK(K_LM_HEAD);
+    launches += 2;
+  } else {
+    ns::launch_copy_rows(x, (float*)out, (long)n_tok * H, st);
+    ++launches;
+    MARK(K_COPY);
+  }
+#undef MARK
+  HIP_TRY(hipGetLastError());
+  e->last_launches = launches;
+  return NS_OK;
+}
+
+int make_second_stream(ns_engine* e, float frac) {
+  if (frac > 0.f) {
+    int ncu = 0;
+    HIP_TRY(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, 0));
+    int use = std::max(1, std::min(ncu, (int)(frac * ncu + 0.5f)));
+    std::vector<uint32_t> mask((ncu + 31) / 32, 0u);
+    for (int i = 0; i < use; ++i) mask[i / 32] |= 1u << (i % 32);
+    HIP_TRY(hipExtStreamCreateWithCUMask(&e->s2, (uint32_t)mask.size(), mask.data()));
+  } else {
+    HIP_TRY(hipStreamCreateWithFlags(&e->s2, hipStreamNonBlocking));
+  }
+  return NS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ns_workspace_bytes(const ns_model_desc* desc, int32_t max_tokens, int32_t max_blocks_per_seq) {
+  if (ns::check_desc(desc) != NS_OK || max_tokens <= 0 || max_blocks_per_seq <= 0) return 0;
+  return make_plan(desc, max_tokens, max_blocks_per_seq).total;
+}
+
+int ns_engine_create(const ns_model_desc* desc, const ns_weights* w, ns_kv* kv, void* kv_dev, size_t kv_bytes,
+                     void* workspace, size_t ws_bytes, int32_t max_tokens, const ns_sched* sched,
+                     ns_engine** out) {
+  if (!out) NS_FAIL(NS_EINVAL, "null output pointer");
+  int rc = ns::check_desc(desc);
+  if (rc) return rc;
+  if ((rc = check_sched(sched))) return rc;
+  if (!w || !kv || !kv_dev || !workspace) NS_FAIL(NS_EINVAL, "null weights, kv manager, kv memory or workspace");
+  if (memcmp(&kv->desc, desc, sizeof *desc) != 0) NS_FAIL(NS_EINVAL, "kv manager was created for another model");
+  if (max_tokens <= 0) NS_FAIL(NS_EINVAL, "max_tokens must be positive");
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  const int dt = desc->dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
+  if (!ns::attention_supported(dt, desc->head_dim, G))
+    NS_FAIL(NS_EINVAL, "no attention kernel for head_dim %d, group %d", desc->head_dim, G);
+  const int QKV = (desc->n_q_heads + 2 * desc->n_kv_heads) * desc->head_dim;
+  if (!ns::gemm_supported(dt, desc->hidden) || !ns::gemm_supported(dt, desc->ffn) ||
+      !ns::gemm_supported(dt, desc->n_q_heads * desc->head_dim) || QKV <= 0)
+    NS_FAIL(NS_EINVAL, "bf16 projections need K dimensions that are multiples of 32");
+  const size_t need_kv = ns_kv_bytes(desc, kv->num_blocks);
+  if (kv_bytes < need_kv) NS_FAIL(NS_ESHAPE, "kv memory of %zu bytes < %zu needed", kv_bytes, need_kv);
+  const Plan plan = make_plan(desc, max_tokens, kv->max_blocks);
+  if (ws_bytes < plan.total) NS_FAIL(NS_ESHAPE, "workspace of %zu bytes < %zu needed", ws_bytes, plan.total);
+  for (int l = 0; l < desc->n_layers; ++l)
+    if (!w->attn_norm || !w->wqkv || !w->wo || !w->mlp_norm || !w->wgu || !w->wdown || !w->attn_norm[l] ||
+        !w->wqkv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->wgu[l] || !w->wdown[l])
+      NS_FAIL(NS_EINVAL, "missing weights of layer %d", l);
+  if (desc->vocab > 0 && (!w->final_norm || !w->embed || !w->lm_head))
+    NS_FAIL(NS_EINVAL, "missing embedding, final norm or LM head");
+
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    NS_FAIL(NS_EINVAL, "built for gfx950 (MI355X); device is %s", prop.gcnArchName);
+
+  ns_engine* e = new ns_engine;
+  e->d = *desc;
+  e->es = elem_size(desc->dtype);
+  e->G = G;
+  for (int l = 0; l < desc->n_layers; ++l) {
+    e->attn_norm.push_back(w->attn_norm[l]);
+    e->wqkv.push_back(w->wqkv[l]);
+    e->wo.push_back(w->wo[l]);
+    e->mlp_norm.push_back(w->mlp_norm[l]);
+    e->wgu.push_back(w->wgu[l]);
+    e->wdown.push_back(w->wdown[l]);
+  }
+  e->final_norm = w->final_norm;
+  e->embed = w->embed;
+  e->lm_head = w->lm_head;
+  e->kv = kv;
+  e->kv_dev = (char*)kv_dev;
+  e->kv_layer = ns::kv_layer_bytes(desc, kv->num_blocks);
+  e->num_blocks = kv->num_blocks;
+  e->max_tokens = max_tokens;
+  e->maxb = kv->max_blocks;
+  e->ws = (char*)workspace;
+  e->plan = plan;
+  if (sched) e->sched = *sched;
+  auto fail = [&](int code) {
+    ns_engine_destroy(e);
+    return code;
+  };
+  if ((rc = make_second_stream(e, e->sched.cu_mask_frac))) return fail(rc);
+  for (int i = 0; i < kMaxParts; ++i) {
+    if (hipEventCreateWithFlags(&e->ev_qkv[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&e->ev_att[i], hipEventDisableTiming) != hipSuccess) {
+      ns::set_error("hipEventCreate failed");
+      return fail(NS_EHIP);
+    }
+  }
+  for (int k = 0; k < 2; ++k) {
+    if (hipHostMalloc((void**)&e->staging[k], plan.meta_ints * sizeof(int32_t), hipHostMallocDefault) !=
+            hipSuccess ||
+        hipEventCreateWithFlags(&e->staging_ev[k], hipEventDisableTiming) != hipSuccess) {
+      ns::set_error("pinned staging allocation failed");
+      return fail(NS_EHIP);
+    }
+    memset(e->staging[k], 0, plan.meta_ints * sizeof(int32_t));
+  }
+  *out = e;
+  return NS_OK;
+}
+
+void ns_engine_destroy(ns_engine* e) {
+  if (!e) return;
+  if (e->s2) {
+    hipStreamSynchronize(e->s2);
+    hipStreamDestroy(e->s2);
+  }
+  for (int i = 0; i < kMaxParts; ++i) {
+    if (e->ev_qkv[i]) hipEventDestroy(e->ev_qkv[i]);
+    if (e->ev_att[i]) hipEventDestroy(e->ev_att[i]);
+  }
+  for (hipEvent_t ev : e->prof_ev) hipEventDestroy(ev);
+  if (e->prof_start) hipEventDestroy(e->prof_start);
+  for (int k = 0; k < 2; ++k) {
+    if (e->staging_ev[k]) {
+      hipEventSynchronize(e->staging_ev[k]);
+      hipEventDestroy(e->staging_ev[k]);
+    }
+    if (e->staging[k]) hipHostFree(e->staging[k]);
+  }
+  delete e;
+}
+
+int ns_engine_set_sched(ns_engine* e, const ns_sched* sched) {
+  if (!e || !sched) NS_FAIL(NS_EINVAL, "null argument");
+  int rc = check_sched(sched);
+  if (rc) return rc;
+  const float frac = e->sched.cu_mask_frac;
+  e->sched = *sched;
+  e->sched.cu_mask_frac = frac;
+  return NS_OK;
+}
+
+int ns_decode_step(ns_engine* e, const ns_batch* b, void* out, void* stream) {
+  if (!e || !out) NS_FAIL(NS_EINVAL, "null engine or output");
+  int rc = check_batch(e, b, e->max_tokens);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = upload_meta(e, b, b->n_tok, st))) return rc;
+  if (e->d.vocab == 0)
+    HIP_TRY(hipMemcpyAsync(e->x(), b->hidden_in, (size_t)b->n_tok * e->d.hidden * 4, hipMemcpyDeviceToDevice, st));
+  return enqueue_step(e, e->sched, b->n_tok, out, st, false);
+}
+
+int ns_graph_capture(ns_engine* e, int32_t bucket, void* out, void* stream, ns_graph** gout) {
+  if (!e || !out || !gout) NS_FAIL(NS_EINVAL, "null argument");
+  if (!stream) NS_FAIL(NS_EINVAL, "graph capture needs a non-null stream");
+  if (bucket <= 0) NS_FAIL(NS_EINVAL, "bucket must be positive");
+  if (bucket > e->max_tokens) NS_FAIL(NS_ESHAPE, "bucket %d exceeds max_tokens %d", bucket, e->max_tokens);
+  hipStream_t st = (hipStream_t)stream;
+  ns_graph* g = new ns_graph;
+  g->e = e;
+  g->bucket = bucket;
+  g->out = out;
+  hipError_t he = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+  if (he != hipSuccess) {
+    delete g;
+    NS_FAIL(NS_EHIP, "hipStreamBeginCapture: %s", hipGetErrorString(he));
+  }
+  int rc = enqueue_step(e, e->sched, bucket, out, st, true);
+  he = hipStreamEndCapture(st, &g->graph);
+  if (rc != NS_OK || he != hipSuccess) {
+    if (g->graph) hipGraphDestroy(g->graph);
+    delete g;
+    if (rc != NS_OK) return rc;
+    NS_FAIL(NS_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(he));
+  }
+  he = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  if (he != hipSuccess) {
+    hipGraphDestroy(g->graph);
+    delete g;
+    NS_FAIL(NS_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(he));
+  }
+  *gout = g;
+  return NS_OK;
+}
+
+int ns_graph_replay(ns_graph* g, const ns_batch* b, void* stream) {
+  if (!g) NS_FAIL(NS_EINVAL, "null graph");
+  ns_engine* e = g->e;
+  int rc = check_batch(e, b, g->bucket);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = upload_meta(e, b, g->bucket, st))) return rc;
+  if (e->d.vocab == 0)
+    HIP_TRY(hipMemcpyAsync(e->x(), b->hidden_in, (size_t)b->n_tok * e->d.hidden * 4, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(hipGraphLaunch(g->exec, st));
+  return NS_OK;
+}
+
+void ns_graph_destroy(ns_graph* g) {
+  if (!g) return;
+  if (g->exec) hipGraphExecDestroy(g->exec);
+  if (g->graph) hipGraphDestroy(g->graph);
+  delete g;
+}
+
+int ns_kv_scatter(ns_engine* e, int32_t layer, int32_t n, const int32_t* slots, const void* k, const void* v,
+                  void* stream) {
+  if (!e || (n > 0 && (!slots || !k || !v))) NS_FAIL(NS_EINVAL, "null argument");
+  if (layer < 0 || layer >= e->d.n_layers || n < 0) NS_FAIL(NS_EINVAL, "bad layer or count");
+  ns::launch_kv_scatter(e->d.dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32, slots, k, v, e->k_layer(layer),
+                        e->v_layer(layer), n, e->d.n_kv_heads, e->d.head_dim, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return NS_OK;
+}
+
+int ns_kv_gather(ns_engine* e, int32_t layer, int32_t n, const int32_t* slots, void* k, void* v, void* stream) {
+  if (!e || (n > 0 && (!slots || !k || !v))) NS_FAIL(NS_EINVAL, "null argument");
+  if (layer < 0 || layer >= e->d.n_layers || n < 0) NS_FAIL(NS_EINVAL, "bad layer or count");
+  ns::launch_kv_gather(e->d.dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32, slots, k, v, e->k_layer(layer),
+                       e->v_layer(layer), n, e->d.n_kv_heads, e->d.head_dim, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return NS_OK;
+}
+
+int ns_engine_profile(ns_engine* e, int32_t enable) {
+  if (!e) NS_FAIL(NS_EINVAL, "null engine");
+  if (enable && !e->prof_start) HIP_TRY(hipEventCreate(&e->prof_start));
+  e->prof = enable != 0;
+  e->prof_n = 0;
+  return NS_OK;
+}
+
+int ns_engine_profile_read(ns_engine* e, int32_t cap, int32_t* kinds, float* us, int32_t* n_out) {
+  if (!e || !n_out || (cap > 0 && (!kinds || !us))) NS_FAIL(NS_EINVAL, "null argument");
+  const int n = std::min(cap, e->prof_n);
+  if (n > 0) HIP_TRY(hipEventSynchronize(e->prof_ev[e->prof_n - 1]));
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, i ? e->prof_ev[i - 1] : e->prof_start, e->prof_ev[i]));
+    kinds[i] = e->prof_kind[i];
+    us[i] = ms * 1e3f;
+  }
+  *n_out = e->prof_n;
+  return NS_OK;
+}
+
+int ns_engine_last_launches(const ns_engine* e, int32_t* out) {
+  if (!e || !out) NS_FAIL(NS_EINVAL, "null argument");
+  *out = e->last_launches;
+  return NS_OK;
+}
+
+// ---------------------------------------------------------------- single ops
+int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, const void* B, void* C,
+               void* stream) {
+  if (dtype != NS_F32 && dtype != NS_BF16) NS_FAIL(NS_EINVAL, "bad dtype");
+  if (epi < 0 || epi > 2) NS_FAIL(NS_EINVAL, "bad epilogue");
+  if (M < 0 || N < 0 || K <= 0) NS_FAIL(NS_EINVAL, "bad sizes");
+  if ((M > 0 && N > 0) && (!A || !B || !C)) NS_FAIL(NS_EINVAL, "null matrix");
+  const int dt = dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
+  if (!ns::gemm_supported(dt, K)) NS_FAIL(NS_ESHAPE, "K = %d unsupported (bf16 needs K %% 32 == 0)", K);
+  ns::launch_gemm(dt, epi, M, N, K, A, K, B, K, C, N, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return NS_OK;
+}
+
+size_t ns_op_attention_ws_bytes(const ns_model_desc* desc, int32_t n_rows, int32_t max_blocks_per_seq) {
+  if (ns::check_desc(desc) != NS_OK || n_rows <= 0 || max_blocks_per_seq <= 0) return 0;
+  int P, np;
+  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &P, &np);
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  const size_t items = (size_t)n_rows * desc->n_kv_heads * np;
+  return align_up(items * G * desc->head_dim * 4, 256) + align_up(items * G * 2 * 4, 256);
+}
+
+int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                    int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
+                    int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap,
+                    void* stream) {
+  int rc = ns::check_desc(desc);
+  if (rc) return rc;
+  if (n_rows <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || wg_cap < 0) NS_FAIL(NS_EINVAL, "bad sizes");
+  if (!q_att || !kv_layer || !row_bseq || !row_pos || !btab || !out) NS_FAIL(NS_EINVAL, "null argument");
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  const int dt = desc->dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
+  if (!ns::attention_supported(dt, desc->head_dim, G))
+    NS_FAIL(NS_EINVAL, "no attention kernel for head_dim %d, group %d", desc->head_dim, G);
+  const size_t need = ns_op_attention_ws_bytes(desc, n_rows, max_blocks_per_seq);
+  if (ws_bytes < need || (need > 0 && !ws)) NS_FAIL(NS_ESHAPE, "workspace of %zu bytes < %zu", ws_bytes, need);
+  ns::AttnArgs a;
+  a.dtype = dt;
+  a.q_att = q_att;
+  a.kc = kv_layer;
+  a.vc = (const char*)kv_layer + ns::kv_layer_bytes(desc, num_blocks) / 2;
+  a.row_bseq = row_bseq;
+  a.row_pos = row_pos;
+  a.btab = btab;
+  a.maxb = max_blocks_per_seq;
+  a.out = out;
+  a.row0 = 0;
+  a.n_rows = n_rows;
+  a.nq = desc->n_q_heads;
+  a.nkv = desc->n_kv_heads;
+  a.d = desc->head_dim;
+  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &a.part_tokens, &a.n_parts);
+  const int G2 = G;
+  const size_t items = (size_t)n_rows * desc->n_kv_heads * a.n_parts;
+  a.part_acc = (float*)ws;
+  a.part_ml = (float*)((char*)ws + align_up(items * G2 * desc->head_dim * 4, 256));
+  a.wg_cap = wg_cap;
+  ns::launch_attention(a, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return NS_OK;
+}
+
+}  // extern "C"

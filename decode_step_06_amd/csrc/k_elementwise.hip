@@ -1,0 +1,232 @@
+// Row-wise kernels of the decode step: embedding gather, RoPE table (once per
+// step), RMSNorm, RoPE + paged KV-cache write, and KV scatter/gather helpers.
+//
+// These are the "negligible" class of the NanoFlow review's operator table
+// (section "Four resource classes, one serialized queue"): each moves a few
+// bytes per row, so the design goal is one launch per use and coalesced
+// row access, not arithmetic throughput.
+#include "ns_kernels.h"
+
+namespace ns {
+
+// ---------------------------------------------------------------- embedding
+// x[t][:] = E[token[t]][:] widened to fp32 (the residual stream is fp32).
+template <typename T>
+__global__ void __launch_bounds__(256) embed_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
+                                                    float* __restrict__ x, int H, int V) {
+  const int t = blockIdx.x;
+  int id = tok[t];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const T* src = E + (long)id * H;
+  float* dst = x + (long)t * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) dst[i] = Elem<T>::load(src, i);
+}
+
+__global__ void __launch_bounds__(256) copy_rows_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                        long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------- RoPE table
+// cos/sin[t][j] of angle pos[t] * base^(-2j/d), built once per step and read
+// by every layer (nanoserve notes, changes table: "RoPE cos/sin computed once
+// per step").  Angles and sin/cos in fp64, stored fp32.
+__global__ void __launch_bounds__(256) rope_table_kernel(const int32_t* __restrict__ pos, float* __restrict__ cosb,
+                                                         float* __restrict__ sinb, int n_rows, int half,
+                                                         double log2_base) {
+  const long n = (long)n_rows * half;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const int t = (int)(i / half), j = (int)(i % half);
+    const double inv_freq = exp2(-2.0 * j / (2.0 * half) * log2_base);
+    const double a = (double)pos[t] * inv_freq;
+    double s, c;
+    sincos(a, &s, &c);
+    cosb[i] = (float)c;
+    sinb[i] = (float)s;
+  }
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// h[t] = x[t] / sqrt(mean(x[t]^2) + eps) * g, one workgroup per row; the
+// residual add that precedes it in the layer is fused into the producing
+// projection's epilogue, so x already holds the updated residual stream.
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x, const T* __restrict__ g,
+                                                      T* __restrict__ h, int H, float eps) {
+  const int t = blockIdx.x;
+  const float* xr = x + (long)t * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    const float v = xr[i];
+    ss += v * v;
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  T* hr = h + (long)t * H;
+  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(hr, i, xr[i] * r * Elem<T>::load(g, i));
+}
+
+// ---------------------------------------------------------------- RoPE + KV write
+// From the QKV projection (fp32 [T, (nq + 2 nkv) d]) for one row per
+// workgroup: rotate-half RoPE on q and k with the step's table, store q in
+// the attention layout [T][nkv][d/E][G][E] (the G query heads of one KV head
+// chunk by chunk, so attention reads them as one uniform block), and write
+// the rotated k and the v into the paged cache at the row's slot (padding
+// rows, slot < 0, write no K/V).
+template <typename T>
+__global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ qkv, const float* __restrict__ cosb,
+                                                      const float* __restrict__ sinb, const int32_t* __restrict__ slot,
+                                                      T* __restrict__ q_att, T* __restrict__ kc, T* __restrict__ vc,
+                                                      int nq, int nkv, int d) {
+  constexpr int E = Elem<T>::per16;
+  const int t = blockIdx.x;
+  const int half = d >> 1, G = nq / nkv, nch = d / E;
+  const float* row = qkv + (long)t * (nq + 2 * nkv) * d;
+  const float* cr = cosb + (long)t * half;
+  const float* sr = sinb + (long)t * half;
+  const int s = slot[t];
+  const long blk = s >= 0 ? (long)(s / NS_BLOCK) : 0;
+  const int tok = s >= 0 ? s % NS_BLOCK : 0;
+  // q heads
+  for (int i = threadIdx.x; i < nq * half; i += 256) {
+    const int hq = i / half, j = i % half;
+    const float x1 = row[hq * d + j], x2 = row[hq * d + j + half];
+    const float c = cr[j], sn = sr[j];
+    const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+    const int g = hq / G, hh = hq % G;
+    const long base = ((long)t * nkv + g) * nch * G * E + (long)hh * E;
+    Elem<T>::store(q_att, base + (long)(j / E) * G * E + j % E, y1);
+    Elem<T>::store(q_att, base + (long)((j + half) / E) * G * E + (j + half) % E, y2);
+  }
+  if (s < 0) return;
+  // k heads (rotated) into the chunk-interleaved K layout
+  const float* kr = row + nq * d;
+  for (int i = threadIdx.x; i < nkv * half; i += 256) {
+    const int g = i / half, j = i % half;
+    const float x1 = kr[g * d + j], x2 = kr[g * d + j + half];
+    const float c = cr[j], sn = sr[j];
+    const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+    const long base = (blk * nkv + g) * (long)nch * NS_BLOCK * E + (long)tok * E;
+    Elem<T>::store(kc, base + (long)(j / E) * NS_BLOCK * E + j % E, y1);
+    Elem<T>::store(kc, base + (long)((j + half) / E) * NS_BLOCK * E + (j + half) % E, y2);
+  }
+  // v heads into token rows
+  const float* vr = row + (nq + nkv) * d;
+  for (int i = threadIdx.x; i < nkv * d; i += 256) {
+    const int g = i / d, j = i % d;
+    Elem<T>::store(vc, ((blk * nkv + g) * NS_BLOCK + tok) * (long)d + j, vr[i]);
+  }
+}
+
+// ---------------------------------------------------------------- KV scatter / gather
+// Logical [n, nkv, d] <-> physical cache layout (setting up or reading back
+// cached context).
+template <typename T>
+__global__ void __launch_bounds__(256) kv_scatter_kernel(const int32_t* __restrict__ slots, const T* __restrict__ k,
+                                                         const T* __restrict__ v, T* __restrict__ kc,
+                                                         T* __restrict__ vc, int nkv, int d) {
+  constexpr int E = Elem<T>::per16;
+  const int i = blockIdx.x;
+  const int s = slots[i];
+  if (s < 0) return;
+  const long blk = s / NS_BLOCK;
+  const int tok = s % NS_BLOCK, nch = d / E;
+  for (int e = threadIdx.x; e < nkv * d; e += 256) {
+    const int g = e / d, j = e % d;
+    kc[((blk * nkv + g) * nch + j / E) * (long)NS_BLOCK * E + (long)tok * E + j % E] = k[(long)i * nkv * d + e];
+    vc[((blk * nkv + g) * NS_BLOCK + tok) * (long)d + j] = v[(long)i * nkv * d + e];
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) kv_gather_kernel(const int32_t* __restrict__ slots, T* __restrict__ k,
+                                                        T* __restrict__ v, const T* __restrict__ kc,
+                                                        const T* __restrict__ vc, int nkv, int d) {
+  constexpr int E = Elem<T>::per16;
+  const int i = blockIdx.x;
+  const int s = slots[i];
+  const int nch = d / E;
+  for (int e = threadIdx.x; e < nkv * d; e += 256) {
+    if (s < 0) {
+      k[(long)i * nkv * d + e] = T(0);
+      v[(long)i * nkv * d + e] = T(0);
+      continue;
+    }
+    const long blk = s / NS_BLOCK;
+    const int tok = s % NS_BLOCK;
+    const int g = e / d, j = e % d;
+    k[(long)i * nkv * d + e] = kc[((blk * nkv + g) * nch + j / E) * (long)NS_BLOCK * E + (long)tok * E + j % E];
+    v[(long)i * nkv * d + e] = vc[((blk * nkv + g) * NS_BLOCK + tok) * (long)d + j];
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+static inline int nblocks(long n, int per) {
+  long b = (n + per - 1) / per;
+  return (int)(b < 1 ? 1 : (b > 65535 ? 65535 : b));
+}
+
+void launch_embed(int dtype, const void* E, const int32_t* tok, float* x, int T, int H, int V, hipStream_t st) {
+  if (dtype == NS_DT_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)E, tok, x, H, V);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)E, tok, x, H, V);
+}
+
+void launch_copy_rows(const float* src, float* dst, long n, hipStream_t st) {
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(nblocks(n, 1024)), dim3(256), 0, st, src, dst, n);
+}
+
+void launch_rope_table(const int32_t* pos, float* cosb, float* sinb, int T, int d, float base, hipStream_t st) {
+  const int half = d / 2;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(nblocks((long)T * half, 256)), dim3(256), 0, st, pos, cosb, sinb, T,
+                     half, log2((double)base));
+}
+
+void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st) {
+  if (T <= 0) return;
+  if (dtype == NS_DT_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(T), dim3(256), 0, st, x, (const bf16_t*)g, (bf16_t*)h, H, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, st, x, (const float*)g, (float*)h, H, eps);
+}
+
+void launch_rope_kv(int dtype, const float* qkv, const float* cosb, const float* sinb, const int32_t* slot,
+                    void* q_att, void* kc, void* vc, int T, int nq, int nkv, int d, hipStream_t st) {
+  if (T <= 0) return;
+  if (dtype == NS_DT_BF16)
+    hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(T), dim3(256), 0, st, qkv, cosb, sinb, slot, (bf16_t*)q_att,
+                       (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
+  else
+    hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(T), dim3(256), 0, st, qkv, cosb, sinb, slot, (float*)q_att,
+                       (float*)kc, (float*)vc, nq, nkv, d);
+}
+
+void launch_kv_scatter(int dtype, const int32_t* slots, const void* k, const void* v, void* kc, void* vc, int n,
+                       int nkv, int d, hipStream_t st) {
+  if (n <= 0) return;
+  if (dtype == NS_DT_BF16)
+    hipLaunchKernelGGL(kv_scatter_kernel<bf16_t>, dim3(n), dim3(256), 0, st, slots, (const bf16_t*)k,
+                       (const bf16_t*)v, (bf16_t*)kc, (bf16_t*)vc, nkv, d);
+  else
+    hipLaunchKernelGGL(kv_scatter_kernel<float>, dim3(n), dim3(256), 0, st, slots, (const float*)k, (const float*)v,
+                       (float*)kc, (float*)vc, nkv, d);
+}
+
+void launch_kv_gather(int dtype, const int32_t* slots, void* k, void* v, const void* kc, const void* vc, int n,
+                      int nkv, int d, hipStream_t st) {
+  if (n <= 0) return;
+  if (dtype == NS_DT_BF16)
+    hipLaunchKernelGGL(kv_gather_kernel<bf16_t>, dim3(n), dim3(256), 0, st, slots, (bf16_t*)k, (bf16_t*)v,
+                       (const bf16_t*)kc, (const bf16_t*)vc, nkv, d);
+  else
+    hipLaunchKernelGGL(kv_gather_kernel<float>, dim3(n), dim3(256), 0, st, slots, (float*)k, (float*)v,
+                       (const float*)kc, (const float*)vc, nkv, d);
+}
+
+}  // namespace ns

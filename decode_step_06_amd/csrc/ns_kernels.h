@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 decode-step kernels (device code in
+// k_*.hip).  Every launcher only enqueues on the given stream; argument
+// checking happens in the engine before anything is enqueued.
+#pragma once
+
+#include "ns_common.h"
+
+#define NS_DT_F32 0
+#define NS_DT_BF16 1
+
+namespace ns {
+
+// GEMM epilogues: C = A * B^T (A [M, K], B [N, K], both K-contiguous).
+enum GemmEpi {
+  EPI_STORE_F32 = 0,  // C fp32 [M, N] = acc
+  EPI_RESID_F32 = 1,  // C fp32 [M, N] += acc              (projection + residual add)
+  EPI_SILU_MUL = 2,   // C (dtype) [M, N] = silu(acc_gate) * acc_up, with the gate rows of B at
+                      // [0, N) and the up rows at [N, 2N)    (gate-up projection + SwiGLU)
+};
+
+// Returns 0, or -1 when the shape is unsupported (K % 32 != 0 for bf16).
+int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C,
+                int ldc, hipStream_t st);
+int gemm_supported(int dtype, int K);
+
+void launch_embed(int dtype, const void* E, const int32_t* tok, float* x, int T, int H, int V, hipStream_t st);
+void launch_copy_rows(const float* src, float* dst, long n, hipStream_t st);
+void launch_rope_table(const int32_t* pos, float* cosb, float* sinb, int T, int d, float base, hipStream_t st);
+void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st);
+void launch_rope_kv(int dtype, const float* qkv, const float* cosb, const float* sinb, const int32_t* slot,
+                    void* q_att, void* kc, void* vc, int T, int nq, int nkv, int d, hipStream_t st);
+void launch_kv_scatter(int dtype, const int32_t* slots, const void* k, const void* v, void* kc, void* vc, int n,
+                       int nkv, int d, hipStream_t st);
+void launch_kv_gather(int dtype, const int32_t* slots, void* k, void* v, const void* kc, const void* vc, int n,
+                      int nkv, int d, hipStream_t st);
+
+// Paged GQA decode attention over rows [row0, row0 + n_rows) of the step.
+struct AttnArgs {
+  int dtype;
+  const void* q_att;        // [T][nkv][d/E][G][E]
+  const void* kc;           // this layer's K region
+  const void* vc;           // this layer's V region
+  const int32_t* row_bseq;  // [T] row -> block-table row (-1: padding)
+  const int32_t* row_pos;   // [T]
+  const int32_t* btab;      // [n_bseq][maxb]
+  int maxb;
+  void* out;                // [T][nq * d] (dtype)
+  float* part_acc;          // [T * nkv * n_parts][G][d]
+  float* part_ml;           // [T * nkv * n_parts][G][2]
+  int row0, n_rows;
+  int nq, nkv, d;
+  int part_tokens;          // P, multiple of 64
+  int n_parts;              // partitions per row (max)
+  int wg_cap;               // 0 = one workgroup per work item
+};
+int attention_supported(int dtype, int d, int G);
+void launch_attention(const AttnArgs& a, hipStream_t st);
+
+}  // namespace ns

@@ -1,0 +1,305 @@
+/*
+ * ns.h -- C ABI of the MI355X (gfx950) batched GQA decode step.
+ *
+ * One decode iteration of a pre-norm grouped-query-attention transformer
+ * stack over a paged KV cache, as hand-written HIP kernels behind plain C
+ * entry points: pointers and sizes only, no C++ or framework types.
+ *
+ * Sources (the pages describe the problem; none gives an interface):
+ *  - page "gpu-waiting-not-working" (nanoserve notes), section "What I
+ *    changed because of it" and its changes table: paged KV cache with
+ *    per-sequence block tables, token -> cache-slot mapping, one pinned
+ *    host-to-device copy of the step metadata, RoPE cos/sin built once per
+ *    step, fused RMSNorm, GQA without an expanded K/V copy; section "Where
+ *    this leaves nanoserve": the decode step captured once as a graph and
+ *    replayed;
+ *  - page "NanoFlow: LLM Serving Is Compute Bound, and Your GPU Is Half
+ *    Idle", section "Nano-batching: manufacturing independence": the dense
+ *    batch split into nano-batches whose compute-bound projections overlap
+ *    memory-bound decode attention, ordered by events across streams
+ *    (section "Runtime details that keep the pipeline fed" and the closing
+ *    implementation note);
+ *  - page "The chef who calls out every order: SMs, CUDA streams and CUDA
+ *    graphs", sections on streams and on graphs captured per batch size.
+ *
+ * Conventions
+ *  - Every call returns NS_OK (0) or a negative status; nothing throws or
+ *    aborts across the ABI.  ns_last_error() gives a message for the last
+ *    failing call on this thread.
+ *  - Arguments are validated before any state changes or any work is
+ *    enqueued: a failing call has no side effects (except NS_EHIP, which
+ *    reports a HIP runtime failure that may have left work enqueued).
+ *  - "device" pointers are GPU memory the caller owns (e.g. torch tensors);
+ *    "host" pointers are ordinary CPU memory read or written before the call
+ *    returns.  The library owns only its opaque objects, its second stream,
+ *    its events and its pinned staging buffers, released by *_destroy.
+ *  - All device work goes to the caller's stream; work forked to the
+ *    library's second stream joins back before the call returns.
+ *  - One host thread per engine.  KV-manager and slot-map calls are
+ *    host-only and need no GPU.
+ */
+#ifndef NS_H
+#define NS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes */
+enum {
+  NS_OK = 0,
+  NS_EINVAL = -1,     /* null pointer, out-of-range id, bad descriptor      */
+  NS_ENOBLOCKS = -2,  /* KV pool exhausted                                   */
+  NS_ESHAPE = -3,     /* size beyond what the object was created for         */
+  NS_ESTATE = -4,     /* call not valid in the object's current state        */
+  NS_EHIP = -5        /* HIP runtime error (message from the runtime)        */
+};
+
+/* Message for the last failing ns_* call on this thread (never NULL). */
+const char* ns_last_error(void);
+
+/* ------------------------------------------------------------ model */
+enum { NS_F32 = 0, NS_BF16 = 1 };
+#define NS_BLOCK_SIZE 16   /* KV slots per cache block */
+
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;       /* H                                                   */
+  int32_t n_q_heads;    /* nq                                                  */
+  int32_t n_kv_heads;   /* nkv; nq % nkv == 0, group G = nq / nkv in {1..8}    */
+  int32_t head_dim;     /* d in {32, 64, 128}                                  */
+  int32_t ffn;          /* F (SwiGLU width)                                    */
+  int32_t vocab;        /* V; 0 = no embedding / LM head (hidden in and out)   */
+  int32_t tied;         /* LM head is the embedding matrix                      */
+  float rms_eps;
+  float rope_base;
+  int32_t dtype;        /* NS_F32 or NS_BF16: storage of weights, activations
+                           and KV cache (accumulation is always fp32)          */
+} ns_model_desc;
+
+/* Device pointers to the weights (element type = dtype), row-major [out, in]:
+ *   attn_norm[l], mlp_norm[l]: [H]
+ *   wqkv[l]: [(nq + 2 nkv) d, H]   rows: all q heads, then k heads, then v heads
+ *   wo[l]:   [H, nq d]
+ *   wgu[l]:  [2F, H]               rows: gate (F rows) then up (F rows)
+ *   wdown[l]:[H, F]
+ *   final_norm: [H]; embed: [V, H]; lm_head: [V, H] (may equal embed).
+ * The per-layer arrays are host arrays of n_layers device pointers; the
+ * engine copies them at creation. */
+typedef struct {
+  const void* const* attn_norm;
+  const void* const* wqkv;
+  const void* const* wo;
+  const void* const* mlp_norm;
+  const void* const* wgu;
+  const void* const* wdown;
+  const void* final_norm;
+  const void* embed;
+  const void* lm_head;
+} ns_weights;
+
+/* ------------------------------------------------------------ KV cache manager
+ * Paged KV cache (nanoserve notes, changes table and the paragraph after
+ * it: block tables and token -> slot mapping).  Host-side block manager
+ * over device memory the caller owns.
+ *
+ * Device layout (element type = dtype, E = 16 bytes / element size):
+ *   for layer l: K region then V region, each num_blocks * nkv * 16 * d
+ *   elements;
+ *   K: [num_blocks][nkv][d / E][16][E]  (16-byte chunks of a block's 16
+ *      tokens interleaved, so one wavefront reads a whole block's chunk
+ *      contiguously);
+ *   V: [num_blocks][nkv][16][d]         (token rows).
+ * Slot s lives in block s / 16 at row s % 16. */
+typedef struct ns_kv ns_kv;
+
+/* Bytes of device memory the cache needs for all layers. */
+size_t ns_kv_bytes(const ns_model_desc* desc, int32_t num_blocks);
+
+/* Create a manager of num_blocks blocks for sequence ids 0..max_seqs-1, each
+ * holding at most max_blocks_per_seq blocks.  free_order: host [num_blocks]
+ * permutation giving the initial free-list order (NULL = 0..num_blocks-1).
+ * Errors: NS_EINVAL (bad sizes, free_order not a permutation). */
+int ns_kv_create(const ns_model_desc* desc, int32_t num_blocks, int32_t max_seqs,
+                 int32_t max_blocks_per_seq, const int32_t* free_order, ns_kv** out);
+
+/* Grow sequence seq to hold n_tokens tokens (ceil(n_tokens / 16) blocks),
+ * taking blocks from the head of the free list.  All or nothing.
+ * Errors: NS_EINVAL (bad seq / n_tokens), NS_ESHAPE (more than
+ * max_blocks_per_seq blocks), NS_ENOBLOCKS (pool exhausted; table unchanged). */
+int ns_kv_alloc(ns_kv* kv, int32_t seq, int32_t n_tokens);
+
+/* Return all blocks of seq to the tail of the free list, in table order. */
+int ns_kv_free_seq(ns_kv* kv, int32_t seq);
+
+/* Copy the block tables to host out[max_seqs][max_blocks_per_seq], -1 padded. */
+int ns_kv_block_table(const ns_kv* kv, int32_t* out);
+
+/* Tokens sequence seq can hold (blocks * 16) and free blocks in the pool. */
+int ns_kv_capacity(const ns_kv* kv, int32_t seq, int32_t* tokens_out);
+int ns_kv_num_free(const ns_kv* kv, int32_t* out);
+
+void ns_kv_destroy(ns_kv* kv);
+
+/* Token -> slot mapping (nanoserve notes, paragraph after the changes table):
+ * slot_out[i] = table[seq[i]][pos[i] / 16] * 16 + pos[i] % 16, or -1 when
+ * seq[i] == -1 (a padding row).  Host arrays of n_tok entries.
+ * Errors: NS_EINVAL (seq out of range), NS_ESHAPE (pos beyond what the
+ * sequence's blocks hold); slot_out is untouched on error. */
+int ns_slot_map(const ns_kv* kv, int32_t n_tok, const int32_t* seq, const int32_t* pos,
+                int32_t* slot_out);
+
+/* ------------------------------------------------------------ engine */
+
+/* Nano-batch schedule (NanoFlow review, "Nano-batching: manufacturing
+ * independence"; its 70B schedule uses four nano-ops at KQV).
+ *   n_nano / nano_rows: the rows split into up to 4 consecutive nano-batches
+ *     for the O projection and the MLP; the last takes any remainder
+ *     (n_nano <= 1: one batch).
+ *   n_qkv / qkv_rows: the same for norm + QKV projection + RoPE/cache write
+ *     and attention (n_qkv <= 1: use the nano-batches).
+ *   overlap: 0 = every kernel in order on the caller's stream; 1 = attention
+ *     nano-ops on the library's second stream, ordered by events, so they
+ *     run beside the projections of other nano-batches.  Results are
+ *     bit-identical either way.
+ *   attn_wg_cap: 0 = no cap; else the attention kernel runs at most this
+ *     many workgroups (a persistent loop), the graph-safe way to bound the
+ *     share of the GPU that attention takes.
+ *   cu_mask_frac: 0 = none; else the second stream is created restricted to
+ *     this fraction of the compute units (hipExtStreamCreateWithCUMask).
+ *     Takes effect at engine creation only. */
+typedef struct {
+  int32_t n_nano;
+  int32_t nano_rows[4];
+  int32_t n_qkv;
+  int32_t qkv_rows[4];
+  int32_t overlap;
+  int32_t attn_wg_cap;
+  float cu_mask_frac;
+} ns_sched;
+
+/* One step's rows.  token_ids (host, [n_tok]) for models with a vocabulary,
+ * else hidden_in (device fp32 [n_tok, H]).  seq (host) is the sequence of
+ * each row, -1 for a padding row; pos (host) its position.  A decode row has
+ * pos = context length - 1; the row's own K/V are written to the cache
+ * before attention, so attention covers positions 0..pos.  Rows of one
+ * sequence must be in increasing position order. */
+typedef struct {
+  int32_t n_tok;
+  const int32_t* token_ids;
+  const void* hidden_in;
+  const int32_t* seq;
+  const int32_t* pos;
+} ns_batch;
+
+typedef struct ns_engine ns_engine;
+typedef struct ns_graph ns_graph;
+
+/* Device workspace the engine needs for batches of up to max_tokens rows
+ * and sequences of up to max_blocks_per_seq blocks. */
+size_t ns_workspace_bytes(const ns_model_desc* desc, int32_t max_tokens,
+                          int32_t max_blocks_per_seq);
+
+/* Create an engine over caller-owned weights, KV memory (kv_dev, kv_bytes >=
+ * ns_kv_bytes) and workspace (ws_bytes >= ns_workspace_bytes).  sched may be
+ * NULL (serial, one batch).  Checks the device is gfx950.
+ * Errors: NS_EINVAL, NS_ESHAPE, NS_EHIP. */
+int ns_engine_create(const ns_model_desc* desc, const ns_weights* weights, ns_kv* kv,
+                     void* kv_dev, size_t kv_bytes, void* workspace, size_t ws_bytes,
+                     int32_t max_tokens, const ns_sched* sched, ns_engine** out);
+void ns_engine_destroy(ns_engine* eng);
+
+/* Replace the engine's schedule (not the CU mask).  Graphs captured earlier
+ * keep the schedule they were captured with. */
+int ns_engine_set_sched(ns_engine* eng, const ns_sched* sched);
+
+/* One eager decode step: each kernel is its own launch on `stream`
+ * (a hipStream_t; NULL = the null stream).  out_dev (device fp32) receives
+ * logits [n_tok, V], or the final hidden state [n_tok, H] when vocab == 0.
+ * Every row's slot must already be allocated (ns_kv_alloc).
+ * Errors: NS_EINVAL, NS_ESHAPE (n_tok > max_tokens, pos beyond the
+ * sequence's blocks), NS_EHIP. */
+int ns_decode_step(ns_engine* eng, const ns_batch* batch, void* out_dev, void* stream);
+
+/* Capture the whole step for batches of exactly `bucket` rows as a hipGraph
+ * (capture once per batch size, replay per step).  out_dev is fixed at
+ * capture.  The capture enqueues nothing that runs.  Errors: NS_EINVAL,
+ * NS_ESHAPE (bucket > max_tokens), NS_EHIP. */
+int ns_graph_capture(ns_engine* eng, int32_t bucket, void* out_dev, void* stream,
+                     ns_graph** out);
+
+/* Replay: one host-to-device copy of the step metadata from pinned staging,
+ * then one graph launch, both on `stream`.  batch->n_tok <= bucket; rows
+ * beyond n_tok are padding (their output rows are unspecified).
+ * Errors: as ns_decode_step. */
+int ns_graph_replay(ns_graph* g, const ns_batch* batch, void* stream);
+
+void ns_graph_destroy(ns_graph* g);
+
+/* ------------------------------------------------------------ helpers */
+
+/* Write n cached positions into the KV cache of one layer: k, v are device
+ * [n, nkv, d] (element type = dtype) in logical order, slots a device int32
+ * [n] (entries < 0 skipped).  For setting up context that earlier steps
+ * would have written.  Enqueued on `stream`. */
+int ns_kv_scatter(ns_engine* eng, int32_t layer, int32_t n, const int32_t* slots_dev,
+                  const void* k_dev, const void* v_dev, void* stream);
+
+/* Read n cached positions of one layer back in logical order (device
+ * k_out, v_out [n, nkv, d]); slots < 0 give zeros. */
+int ns_kv_gather(ns_engine* eng, int32_t layer, int32_t n, const int32_t* slots_dev,
+                 void* k_out, void* v_out, void* stream);
+
+/* Kernels launched by the last ns_decode_step (for launch counting). */
+int ns_engine_last_launches(const ns_engine* eng, int32_t* out);
+
+/* Profiling of eager steps (measurement only).  When enabled, a serial
+ * (overlap = 0) ns_decode_step records a HIP event after every launch on
+ * the caller's stream.  ns_engine_profile_read waits for the last one and
+ * returns, for the first min(cap, n) launches, the kernel class and the
+ * device time since the previous event in microseconds; *n_out = launches
+ * recorded.  Classes: 0 embedding, 1 RoPE table, 2 RMSNorm, 3 QKV
+ * projection, 4 RoPE + cache write, 5 attention (with its combine),
+ * 6 O projection, 7 gate-up projection, 8 down projection, 9 LM head,
+ * 10 output copy.  Graph capture ignores the setting. */
+int ns_engine_profile(ns_engine* eng, int32_t enable);
+int ns_engine_profile_read(ns_engine* eng, int32_t cap, int32_t* kinds, float* us, int32_t* n_out);
+
+/* ------------------------------------------------------------ single kernels
+ * The hot kernels on their own, for kernel-level checks and roofline
+ * timing.  All pointers are device memory; work goes to `stream`. */
+
+enum { NS_EPI_STORE = 0, NS_EPI_RESID = 1, NS_EPI_SILU = 2 };
+
+/* Dense projection C = A * B^T (NanoFlow review, operator table: the dense
+ * class).  A [M, K], B [N, K] row-major, element type dtype, fp32
+ * accumulation.  epi NS_EPI_STORE: C fp32 [M, N] = result; NS_EPI_RESID:
+ * C fp32 [M, N] += result; NS_EPI_SILU: B is [2N, K] (gate rows then up
+ * rows) and C (dtype) [M, N] = silu(gate) * up.  bf16 needs K % 32 == 0
+ * (NS_ESHAPE otherwise). */
+int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
+               void* C, void* stream);
+
+/* Paged GQA decode attention (nanoserve notes, changes table; NanoFlow
+ * review, operator table: decode attention).  Row i (query position
+ * row_pos[i] of the sequence whose block-table row is row_bseq[i], -1 for a
+ * padding row) attends over positions 0..row_pos[i] with scale 1/sqrt(d).
+ *   q_att: [n_rows][nkv][d/E][G][E] (E = 16 bytes / element size): the G
+ *     query heads of each KV head, 16-byte chunk by chunk;
+ *   kv_layer: one layer of the cache (layout as in ns_kv_bytes);
+ *   btab: [*][max_blocks_per_seq] block ids; out: [n_rows][nq * d];
+ *   ws: ns_op_attention_ws_bytes() bytes for split-context partials;
+ *   wg_cap: 0 or the maximum number of workgroups. */
+size_t ns_op_attention_ws_bytes(const ns_model_desc* desc, int32_t n_rows, int32_t max_blocks_per_seq);
+int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                    int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
+                    int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NS_H */

@@ -1,0 +1,125 @@
+"""Shared setup for the GPU parity tests: run a workload through the C ABI
+and through the oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from decode_step_06_amd import ns
+from decode_step_06_amd.configs import ModelShape, Workload
+from decode_step_06_amd.inputs import Batch, gen_batch, gen_weights
+from decode_step_06_amd.runner import (DeviceWeights, alloc_sequences, blocks_for, create_engine, fill_past)
+from oracle import decoder as od
+from oracle import kvcache as okv
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+# Tolerances (relative L2, max abs) over an output.
+#  bf16: the bound for bf16 activations -- one layer, or one kernel, given the
+#        same inputs on both sides.
+#  bf16_stack: a whole multi-layer stack.  GPU and oracle round to bf16 at
+#        the same storage points, but from fp32 vs fp64 values, so some
+#        roundings land on neighbouring bf16 values; such differences are
+#        re-rounded at every later storage point and compound with depth
+#        until they reach the size of bf16 rounding noise itself.  With
+#        relative RMS rounding noise 2^-8 / sqrt(3) ~ 2.3e-3 per storage point
+#        on the residual path and 2L + 1 = 49 such points in 24 layers, the
+#        compounded bound is 2.3e-3 * sqrt(49) ~ 1.6e-2; max abs scales alike
+#        (2e-2 * 7 / 2, rounded to 6e-2).
+#  f32: fp32 models at fp32 accuracy.
+TOL = {"bf16": (5e-3, 2e-2), "bf16_stack": (1.6e-2, 6e-2), "f32": (1e-5, 1e-5)}
+
+
+def assert_close(gpu, ref, dtype, what=""):
+    """Relative L2 and max abs error.  The max-abs bound is stated for
+    unit-scale activations: when the reference's RMS exceeds 1 (e.g. a
+    LLaMA-70B-shaped layer, whose down projection sums 28672 products) the
+    bound scales with it."""
+    r, m = rel_l2(gpu, ref), max_abs(gpu, ref)
+    tr, tm = TOL[dtype]
+    scale = max(1.0, float(np.sqrt(np.mean(np.square(np.asarray(ref, np.float64))))))
+    tm = tm * scale
+    say(f"  parity {what}: rel_l2={r:.3e} (<= {tr:g}) max_abs={m:.3e} (<= {tm:g}, output rms scale {scale:.2f})")
+    assert np.isfinite(np.asarray(gpu)).all(), "non-finite GPU output"
+    assert r <= tr and m <= tm, f"{what}: rel_l2 {r:.3e}, max_abs {m:.3e}"
+
+
+class Case:
+    """A workload set up on the device (weights, KV manager, cached context)."""
+
+    def __init__(self, w: Workload, weights=None, batch: Batch = None, sched=None, max_tokens=None, maxb=None,
+                 n_layers=None):
+        self.w = w
+        self.shape: ModelShape = w.model
+        self.weights = weights if weights is not None else gen_weights(self.shape, seed=w.seeds["weights"])
+        self.batch = batch if batch is not None else gen_batch(w)
+        b = self.batch
+        self.maxb = maxb or blocks_for(b.seq_lens)
+        self.max_tokens = max_tokens or b.n_rows
+        self.dw = DeviceWeights.from_numpy(self.shape, self.weights)
+        self.h = create_engine(self.shape, self.dw, b.num_blocks, b.n_seqs, self.maxb, self.max_tokens,
+                               b.free_order, sched)
+        alloc_sequences(self.h, b.seq_lens)
+        fill_past(self.h, b.past_seq, b.past_pos, b.past_k, b.past_v)
+        self.x_dev = None if b.x is None else torch.from_numpy(b.x).cuda()
+
+    @property
+    def out_cols(self):
+        return self.shape.vocab or self.shape.hidden
+
+    def ns_batch(self, rows=None):
+        b = self.batch
+        sel = slice(None) if rows is None else rows
+        x = None if self.x_dev is None else self.x_dev[sel].contiguous()
+        return ns.Batch(b.row_seq[sel], b.row_pos[sel], None if b.tokens is None else b.tokens[sel], x)
+
+    def step(self, stream=None, rows=None):
+        nb = self.ns_batch(rows)
+        n = nb.seq.shape[0]
+        out = torch.full((n, self.out_cols), float("nan"), device="cuda")
+        ns.ns_decode_step(self.h.eng, nb, out.data_ptr(), stream)
+        torch.cuda.synchronize()
+        return out
+
+    def reset_cache(self):
+        """Re-poison and re-fill the cache (a step writes its rows' K/V)."""
+        from decode_step_06_amd.runner import nan_fill_
+        nan_fill_(self.h.kv_mem, self.shape)
+        b = self.batch
+        fill_past(self.h, b.past_seq, b.past_pos, b.past_k, b.past_v)
+
+    def tables(self):
+        return ns.ns_kv_block_table(self.h.kv, self.batch.n_seqs, self.maxb)
+
+    def close(self):
+        self.h.destroy()
+        torch.cuda.synchronize()
+
+
+def oracle_run(shape, weights, batch: Batch, maxb, nano_splits=None, emulate=None):
+    alloc = okv.BlockAllocator(batch.num_blocks, batch.free_order, batch.n_seqs, maxb)
+    for s, n in enumerate(batch.seq_lens):
+        alloc.alloc(s, int(n))
+    tables = alloc.table_rows()
+    cache = od.OracleKV(shape.n_layers, batch.num_blocks, shape.n_kv_heads, shape.head_dim)
+    od.fill_past(cache, tables, batch.past_seq, batch.past_pos, batch.past_k, batch.past_v)
+    orc = od.Oracle(shape, weights, emulate_bf16=emulate)
+    out = orc.step(cache, tables, batch.row_seq, batch.row_pos, tokens=batch.tokens, x=batch.x,
+                   nano_splits=nano_splits)
+    return out, cache, tables

@@ -1,0 +1,181 @@
+"""Kernel-level parity on the GPU, through the C ABI: the dense projection
+against a float64 reference of the same product, and paged attention against
+the oracle (plus its exact special cases)."""
+import numpy as np
+import pytest
+import torch
+
+from decode_step_06_amd import ns
+from decode_step_06_amd.configs import ModelShape
+from gpu_helpers import max_abs, rel_l2, say
+from oracle import decoder as od
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_grid(a):
+    return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+
+
+GEMM_SHAPES = [(1, 64, 64), (5, 130, 96), (16, 896, 896), (17, 1152, 896), (32, 300, 128), (33, 256, 4864),
+               (64, 64, 256), (100, 520, 160), (130, 384, 512), (257, 640, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("epi", [ns.NS_EPI_STORE, ns.NS_EPI_RESID, ns.NS_EPI_SILU])
+def test_gemm_bf16_matches_float64(M, N, K, epi):
+    say(f"gemm bf16 M={M} N={N} K={K} epi={epi}")
+    rng = np.random.default_rng(M * 7 + N + K + epi)
+    A = _bf16_grid(rng.standard_normal((M, K)))
+    Bn = 2 * N if epi == ns.NS_EPI_SILU else N
+    B = _bf16_grid(rng.standard_normal((Bn, K)) * 0.05)
+    ref = A.double() @ B.double().T
+    if epi == ns.NS_EPI_SILU:
+        g, u = ref[:, :N], ref[:, N:]
+        ref = g / (1 + torch.exp(-g)) * u
+        C = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    else:
+        C0 = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32))
+        C = C0.cuda().clone()
+        if epi == ns.NS_EPI_RESID:
+            ref = ref + C0.double()
+    Ad, Bd = A.cuda(), B.cuda()
+    ns.ns_op_gemm(ns.NS_BF16, epi, M, N, K, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr())
+    torch.cuda.synchronize()
+    got = C.double().cpu().numpy()
+    ref = ref.numpy()
+    # fp32 accumulation of K products (and a final bf16 rounding for SwiGLU)
+    tol = 4e-3 if epi == ns.NS_EPI_SILU else 1e-5
+    assert rel_l2(got, ref) < tol, (rel_l2(got, ref), max_abs(got, ref))
+
+
+@pytest.mark.parametrize("epi", [ns.NS_EPI_STORE, ns.NS_EPI_RESID, ns.NS_EPI_SILU])
+def test_gemm_f32_matches_float64(epi):
+    rng = np.random.default_rng(epi)
+    M, N, K = 7, 45, 70
+    A = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))
+    Bn = 2 * N if epi == ns.NS_EPI_SILU else N
+    B = torch.from_numpy(rng.standard_normal((Bn, K)).astype(np.float32))
+    ref = A.double() @ B.double().T
+    C0 = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32))
+    if epi == ns.NS_EPI_SILU:
+        ref = ref[:, :N] / (1 + torch.exp(-ref[:, :N])) * ref[:, N:]
+    elif epi == ns.NS_EPI_RESID:
+        ref = ref + C0.double()
+    C = C0.cuda().clone()
+    Ad, Bd = A.cuda(), B.cuda()   # keep the device copies alive across the call
+    ns.ns_op_gemm(ns.NS_F32, epi, M, N, K, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr())
+    torch.cuda.synchronize()
+    assert rel_l2(C.double().cpu().numpy(), ref.numpy()) < 1e-6
+
+
+def test_gemm_rejects_unsupported_k():
+    A = torch.zeros((4, 40), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ns.NSError) as ei:
+        ns.ns_op_gemm(ns.NS_BF16, 0, 4, 4, 40, A.data_ptr(), A.data_ptr(), A.data_ptr())
+    assert ei.value.code == ns.NS_ESHAPE
+
+
+# ---------------------------------------------------------------- attention
+def _attn_setup(shape: ModelShape, ctx, seed, shuffle=True, nan_poison=True):
+    """Cache and queries for rows (one per sequence) with the given context
+    lengths; returns device buffers and the logical host copies."""
+    rng = np.random.default_rng(seed)
+    nkv, d, G = shape.n_kv_heads, shape.head_dim, shape.group
+    E = 8 if shape.dtype == "bf16" else 4
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    S = len(ctx)
+    maxb = max(-(-c // 16) for c in ctx)
+    nb = sum(-(-c // 16) for c in ctx) + 3
+    # the block order comes from its own generator so the data are the same either way
+    order = np.random.default_rng(seed + 1000).permutation(nb) if shuffle else np.arange(nb)
+    btab = -np.ones((S, maxb), np.int32)
+    k = 0
+    for s, c in enumerate(ctx):
+        for j in range(-(-c // 16)):
+            btab[s, j] = order[k]
+            k += 1
+    desc = ns.model_desc(shape)
+    kvb = ns.ns_kv_bytes(desc, nb) // shape.n_layers
+    # physical layout (documented in ns.h), built on the host: unused slots NaN
+    fill = float("nan") if nan_poison else 0.0
+    kphys = torch.full((nb, nkv, d // E, 16, E), fill, dtype=dt)
+    vphys = torch.full((nb, nkv, 16, d), fill, dtype=dt)
+    K, V = {}, {}
+    for s, c in enumerate(ctx):
+        kk = torch.from_numpy(rng.standard_normal((c, nkv, d)).astype(np.float32)).to(dt)
+        vv = torch.from_numpy(rng.standard_normal((c, nkv, d)).astype(np.float32)).to(dt)
+        K[s], V[s] = kk, vv
+        for p in range(c):
+            blk, tok = int(btab[s, p // 16]), p % 16
+            kphys[blk, :, :, tok, :] = kk[p].reshape(nkv, d // E, E)
+            vphys[blk, :, tok, :] = vv[p]
+    kv = torch.cat([kphys.reshape(-1).view(torch.uint8), vphys.reshape(-1).view(torch.uint8)]).cuda()
+    assert kv.numel() == kvb
+    q = torch.from_numpy(rng.standard_normal((S, shape.n_q_heads, d)).astype(np.float32)).to(dt)
+    # attention layout [S][nkv][d/E][G][E]
+    q_att = q.reshape(S, nkv, G, d // E, E).permute(0, 1, 3, 2, 4).contiguous()
+    return dict(desc=desc, kv=kv, nb=nb, btab=btab, maxb=maxb, K=K, V=V, q=q, q_att=q_att, dt=dt)
+
+
+def _attn_run(shape, st, ctx, wg_cap=0):
+    S = len(ctx)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    rowb, pos, bt = dev(np.arange(S)), dev(np.array(ctx) - 1), dev(st["btab"])
+    out = torch.full((S, shape.n_q_heads * shape.head_dim), float("nan"), dtype=st["dt"], device="cuda")
+    wsb = ns.ns_op_attention_ws_bytes(st["desc"], S, st["maxb"])
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    qa = st["q_att"].cuda()
+    ns.ns_op_attention(st["desc"], S, qa.data_ptr(), st["kv"].data_ptr(), st["nb"], rowb.data_ptr(),
+                       pos.data_ptr(), bt.data_ptr(), st["maxb"], out.data_ptr(), ws.data_ptr(), wsb, wg_cap)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().reshape(S, shape.n_q_heads, shape.head_dim)
+
+
+ATTN_SHAPES = [
+    ModelShape("qwen-attn", 1, 896, 14, 2, 64, 64, 0, False, "bf16"),
+    ModelShape("llama-attn", 1, 8192, 64, 8, 128, 64, 0, False, "bf16"),
+    ModelShape("tiny-attn", 1, 128, 4, 1, 32, 64, 0, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", ATTN_SHAPES, ids=lambda s: s.name)
+def test_attention_matches_oracle_ragged(shape):
+    ctx = [1, 2, 15, 16, 17, 63, 64, 65, 130, 511, 700]
+    if shape.n_kv_heads == 8:
+        ctx = [1, 17, 64, 300, 1024]
+    say(f"attention {shape.name} ctx={ctx}")
+    st = _attn_setup(shape, ctx, seed=1)
+    got = _attn_run(shape, st, ctx)
+    for s, c in enumerate(ctx):
+        ref, _ = od.attention_row(st["q"][s].double().numpy(), st["K"][s].double().numpy(),
+                                  st["V"][s].double().numpy(), shape.group)
+        tol = 4e-3 if shape.dtype == "bf16" else 1e-5   # output stored in bf16
+        assert rel_l2(got[s], ref) < tol, (s, c, rel_l2(got[s], ref))
+
+
+@pytest.mark.parametrize("shape", ATTN_SHAPES[:2], ids=lambda s: s.name)
+def test_attention_single_cached_token_returns_v_exactly(shape):
+    ctx = [1] * 5
+    st = _attn_setup(shape, ctx, seed=2)
+    got = _attn_run(shape, st, ctx)
+    for s in range(5):
+        for h in range(shape.n_q_heads):
+            np.testing.assert_array_equal(got[s, h], st["V"][s][0, h // shape.group].float().numpy())
+
+
+def test_attention_shuffled_table_equals_identity_bit_exact():
+    shape = ATTN_SHAPES[0]
+    ctx = [37, 300, 64, 129]
+    a = _attn_run(shape, _attn_setup(shape, ctx, seed=3, shuffle=True), ctx)
+    b = _attn_run(shape, _attn_setup(shape, ctx, seed=3, shuffle=False), ctx)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_attention_workgroup_cap_is_bit_exact():
+    shape = ATTN_SHAPES[1]
+    ctx = [100, 1024, 333, 5]
+    st = _attn_setup(shape, ctx, seed=4)
+    a = _attn_run(shape, st, ctx, wg_cap=0)
+    b = _attn_run(shape, st, ctx, wg_cap=7)
+    np.testing.assert_array_equal(a, b)

@@ -1,0 +1,210 @@
+"""Whole decode steps on the GPU through the C ABI against the oracle, and
+the bit-exact self-consistency checks (graph = eager, overlapped nano-batches
+= serial, padding rows inert, repeat runs identical)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from decode_step_06_amd import ns
+from decode_step_06_amd.configs import QWEN05B, TINY, ModelShape, Workload, WORKLOADS
+from decode_step_06_amd.inputs import gen_batch, gen_weights
+from gpu_helpers import Case, assert_close, oracle_run, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ModelShape("small", 2, 256, 8, 2, 64, 512, 1000, True, "bf16")
+SMALL_NOVOCAB = ModelShape("small_h", 2, 256, 8, 2, 64, 512, 0, False, "bf16")
+
+
+def _small_workload(shape, name="small", nano=()):
+    return Workload(name, shape, 6, ctx_range=(1, 200), prefill_chunks=(40, 25), nano_splits=nano)
+
+
+def test_tiny_fp32_layer_matches_oracle():
+    w = WORKLOADS["tiny_b4"]
+    say("step tiny_b4 (fp32, one layer, shuffled 16-block pool)")
+    c = Case(w)
+    try:
+        got = c.step().cpu().numpy()
+        ref, cache, tables = oracle_run(w.model, c.weights, c.batch, c.maxb)
+        assert_close(got, ref, "f32", "tiny_b4 hidden out")
+        # the K/V this step wrote, read back in logical order
+        np.testing.assert_array_equal(c.tables(), np.array(tables, dtype=np.int32))
+        slots = ns.ns_slot_map(c.h.kv, c.batch.row_seq, c.batch.row_pos)
+        n = len(slots)
+        k = torch.empty((n, TINY.n_kv_heads, TINY.head_dim), device="cuda")
+        v = torch.empty_like(k)
+        sd = torch.from_numpy(slots).cuda()
+        ns.ns_kv_gather(c.h.eng, 0, n, sd.data_ptr(), k.data_ptr(), v.data_ptr())
+        torch.cuda.synchronize()
+        assert_close(k.cpu().numpy(), cache.k[0][slots], "f32", "written K")
+        assert_close(v.cpu().numpy(), cache.v[0][slots], "f32", "written V")
+    finally:
+        c.close()
+
+
+@pytest.mark.parametrize("shape", [SMALL, SMALL_NOVOCAB], ids=lambda s: s.name)
+def test_small_bf16_stack_matches_oracle(shape):
+    w = _small_workload(shape)
+    say(f"step {shape.name}: 6 decode rows + prefill chunks 40, 25")
+    c = Case(w)
+    try:
+        got = c.step().cpu().numpy()
+        ref, _, _ = oracle_run(shape, c.weights, c.batch, c.maxb)
+        assert_close(got, ref, "bf16", f"{shape.name} out")
+    finally:
+        c.close()
+
+
+@pytest.mark.parametrize("wname", ["qwen05b_b32_ctx512", "qwen05b_b1_ctx512"])
+def test_qwen05b_one_layer_matches_oracle(wname):
+    """One Qwen2.5-0.5B-shaped layer (hidden in, hidden out) at the full
+    batch and context: the bf16-activation bound applies as stated."""
+    w0 = WORKLOADS[wname]
+    shape = replace(QWEN05B, n_layers=1, vocab=0, tied=False)
+    w = replace(w0, model=shape)
+    say(f"layer {wname}: one Qwen-shaped layer")
+    c = Case(w)
+    try:
+        got = c.step().cpu().numpy()
+        ref, _, _ = oracle_run(shape, c.weights, c.batch, c.maxb)
+        assert_close(got, ref, "bf16", f"{wname} layer out")
+    finally:
+        c.close()
+
+
+@pytest.mark.parametrize("wname", ["qwen05b_b32_ctx512", "qwen05b_b1_ctx512"])
+def test_qwen05b_full_step_matches_oracle(wname):
+    """The 24-layer Qwen2.5-0.5B-shaped step at full size (logits of every
+    row), against the depth-compounded bound (STACK_TOL)."""
+    w = WORKLOADS[wname]
+    say(f"step {wname}: 24 layers, vocab 151936")
+    weights = gen_weights(w.model, seed=0)
+    c = Case(w, weights=weights)
+    try:
+        got = c.step().cpu().numpy()
+        ref, _, _ = oracle_run(w.model, weights, c.batch, c.maxb)
+        assert_close(got, ref, "bf16_stack", f"{wname} logits")
+        agree = (np.argmax(got, 1) == np.argmax(ref, 1)).mean()
+        say(f"  argmax agreement {agree:.3f}")
+        assert agree >= 0.9
+    finally:
+        c.close()
+
+
+def _graph_case():
+    w = _small_workload(SMALL, nano=(30, 41))
+    return Case(w, sched=ns.make_sched(nano_rows=(30, 41), overlap=True), max_tokens=80)
+
+
+def test_graph_replay_equals_eager_bit_exact():
+    c = _graph_case()
+    st = torch.cuda.Stream()
+    try:
+        n = c.batch.n_rows
+        eager = c.step().cpu()
+        c.reset_cache()
+        out = torch.full((n, SMALL.vocab), float("nan"), device="cuda")
+        with torch.cuda.stream(st):
+            g = ns.ns_graph_capture(c.h.eng, n, out.data_ptr(), st)
+        try:
+            for rep in range(3):  # replays with the program's own work in between
+                c.reset_cache()
+                ns.ns_graph_replay(g, c.ns_batch(), st)
+                st.synchronize()
+                torch.testing.assert_close(out.cpu(), eager, rtol=0, atol=0)
+                _ = torch.randn(1000, device="cuda").sum().item()
+        finally:
+            ns.ns_graph_destroy(g)
+    finally:
+        c.close()
+
+
+def test_graph_replay_with_changing_metadata_matches_eager():
+    """Back-to-back replays with different rows: the pinned metadata staging
+    must not be overwritten while a copy is in flight."""
+    c = _graph_case()
+    st = torch.cuda.Stream()
+    try:
+        n = c.batch.n_rows
+        sub = np.arange(0, 6)             # decode rows only
+        eager_full = c.step().cpu()
+        c.reset_cache()
+        eager_sub = c.step(rows=sub).cpu()
+        c.reset_cache()
+        out = torch.full((n, SMALL.vocab), float("nan"), device="cuda")
+        g = ns.ns_graph_capture(c.h.eng, n, out.data_ptr(), st)
+        try:
+            ns.ns_graph_replay(g, c.ns_batch(), st)
+            st.synchronize()
+            torch.testing.assert_close(out.cpu(), eager_full, rtol=0, atol=0)
+            c.reset_cache()
+            ns.ns_graph_replay(g, c.ns_batch(sub), st)   # 6 real rows, the rest padding
+            st.synchronize()
+            torch.testing.assert_close(out[: len(sub)].cpu(), eager_sub, rtol=0, atol=0)
+        finally:
+            ns.ns_graph_destroy(g)
+    finally:
+        c.close()
+
+
+def test_overlap_equals_serial_and_split_matches_unsplit():
+    w = _small_workload(SMALL)
+    c = Case(w, max_tokens=80)
+    try:
+        base = c.step().cpu()
+        for sched in (ns.make_sched(nano_rows=(30, 41)), ns.make_sched(nano_rows=(30, 41), overlap=True),
+                      ns.make_sched(nano_rows=(10, 20, 20, 21), qkv_rows=(16, 16, 16, 23), overlap=True)):
+            ns.ns_engine_set_sched(c.h.eng, sched)
+            c.reset_cache()
+            got = c.step().cpu()
+            # same kernels on the same rows in a different order: bit-exact
+            torch.testing.assert_close(got, base, rtol=0, atol=0)
+    finally:
+        c.close()
+
+
+def test_repeat_runs_are_identical_and_launch_count():
+    c = Case(_small_workload(SMALL))
+    try:
+        a = c.step().cpu()
+        c.reset_cache()
+        b = c.step().cpu()
+        torch.testing.assert_close(a, b, rtol=0, atol=0)
+        launches = ns.ns_engine_last_launches(c.h.eng)
+        say(f"  kernels per step (2 layers): {launches}")
+        assert launches <= 2 + 2 * 10 + 2
+    finally:
+        c.close()
+
+
+def test_step_errors_are_reported_without_side_effects():
+    c = Case(_small_workload(SMALL))
+    try:
+        b = c.batch
+        bad_pos = b.row_pos.copy()
+        bad_pos[0] = 10_000
+        with pytest.raises(ns.NSError) as ei:
+            out = torch.empty((b.n_rows, SMALL.vocab), device="cuda")
+            ns.ns_decode_step(c.h.eng, ns.Batch(b.row_seq, bad_pos, b.tokens), out.data_ptr())
+        assert ei.value.code == ns.NS_ESHAPE
+        bad_tok = b.tokens.copy()
+        bad_tok[1] = SMALL.vocab
+        with pytest.raises(ns.NSError) as ei:
+            ns.ns_decode_step(c.h.eng, ns.Batch(b.row_seq, b.row_pos, bad_tok), out.data_ptr())
+        assert ei.value.code == ns.NS_EINVAL
+        with pytest.raises(ns.NSError) as ei:
+            ns.ns_graph_capture(c.h.eng, 8, out.data_ptr(), None)
+        assert ei.value.code == ns.NS_EINVAL
+        with pytest.raises(ns.NSError) as ei:
+            ns.ns_graph_capture(c.h.eng, c.max_tokens + 1, out.data_ptr(), torch.cuda.Stream())
+        assert ei.value.code == ns.NS_ESHAPE
+        # the engine still works afterwards
+        c.reset_cache()
+        got = c.step().cpu().numpy()
+        ref, _, _ = oracle_run(SMALL, c.weights, b, c.maxb)
+        assert_close(got, ref, "bf16", "after errors")
+    finally:
+        c.close()
