@@ -293,6 +293,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ns.lib()
     stream = torch.cuda.Stream()
+    # a plain device copy of known size: calibrates the HBM byte counters
+    # (FETCH_SIZE / WRITE_SIZE) of a profiled run of this same command
+    calib_bytes = 256 << 20
+    calib_src = torch.ones(calib_bytes // 4, device="cuda")
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
     w, weights, b, h, maxb = setup_step(WORKLOAD)
     try:
         runs, eager, launches = run_step_bench(h, b, args.steps, args.warmup, args.warm_seconds, stream)
@@ -326,6 +334,7 @@ def main():
         "config": {"workload": w.name, "batch": b.n_rows, "context": int(w.decode_ctx), "layers": w.model.n_layers,
                    "kv_block": 16, "mode": "hipGraph replay", "parallelism": "single GPU"},
         "roofline": roof,
+        "calibration_copy_bytes": calib_bytes,
         "step": {"runs_ms": [round(r * 1e3, 4) for r in runs],
                  "runs_disagree_over_15pct": bool(max(runs) > 1.15 * min(runs)),
                  "eager_ms": round(eager * 1e3, 4), "fixed_cost_ms": round((eager - step_s) * 1e3, 4),

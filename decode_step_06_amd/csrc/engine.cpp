@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -35,28 +36,54 @@ size_t kv_layer_bytes(const ns_model_desc* d, int32_t num_blocks);
 
 namespace {
 
-constexpr int kAttnTargetWaves = 2048;  // attention wavefronts to aim for (8 per CU)
 constexpr int kMaxParts = 4;
+constexpr int kDecodeRows = 64;  // steps of at most this many rows use the weight-streaming split-K path
+constexpr int kMaxSlices = 8;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int elem_size(int32_t dtype) { return dtype == NS_BF16 ? 2 : 4; }
 
-// Context partition size (tokens, a multiple of 64) and partition count for
-// a batch of n_rows rows when sequences hold at most cap_tokens tokens.  It
-// depends only on the whole batch's row count, so a nano-batched step and an
-// unsplit step, eager and captured, partition identically.
-void attn_partition(int n_rows, int nkv, int cap_tokens, int* part_tokens, int* n_parts) {
+// Attention launch shape for a batch of n_rows rows when sequences hold at
+// most cap_tokens tokens: partition size (tokens, a multiple of 64),
+// partitions per row, and wavefronts per work item (row, KV head,
+// partition).  When rows x KV heads alone fill the chip (>= 2048 items), one
+// wavefront per item streams the whole context; otherwise 4 wavefronts take
+// interleaved 64-token passes and the partition count minimises a simple
+// cost: passes per wavefront (each is mostly memory latency), scaled up when
+// the wavefronts exceed what the chip keeps resident (about 4096), plus the
+// combine launch when the context is split.  The shape depends only on the
+// whole batch's row count and the capacity, so nano-batched and unsplit
+// steps, eager and captured, compute identically.
+void attn_partition(int n_rows, int nkv, int cap_tokens, int* part_tokens, int* n_parts, int* waves) {
   const int chunks = std::max(1, (cap_tokens + 63) / 64);
   const long items = std::max(1L, (long)n_rows * nkv);
-  int want = (int)std::max(1L, (kAttnTargetWaves + items - 1) / items);
-  want = std::min(want, chunks);
-  const int per = (chunks + want - 1) / want;
+  if (items >= 2048) {
+    *waves = 1;
+    *part_tokens = 64 * chunks;
+    *n_parts = 1;
+    return;
+  }
+  *waves = 4;
+  int best_parts = 1;
+  double best = 1e30;
+  for (int parts = 1; parts <= chunks; parts *= 2) {
+    const int per = (chunks + parts - 1) / parts;
+    const double passes = std::ceil(per / 4.0);
+    const double wv = (double)items * 4 * parts;
+    const double cost = passes * std::max(1.0, wv / 4096.0) + (parts > 1 ? 2.0 : 0.0);
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_parts = parts;
+    }
+  }
+  const int per = (chunks + best_parts - 1) / best_parts;
   *part_tokens = 64 * per;
   *n_parts = (chunks + per - 1) / per;
 }
 
 struct Plan {
-  size_t x, h, qkv, q_att, o, act, cosb, sinb, meta, part_acc, part_ml, total;
+  size_t x, h, qkv, q_att, o, act, cosb, sinb, meta, part_acc, part_ml, part_qkv, part_res, total;
+  int tdec;  // rows of the split-K slice buffers (decode steps: at most 64 rows)
   size_t meta_ints;  // int32 entries of the metadata block
 };
 
@@ -82,12 +109,19 @@ Plan make_plan(const ns_model_desc* d, int T, int maxb) {
   p.meta = take(p.meta_ints * 4);
   long items = 0;
   for (int n = 1; n <= T; ++n) {
-    int P, np;
-    attn_partition(n, d->n_kv_heads, maxb * NS_BLOCK_SIZE, &P, &np);
+    int P, np, nw;
+    attn_partition(n, d->n_kv_heads, maxb * NS_BLOCK_SIZE, &P, &np, &nw);
     if (np > 1) items = std::max(items, (long)n * d->n_kv_heads * np);
   }
   p.part_acc = take((size_t)items * G * d->head_dim * 4);
   p.part_ml = take((size_t)items * G * 2 * 4);
+  // split-K slices of decode steps (bf16 models, <= 64 rows): the QKV result,
+  // and the O / down projections' residual adds (up to 8 slices each)
+  p.tdec = std::min(T, kDecodeRows);
+  const int qkv_w = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  const bool dec = d->dtype == NS_BF16;
+  p.part_qkv = take(dec ? (size_t)kMaxSlices * p.tdec * qkv_w * 4 : 0);
+  p.part_res = take(dec ? (size_t)kMaxSlices * p.tdec * d->hidden * 4 : 0);
   p.total = off;
   return p;
 }
@@ -162,6 +196,8 @@ struct ns_engine {
   int32_t* m_pos() const { return meta() + 2 * max_tokens; }
   int32_t* m_slot() const { return meta() + 3 * max_tokens; }
   int32_t* m_btab() const { return meta() + 4 * max_tokens; }
+  float* part_qkv() const { return (float*)(ws + plan.part_qkv); }
+  float* part_res() const { return (float*)(ws + plan.part_res); }
   char* k_layer(int l) const { return kv_dev + (size_t)l * kv_layer; }
   char* v_layer(int l) const { return kv_dev + (size_t)l * kv_layer + kv_layer / 2; }
 };
@@ -272,7 +308,7 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
   a->nq = e->d.n_q_heads;
   a->nkv = e->d.n_kv_heads;
   a->d = e->d.head_dim;
-  attn_partition(n_tok, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, &a->part_tokens, &a->n_parts);
+  attn_partition(n_tok, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, &a->part_tokens, &a->n_parts, &a->waves);
   a->wg_cap = e->sched.attn_wg_cap;
 }
 
@@ -314,35 +350,56 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
     if (_rc) return _rc;        \
   } while (0)
 
-  if (d.vocab > 0) {
-    ns::launch_embed(dt, e->embed, e->m_tok(), e->x(), n_tok, H, d.vocab, st);
-    ++launches;
-    MARK(K_EMBED);
-  }
-  ns::launch_rope_table(e->m_pos(), e->cosb(), e->sinb(), n_tok, hd, d.rope_base, st);
+  // embedding (or the hidden input already in x), RoPE table, layer 0's norm
+  ns::launch_step_prologue(dt, d.vocab > 0 ? e->embed : nullptr, e->m_tok(), e->x(), e->m_pos(), e->cosb(),
+                           e->sinb(), e->attn_norm[0], e->h(), n_tok, H, d.vocab, hd, d.rope_base, d.rms_eps, st);
   ++launches;
-  MARK(K_ROPE_TABLE);
+  MARK(K_EMBED);
 
   char* h = (char*)e->h();
   char* o = (char*)e->o();
   char* act = (char*)e->act();
   float* x = e->x();
   float* qkv = e->qkv();
+  // Decode steps (bf16, <= 64 rows): the projections stream their weights
+  // with K split across workgroups; each split writes an fp32 slice and the
+  // next kernel on those rows (RoPE/cache write, or the next RMSNorm, or the
+  // output) sums the slices in order -- the residual add of the O and down
+  // projections happens there.
+  const bool dec = dt == NS_DT_BF16 && n_tok <= e->plan.tdec;
+  const long sq = (long)e->plan.tdec * QKV, sr = (long)e->plan.tdec * H;  // slice strides
+  const int S_qkv = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(QKV, H)) : 1;
+  const int S_o = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(H, DQ)) : 1;
+  const int S_d = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(H, F)) : 1;
+  float* pq = e->part_qkv();
+  float* pr = e->part_res();
   for (int l = 0; l < d.n_layers; ++l) {
     for (size_t j = 0; j < qparts.size(); ++j) {
       const int r0 = qparts[j].first, n = qparts[j].second - r0;
-      ns::launch_rmsnorm(dt, x + (size_t)r0 * H, e->attn_norm[l], h + r0 * H * es, n, H, d.rms_eps, st);
-      MARK(K_NORM);
-      if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n, QKV, H, h + r0 * H * es, H, e->wqkv[l], H,
-                          qkv + (size_t)r0 * QKV, QKV, st))
+      if (l > 0) {  // layer 0's norm ran in the prologue
+        if (dec)      // finishing the previous layer's down projection
+          ns::launch_rmsnorm_reduce(dt, x + (size_t)r0 * H, pr + (size_t)r0 * H, sr, S_d, e->attn_norm[l],
+                                    h + r0 * H * es, n, H, d.rms_eps, st);
+        else
+          ns::launch_rmsnorm(dt, x + (size_t)r0 * H, e->attn_norm[l], h + r0 * H * es, n, H, d.rms_eps, st);
+        ++launches;
+        MARK(K_NORM);
+      }
+      if (dec) {
+        if (ns::launch_gemm_partial(n, QKV, H, h + r0 * H * es, H, e->wqkv[l], H, pq + (size_t)r0 * QKV, QKV, sq,
+                                    S_qkv, st))
+          NS_FAIL(NS_ESHAPE, "unsupported QKV projection shape");
+      } else if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n, QKV, H, h + r0 * H * es, H, e->wqkv[l], H,
+                                 qkv + (size_t)r0 * QKV, QKV, st)) {
         NS_FAIL(NS_ESHAPE, "unsupported QKV projection shape");
+      }
       MARK(K_QKV);
-      ns::launch_rope_kv(dt, qkv + (size_t)r0 * QKV, e->cosb() + (size_t)r0 * hd / 2,
-                         e->sinb() + (size_t)r0 * hd / 2, e->m_slot() + r0,
+      ns::launch_rope_kv(dt, (dec ? pq : qkv) + (size_t)r0 * QKV, dec ? sq : 0, S_qkv,
+                         e->cosb() + (size_t)r0 * hd / 2, e->sinb() + (size_t)r0 * hd / 2, e->m_slot() + r0,
                          (char*)e->q_att() + (size_t)r0 * DQ * es, e->k_layer(l), e->v_layer(l), n, nq, nkv, hd,
                          st);
       MARK(K_ROPE_KV);
-      launches += 3;
+      launches += 2;
       ns::AttnArgs a;
       attn_args(e, l, r0, r0 + n, n_tok, &a);
       if (overlap) {
@@ -359,32 +416,50 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
       if (overlap)
         for (size_t j = 0; j < qparts.size(); ++j)
           if (qparts[j].first < r1 && qparts[j].second > r0) HIP_TRY(hipStreamWaitEvent(st, e->ev_att[j], 0));
-      if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, DQ, o + r0 * DQ * es, DQ, e->wo[l], DQ, x + (size_t)r0 * H,
-                          H, st))
+      if (dec) {
+        if (ns::launch_gemm_partial(n, H, DQ, o + r0 * DQ * es, DQ, e->wo[l], DQ, pr + (size_t)r0 * H, H, sr, S_o,
+                                    st))
+          NS_FAIL(NS_ESHAPE, "unsupported O projection shape");
+      } else if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, DQ, o + r0 * DQ * es, DQ, e->wo[l], DQ,
+                                 x + (size_t)r0 * H, H, st)) {
         NS_FAIL(NS_ESHAPE, "unsupported O projection shape");
+      }
       MARK(K_O);
-      ns::launch_rmsnorm(dt, x + (size_t)r0 * H, e->mlp_norm[l], h + r0 * H * es, n, H, d.rms_eps, st);
+      if (dec)
+        ns::launch_rmsnorm_reduce(dt, x + (size_t)r0 * H, pr + (size_t)r0 * H, sr, S_o, e->mlp_norm[l],
+                                  h + r0 * H * es, n, H, d.rms_eps, st);
+      else
+        ns::launch_rmsnorm(dt, x + (size_t)r0 * H, e->mlp_norm[l], h + r0 * H * es, n, H, d.rms_eps, st);
       MARK(K_NORM);
       if (ns::launch_gemm(dt, ns::EPI_SILU_MUL, n, F, H, h + r0 * H * es, H, e->wgu[l], H, act + r0 * F * es, F,
                           st))
         NS_FAIL(NS_ESHAPE, "unsupported gate-up projection shape");
       MARK(K_GU);
-      if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, F, act + r0 * F * es, F, e->wdown[l], F,
-                          x + (size_t)r0 * H, H, st))
+      if (dec) {
+        if (ns::launch_gemm_partial(n, H, F, act + r0 * F * es, F, e->wdown[l], F, pr + (size_t)r0 * H, H, sr, S_d,
+                                    st))
+          NS_FAIL(NS_ESHAPE, "unsupported down projection shape");
+      } else if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, F, act + r0 * F * es, F, e->wdown[l], F,
+                                 x + (size_t)r0 * H, H, st)) {
         NS_FAIL(NS_ESHAPE, "unsupported down projection shape");
+      }
       MARK(K_DOWN);
       launches += 4;
     }
   }
   if (d.vocab > 0) {
-    ns::launch_rmsnorm(dt, x, e->final_norm, h, n_tok, H, d.rms_eps, st);
+    if (dec)
+      ns::launch_rmsnorm_reduce(dt, x, pr, sr, S_d, e->final_norm, h, n_tok, H, d.rms_eps, st);
+    else
+      ns::launch_rmsnorm(dt, x, e->final_norm, h, n_tok, H, d.rms_eps, st);
     MARK(K_NORM);
     if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n_tok, d.vocab, H, h, H, e->lm_head, H, out, d.vocab, st))
       NS_FAIL(NS_ESHAPE, "unsupported LM head shape");
     MARK(K_LM_HEAD);
     launches += 2;
   } else {
-    ns::launch_copy_rows(x, (float*)out, (long)n_tok * H, st);
+    if (dec) ns::launch_reduce_rows(x, pr, sr, S_d, (float*)out, n_tok, H, st);
+    else ns::launch_copy_rows(x, (float*)out, (long)n_tok * H, st);
     ++launches;
     MARK(K_COPY);
   }
@@ -661,8 +736,8 @@ int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, cons
 
 size_t ns_op_attention_ws_bytes(const ns_model_desc* desc, int32_t n_rows, int32_t max_blocks_per_seq) {
   if (ns::check_desc(desc) != NS_OK || n_rows <= 0 || max_blocks_per_seq <= 0) return 0;
-  int P, np;
-  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &P, &np);
+  int P, np, nw;
+  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &P, &np, &nw);
   const int G = desc->n_q_heads / desc->n_kv_heads;
   const size_t items = (size_t)n_rows * desc->n_kv_heads * np;
   return align_up(items * G * desc->head_dim * 4, 256) + align_up(items * G * 2 * 4, 256);
@@ -697,7 +772,8 @@ int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att
   a.nq = desc->n_q_heads;
   a.nkv = desc->n_kv_heads;
   a.d = desc->head_dim;
-  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &a.part_tokens, &a.n_parts);
+  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &a.part_tokens, &a.n_parts,
+                 &a.waves);
   const int G2 = G;
   const size_t items = (size_t)n_rows * desc->n_kv_heads * a.n_parts;
   a.part_acc = (float*)ws;

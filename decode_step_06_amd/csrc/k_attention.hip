@@ -7,9 +7,12 @@
 // over keys 0..pos of its sequence, reading KV head h / G.
 //
 // Design (MI355X-first):
-//  * one wavefront per work item (row, KV head, partition of the context);
-//    it streams each K/V block of its KV head exactly once for all G query
-//    heads of the group, so the HBM traffic is the cache bytes themselves;
+//  * one workgroup of 1 or 4 wavefronts per work item (row, KV head,
+//    partition of the context): 4 when there are few items (small batches),
+//    1 when items alone fill the chip; the wavefronts take interleaved
+//    64-token passes and each
+//    K/V block of the KV head is streamed exactly once for all G query heads
+//    of the group, so the HBM traffic is the cache bytes themselves;
 //  * QK: lane = token (64 tokens = 4 blocks per pass).  The K cache stores
 //    each block as 16-byte chunks interleaved over its 16 tokens, so for every
 //    chunk the 16 lanes of a block read 256 contiguous bytes.  The q values
@@ -22,10 +25,10 @@
 //    V rows are read 16 bytes per lane, a whole block row per 64/TL lanes;
 //  * all K and V loads of a pass are issued before any arithmetic, so each
 //    wavefront keeps 2 x 64 tokens of KV in flight;
-//  * split-K over context partitions (a multiple of 64 tokens) gives enough
-//    wavefronts for small batches; a combine kernel merges the partials with
-//    the usual max/sum rescaling.  A row that fits one partition writes its
-//    output directly.
+//  * the wavefronts of a workgroup merge their (max, sum, accumulator)
+//    triples in LDS; split context partitions (a multiple of 64 tokens, for
+//    long contexts with few rows) write partials that a combine kernel merges
+//    the same way.  A row that fits one partition writes its output directly.
 #include "ns_kernels.h"
 
 namespace ns {
@@ -77,23 +80,18 @@ __device__ __forceinline__ void unpack_chunk(const u32x4_t& v, float* f, float) 
   f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 
-__device__ __forceinline__ void store_chunk(bf16_t* p, const float* f) {
-  u32x4_t v;
-  v.x = pack_bf16(f[0], f[1]); v.y = pack_bf16(f[2], f[3]);
-  v.z = pack_bf16(f[4], f[5]); v.w = pack_bf16(f[6], f[7]);
-  *(u32x4_t*)p = v;
-}
-__device__ __forceinline__ void store_chunk(float* p, const float* f) {
-  *(f32x4_t*)p = f32x4_t{f[0], f[1], f[2], f[3]};
-}
-
 }  // namespace
 
 // Pointers are separate __restrict__ parameters (not struct members) so the
 // compiler can prove the wavefront-uniform q and block-table reads are never
 // clobbered and serve them from the scalar cache.
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(64) attn_decode_kernel(
+//
+// A workgroup of NWAVE wavefronts owns one work item (row, KV head, context
+// partition); wavefront w takes the 64-token passes w, w + NWAVE, ... of the
+// partition with its own running max, sums and accumulators, and the
+// wavefronts' results are merged in LDS in wavefront order (deterministic).
+template <typename T, int D, int G, int NWAVE>
+__global__ void __launch_bounds__(64 * NWAVE) attn_decode_kernel(
     const T* __restrict__ qatt, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ row_bseq, const int32_t* __restrict__ row_pos, const int32_t* __restrict__ btab,
     T* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml, int maxb, int row0, int n_rows,
@@ -105,9 +103,11 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(
   // than this (log2 units): exp2 of at most 2^8 cannot overflow, and the
   // final division by the summed weights cancels the common factor.
   constexpr float kSlack = 8.0f;
-  __shared__ float plds[64][8];
+  __shared__ float plds[NWAVE][64][8];  // a wavefront's probabilities, token x head
+  __shared__ float macc[NWAVE][G][D];   // per-wavefront accumulators for the merge
+  __shared__ float mml[NWAVE][G][2];    // per-wavefront shift and sum
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int pj = lane / NCH, pc = lane % NCH;  // PV layout
   const int total = n_rows * nkv * n_parts;
 
@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(
     T* outp = out + (long)t * nq * D + (long)g * G * D;
     if (bs < 0) {  // padding row: zero output
       if (part == 0)
-        for (int i = lane; i < G * D; i += 64) outp[i] = T(0);
+        for (int i = threadIdx.x; i < G * D; i += 64 * NWAVE) outp[i] = T(0);
       continue;
     }
     const int ctx = row_pos[t] + 1;
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(
       for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
 
-    for (int c0 = start; c0 < end; c0 += 64) {
+    for (int c0 = start + 64 * wave; c0 < end; c0 += 64 * NWAVE) {
       // Block ids of this pass's 4 blocks (wavefront-uniform).
       int blk[4];
 #pragma unroll
@@ -206,15 +206,18 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(
         l[h] += pr[h];
       }
 #pragma unroll
-      for (int h = 0; h < 8; ++h) plds[lane][h] = h < G ? pr[h] : 0.f;
-      __syncthreads();
+      for (int h = 0; h < 8; ++h) plds[wave][lane][h] = h < G ? pr[h] : 0.f;
+      // the probabilities cross lanes within the wavefront only
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
       // PV: lane = (token lane pj, chunk pc).
 #pragma unroll
       for (int it = 0; it < NCH; ++it) {
         const int tl = it * TL + pj;
-        const f32x4_t p0 = *(const f32x4_t*)&plds[tl][0];
-        const f32x4_t p1 = *(const f32x4_t*)&plds[tl][4];
+        const f32x4_t p0 = *(const f32x4_t*)&plds[wave][tl][0];
+        const f32x4_t p1 = *(const f32x4_t*)&plds[wave][tl][4];
         const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
         float vf[E];
         unpack_chunk(vr[it], vf, T());
@@ -223,11 +226,14 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(
 #pragma unroll
           for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv[h], vf[e], acc[h][e]);
       }
-      __syncthreads();
+      // the next pass overwrites this wavefront's probabilities
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // Finish: sum the per-lane softmax denominators and the PV partials of
-    // the token lanes.
+    // Finish the wavefront: sum the per-lane softmax denominators and the PV
+    // partials of the token lanes.
     float lsum[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) lsum[h] = wave_sum(l[h]);
@@ -238,39 +244,47 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
 
-    if (nparts_row == 1) {
-      if (lane < NCH) {
+    // Merge the wavefronts: M = max m_w, L = sum l_w 2^(m_w - M),
+    // acc = sum acc_w 2^(m_w - M), in wavefront order.  A wavefront that had
+    // no pass contributes m = -1e30, l = 0, acc = 0 (weight 0).
+    if (lane < NCH) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float o[E];
-          const float inv = 1.0f / lsum[h];
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = acc[h][e] * inv;
-          store_chunk(outp + (long)h * D + pc * E, o);
-        }
+        for (int e = 0; e < E; ++e) macc[wave][h][pc * E + e] = acc[h][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        mml[wave][h][0] = m[h];
+        mml[wave][h][1] = lsum[h];
       }
-    } else {
-      const long item = ((long)t * nkv + g) * n_parts + part;
-      if (lane < NCH) {
-        float* pa = part_acc + item * G * D;
+    }
+    __syncthreads();
+    const long item = ((long)t * nkv + g) * n_parts + part;
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NWAVE) {
+      const int h = idx / D, dd = idx % D;
+      float M = mml[0][h][0];
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-          *(f32x4_t*)(pa + (long)h * D + pc * E) = f32x4_t{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-        if constexpr (E == 8) {
+      for (int v = 1; v < NWAVE; ++v) M = fmaxf(M, mml[v][h][0]);
+      float L = 0.f, o = 0.f;
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-            *(f32x4_t*)(pa + (long)h * D + pc * E + 4) = f32x4_t{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-        }
+      for (int v = 0; v < NWAVE; ++v) {
+        const float wgt = exp2f(mml[v][h][0] - M);
+        L += mml[v][h][1] * wgt;
+        o += macc[v][h][dd] * wgt;
       }
-      if (lane == 0) {
-        float* pm = part_ml + item * G * 2;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          pm[2 * h] = m[h];
-          pm[2 * h + 1] = lsum[h];
+      if (nparts_row == 1) {
+        Elem<T>::store(outp, (long)h * D + dd, o / L);
+      } else {
+        part_acc[item * G * D + idx] = o;
+        if (dd == 0) {
+          part_ml[(item * G + h) * 2] = M;
+          part_ml[(item * G + h) * 2 + 1] = L;
         }
       }
     }
+    __syncthreads();  // the LDS is reused by the next work item
   }
 }
 
@@ -306,9 +320,14 @@ static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
   long grid = total;
   if (a.wg_cap > 0 && grid > a.wg_cap) grid = a.wg_cap;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), dim3((unsigned)grid), dim3(64), 0, st, (const T*)a.q_att,
-                     (const T*)a.kc, (const T*)a.vc, a.row_bseq, a.row_pos, a.btab, (T*)a.out, a.part_acc, a.part_ml,
-                     a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts, scale_log2);
+#define NS_ATTN_LAUNCH(NW)                                                                                         \
+  hipLaunchKernelGGL((attn_decode_kernel<T, D, G, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st,               \
+                     (const T*)a.q_att, (const T*)a.kc, (const T*)a.vc, a.row_bseq, a.row_pos, a.btab, (T*)a.out, \
+                     a.part_acc, a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts,      \
+                     scale_log2)
+  if (a.waves == 1) NS_ATTN_LAUNCH(1);
+  else NS_ATTN_LAUNCH(4);
+#undef NS_ATTN_LAUNCH
   if (a.n_parts > 1)
     hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3((unsigned)(a.n_rows * a.nkv)), dim3(256), 0, st, a);
 }

@@ -71,6 +71,91 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(hr, i, xr[i] * r * Elem<T>::load(g, i));
 }
 
+// The split-K residual add fused in front of the norm: x[t] += the slices
+// of the previous projection (slice order), written back, then the norm.
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_reduce_kernel(float* __restrict__ x, const float* __restrict__ P,
+                                                             long slice_stride, int splits, const T* __restrict__ g,
+                                                             T* __restrict__ h, int H, float eps) {
+  const int t = blockIdx.x;
+  float* xr = x + (long)t * H;
+  const float* pr = P + (long)t * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    float v = xr[i];
+    float add = 0.f;
+    for (int sp = 0; sp < splits; ++sp) add += pr[sp * slice_stride + i];
+    v += add;
+    xr[i] = v;
+    ss += v * v;
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  T* hr = h + (long)t * H;
+  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(hr, i, xr[i] * r * Elem<T>::load(g, i));
+}
+
+__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ x, const float* __restrict__ P,
+                                                          long slice_stride, int splits, float* __restrict__ out,
+                                                          int H) {
+  const int t = blockIdx.x;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    float add = 0.f;
+    for (int sp = 0; sp < splits; ++sp) add += P[sp * slice_stride + (long)t * H + i];
+    out[(long)t * H + i] = x[(long)t * H + i] + add;
+  }
+}
+
+// ---------------------------------------------------------------- step prologue
+// One workgroup per row does everything the step needs before layer 0's
+// projections: the embedding gather (models with a vocabulary; otherwise x
+// already holds the hidden input), this row's RoPE cos/sin (the table every
+// layer reads, built once per step) and layer 0's RMSNorm.  Three launches
+// become one.
+template <typename T>
+__global__ void __launch_bounds__(256) step_prologue_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
+                                                            float* __restrict__ x, const int32_t* __restrict__ pos,
+                                                            float* __restrict__ cosb, float* __restrict__ sinb,
+                                                            const T* __restrict__ g0, T* __restrict__ h, int H, int V,
+                                                            int half, double log2_base, float eps) {
+  const int t = blockIdx.x;
+  float* xr = x + (long)t * H;
+  float ss = 0.f;
+  if (E) {
+    int id = tok[t];
+    id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+    const T* src = E + (long)id * H;
+    for (int i = threadIdx.x; i < H; i += 256) {
+      const float v = Elem<T>::load(src, i);
+      xr[i] = v;
+      ss += v * v;
+    }
+  } else {
+    for (int i = threadIdx.x; i < H; i += 256) {
+      const float v = xr[i];
+      ss += v * v;
+    }
+  }
+  const double p = (double)pos[t];
+  for (int j = threadIdx.x; j < half; j += 256) {
+    const double a = p * exp2(-2.0 * j / (2.0 * half) * log2_base);
+    double sn, cs;
+    sincos(a, &sn, &cs);
+    cosb[(long)t * half + j] = (float)cs;
+    sinb[(long)t * half + j] = (float)sn;
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  T* hr = h + (long)t * H;
+  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(hr, i, xr[i] * r * Elem<T>::load(g0, i));
+}
+
 // ---------------------------------------------------------------- RoPE + KV write
 // From the QKV projection (fp32 [T, (nq + 2 nkv) d]) for one row per
 // workgroup: rotate-half RoPE on q and k with the step's table, store q in
@@ -78,15 +163,30 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
 // chunk by chunk, so attention reads them as one uniform block), and write
 // the rotated k and the v into the paged cache at the row's slot (padding
 // rows, slot < 0, write no K/V).
+//
+// With splits > 1 the projection result arrives as fp32 slices (split K); the
+// row is first summed in slice order into LDS.
 template <typename T>
-__global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ qkv, const float* __restrict__ cosb,
+__global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ qkv, long slice_stride, int splits,
+                                                      const float* __restrict__ cosb,
                                                       const float* __restrict__ sinb, const int32_t* __restrict__ slot,
                                                       T* __restrict__ q_att, T* __restrict__ kc, T* __restrict__ vc,
                                                       int nq, int nkv, int d) {
   constexpr int E = Elem<T>::per16;
+  extern __shared__ float rowbuf[];
   const int t = blockIdx.x;
   const int half = d >> 1, G = nq / nkv, nch = d / E;
-  const float* row = qkv + (long)t * (nq + 2 * nkv) * d;
+  const int width = (nq + 2 * nkv) * d;
+  const float* row = qkv + (long)t * width;
+  if (splits > 1) {
+    for (int i = threadIdx.x; i < width; i += 256) {
+      float v = 0.f;
+      for (int sp = 0; sp < splits; ++sp) v += row[sp * slice_stride + i];
+      rowbuf[i] = v;
+    }
+    __syncthreads();
+    row = rowbuf;
+  }
   const float* cr = cosb + (long)t * half;
   const float* sr = sinb + (long)t * half;
   const int s = slot[t];
@@ -188,6 +288,19 @@ void launch_rope_table(const int32_t* pos, float* cosb, float* sinb, int T, int 
                      half, log2((double)base));
 }
 
+void launch_step_prologue(int dtype, const void* E, const int32_t* tok, float* x, const int32_t* pos, float* cosb,
+                          float* sinb, const void* g0, void* h, int T, int H, int V, int d, float base, float eps,
+                          hipStream_t st) {
+  if (T <= 0) return;
+  const double lb = log2((double)base);
+  if (dtype == NS_DT_BF16)
+    hipLaunchKernelGGL(step_prologue_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)E, tok, x, pos, cosb,
+                       sinb, (const bf16_t*)g0, (bf16_t*)h, H, V, d / 2, lb, eps);
+  else
+    hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)E, tok, x, pos, cosb,
+                       sinb, (const float*)g0, (float*)h, H, V, d / 2, lb, eps);
+}
+
 void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st) {
   if (T <= 0) return;
   if (dtype == NS_DT_BF16)
@@ -196,15 +309,34 @@ void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, in
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, st, x, (const float*)g, (float*)h, H, eps);
 }
 
-void launch_rope_kv(int dtype, const float* qkv, const float* cosb, const float* sinb, const int32_t* slot,
-                    void* q_att, void* kc, void* vc, int T, int nq, int nkv, int d, hipStream_t st) {
+void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, const float* cosb,
+                    const float* sinb, const int32_t* slot, void* q_att, void* kc, void* vc, int T, int nq, int nkv,
+                    int d, hipStream_t st) {
+  if (T <= 0) return;
+  const size_t lds = splits > 1 ? (size_t)(nq + 2 * nkv) * d * sizeof(float) : 0;
+  if (dtype == NS_DT_BF16)
+    hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb, sinb,
+                       slot, (bf16_t*)q_att, (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
+  else
+    hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb, sinb,
+                       slot, (float*)q_att, (float*)kc, (float*)vc, nq, nkv, d);
+}
+
+void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_stride, int splits, const void* g,
+                           void* h, int T, int H, float eps, hipStream_t st) {
   if (T <= 0) return;
   if (dtype == NS_DT_BF16)
-    hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(T), dim3(256), 0, st, qkv, cosb, sinb, slot, (bf16_t*)q_att,
-                       (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
+    hipLaunchKernelGGL(rmsnorm_reduce_kernel<bf16_t>, dim3(T), dim3(256), 0, st, x, P, slice_stride, splits,
+                       (const bf16_t*)g, (bf16_t*)h, H, eps);
   else
-    hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(T), dim3(256), 0, st, qkv, cosb, sinb, slot, (float*)q_att,
-                       (float*)kc, (float*)vc, nq, nkv, d);
+    hipLaunchKernelGGL(rmsnorm_reduce_kernel<float>, dim3(T), dim3(256), 0, st, x, P, slice_stride, splits,
+                       (const float*)g, (float*)h, H, eps);
+}
+
+void launch_reduce_rows(const float* x, const float* P, long slice_stride, int splits, float* out, int T, int H,
+                        hipStream_t st) {
+  if (T <= 0) return;
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3(T), dim3(256), 0, st, x, P, slice_stride, splits, out, H);
 }
 
 void launch_kv_scatter(int dtype, const int32_t* slots, const void* k, const void* v, void* kc, void* vc, int n,

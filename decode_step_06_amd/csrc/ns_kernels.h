@@ -16,6 +16,7 @@ enum GemmEpi {
   EPI_RESID_F32 = 1,  // C fp32 [M, N] += acc              (projection + residual add)
   EPI_SILU_MUL = 2,   // C (dtype) [M, N] = silu(acc_gate) * acc_up, with the gate rows of B at
                       // [0, N) and the up rows at [N, 2N)    (gate-up projection + SwiGLU)
+  EPI_PARTIAL = 3,    // C fp32 slice s [M, N] = acc over the s-th K range (split K, decode batches)
 };
 
 // Returns 0, or -1 when the shape is unsupported (K % 32 != 0 for bf16).
@@ -23,12 +24,35 @@ int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda,
                 int ldc, hipStream_t st);
 int gemm_supported(int dtype, int K);
 
+// Split-K projection for decode batches (bf16, M <= 64): slice s of the
+// result (P + s * slice_stride, [M, N] with row stride ldp) holds the sum
+// over the s-th of `splits` contiguous K ranges; the consumer sums the
+// slices in order.  gemm_partial_splits picks the split count from N and K
+// alone.  Returns -1 for unsupported shapes.
+int gemm_partial_splits(int N, int K);
+int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* P, int ldp,
+                        long slice_stride, int splits, hipStream_t st);
+
 void launch_embed(int dtype, const void* E, const int32_t* tok, float* x, int T, int H, int V, hipStream_t st);
 void launch_copy_rows(const float* src, float* dst, long n, hipStream_t st);
 void launch_rope_table(const int32_t* pos, float* cosb, float* sinb, int T, int d, float base, hipStream_t st);
 void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st);
-void launch_rope_kv(int dtype, const float* qkv, const float* cosb, const float* sinb, const int32_t* slot,
-                    void* q_att, void* kc, void* vc, int T, int nq, int nkv, int d, hipStream_t st);
+// x[t] += sum_s P[s][t] (slice order; the split-K residual add of the
+// previous projection), written back to x, then RMSNorm into h.
+void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_stride, int splits, const void* g,
+                           void* h, int T, int H, float eps, hipStream_t st);
+// out[t] = x[t] + sum_s P[s][t]  (the last layer's residual add, fp32 out)
+void launch_reduce_rows(const float* x, const float* P, long slice_stride, int splits, float* out, int T, int H,
+                        hipStream_t st);
+// Embedding (E non-null) or hidden input already in x, RoPE cos/sin table,
+// and layer 0's RMSNorm, one workgroup per row.
+void launch_step_prologue(int dtype, const void* E, const int32_t* tok, float* x, const int32_t* pos, float* cosb,
+                          float* sinb, const void* g0, void* h, int T, int H, int V, int d, float base, float eps,
+                          hipStream_t st);
+// qkv holds `splits` fp32 slices (slice_stride apart) that are summed first.
+void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, const float* cosb,
+                    const float* sinb, const int32_t* slot, void* q_att, void* kc, void* vc, int T, int nq, int nkv,
+                    int d, hipStream_t st);
 void launch_kv_scatter(int dtype, const int32_t* slots, const void* k, const void* v, void* kc, void* vc, int n,
                        int nkv, int d, hipStream_t st);
 void launch_kv_gather(int dtype, const int32_t* slots, void* k, void* v, const void* kc, const void* vc, int n,
@@ -51,6 +75,7 @@ struct AttnArgs {
   int nq, nkv, d;
   int part_tokens;          // P, multiple of 64
   int n_parts;              // partitions per row (max)
+  int waves;                // wavefronts per work item: 1 or 4
   int wg_cap;               // 0 = one workgroup per work item
 };
 int attention_supported(int dtype, int d, int G);

@@ -18,7 +18,8 @@ def _bf16_grid(a):
 
 
 GEMM_SHAPES = [(1, 64, 64), (5, 130, 96), (16, 896, 896), (17, 1152, 896), (32, 300, 128), (33, 256, 4864),
-               (64, 64, 256), (100, 520, 160), (130, 384, 512), (257, 640, 1024)]
+               (64, 64, 256), (100, 520, 160), (130, 384, 512), (257, 640, 1024), (32, 896, 4864),
+               (1, 896, 4864), (32, 4864, 896), (8, 1000, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -40,9 +41,15 @@ def test_gemm_bf16_matches_float64(M, N, K, epi):
         if epi == ns.NS_EPI_RESID:
             ref = ref + C0.double()
     Ad, Bd = A.cuda(), B.cuda()
+    C_in = C.clone()
     ns.ns_op_gemm(ns.NS_BF16, epi, M, N, K, Ad.data_ptr(), Bd.data_ptr(), C.data_ptr())
     torch.cuda.synchronize()
     got = C.double().cpu().numpy()
+    # deterministic: a second call gives the same bits
+    C2 = C_in.clone()
+    ns.ns_op_gemm(ns.NS_BF16, epi, M, N, K, Ad.data_ptr(), Bd.data_ptr(), C2.data_ptr())
+    torch.cuda.synchronize()
+    assert torch.equal(C2.cpu(), C.cpu())
     ref = ref.numpy()
     # fp32 accumulation of K products (and a final bf16 rounding for SwiGLU)
     tol = 4e-3 if epi == ns.NS_EPI_SILU else 1e-5

@@ -129,10 +129,24 @@ def test_graph_replay_with_changing_metadata_matches_eager():
     st = torch.cuda.Stream()
     try:
         n = c.batch.n_rows
+        b = c.batch
         sub = np.arange(0, 6)             # decode rows only
         eager_full = c.step().cpu()
         c.reset_cache()
-        eager_sub = c.step(rows=sub).cpu()
+        # eager step over the same bucket: 6 real rows, the rest padding
+        seq_p = np.full(n, -1, np.int32)
+        seq_p[sub] = b.row_seq[sub]
+        pos_p = np.zeros(n, np.int32)
+        pos_p[sub] = b.row_pos[sub]
+        tok_p = np.zeros(n, np.int32)
+        tok_p[sub] = b.tokens[sub]
+        outp = torch.full((n, SMALL.vocab), float("nan"), device="cuda")
+        ns.ns_decode_step(c.h.eng, ns.Batch(seq_p, pos_p, tok_p), outp.data_ptr())
+        torch.cuda.synchronize()
+        eager_sub = outp[: len(sub)].cpu()
+        c.reset_cache()
+        eager_6 = c.step(rows=sub).cpu()    # a 6-row launch: other kernels, same values within the bound
+        assert_close(eager_sub.numpy(), eager_6.numpy(), "bf16", "padded bucket vs 6-row step")
         c.reset_cache()
         out = torch.full((n, SMALL.vocab), float("nan"), device="cuda")
         g = ns.ns_graph_capture(c.h.eng, n, out.data_ptr(), st)
@@ -151,17 +165,24 @@ def test_graph_replay_with_changing_metadata_matches_eager():
 
 
 def test_overlap_equals_serial_and_split_matches_unsplit():
+    """Overlapping the attention nano-ops with the projections of other
+    nano-batches changes only the order of independent work: bit-exact with
+    the serial run of the same split.  A different split changes the row
+    count of each projection launch, hence its tiling and split-K partition
+    (fp32 summation order): equal within the bf16 bound."""
     w = _small_workload(SMALL)
     c = Case(w, max_tokens=80)
     try:
         base = c.step().cpu()
-        for sched in (ns.make_sched(nano_rows=(30, 41)), ns.make_sched(nano_rows=(30, 41), overlap=True),
-                      ns.make_sched(nano_rows=(10, 20, 20, 21), qkv_rows=(16, 16, 16, 23), overlap=True)):
-            ns.ns_engine_set_sched(c.h.eng, sched)
+        for rows, qrows in (((30, 41), ()), ((10, 20, 20, 21), (16, 16, 16, 23))):
+            ns.ns_engine_set_sched(c.h.eng, ns.make_sched(nano_rows=rows, qkv_rows=qrows))
             c.reset_cache()
-            got = c.step().cpu()
-            # same kernels on the same rows in a different order: bit-exact
-            torch.testing.assert_close(got, base, rtol=0, atol=0)
+            serial = c.step().cpu()
+            ns.ns_engine_set_sched(c.h.eng, ns.make_sched(nano_rows=rows, qkv_rows=qrows, overlap=True))
+            c.reset_cache()
+            over = c.step().cpu()
+            torch.testing.assert_close(over, serial, rtol=0, atol=0)
+            assert_close(serial.numpy(), base.numpy(), "bf16", f"split {rows} vs unsplit")
     finally:
         c.close()
 
@@ -208,3 +229,27 @@ def test_step_errors_are_reported_without_side_effects():
         assert_close(got, ref, "bf16", "after errors")
     finally:
         c.close()
+
+
+def test_decode_batch_path_nano_overlap_and_oracle():
+    """A step of at most 64 rows takes the weight-streaming path (split-K
+    slices summed by the next kernel on the same rows).  Overlapped
+    nano-batches are bit-exact with serial ones, and the step matches the
+    oracle; the vocabulary-free variant exercises the output reduction."""
+    for shape in (SMALL, SMALL_NOVOCAB):
+        w = Workload("small_dec", shape, 6, ctx_range=(1, 200), prefill_chunks=(20,))
+        c = Case(w, max_tokens=64)
+        try:
+            base = c.step().cpu()
+            ref, _, _ = oracle_run(shape, c.weights, c.batch, c.maxb)
+            assert_close(base.numpy(), ref, "bf16", f"{shape.name} decode-batch path")
+            ns.ns_engine_set_sched(c.h.eng, ns.make_sched(nano_rows=(10, 16)))
+            c.reset_cache()
+            serial = c.step().cpu()
+            ns.ns_engine_set_sched(c.h.eng, ns.make_sched(nano_rows=(10, 16), qkv_rows=(8, 8, 10), overlap=True))
+            c.reset_cache()
+            over = c.step().cpu()
+            torch.testing.assert_close(over, serial, rtol=0, atol=0)
+            torch.testing.assert_close(serial, base, rtol=0, atol=0)  # same K partition whatever the rows
+        finally:
+            c.close()
