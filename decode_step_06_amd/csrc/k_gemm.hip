@@ -196,30 +196,70 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
   }
 }
 
-// Dense-batch projection (M >= 256): a 256 x 256 output tile per workgroup,
-// 8 wavefronts in a 2 x 4 grid each owning a 128 x 64 sub-tile (8 x 4
-// fragments, 128 accumulators per lane), K in 64-wide slabs through
-// double-buffered padded LDS (2 x 72 KB).  A wavefront tile this large needs
-// 3/4 of the LDS bytes per MFMA of a 64 x 64 one.
+// Dense-batch projection (M >= 256, K % 32 == 0): a 256 x 256 output tile
+// per workgroup of 4 wavefronts in a 2 x 2 grid, each owning a 128 x 128
+// sub-tile (4 x 4 fragments of 32 x 32, 256 accumulators per lane): per FLOP
+// that needs half the LDS bytes of a 64 x 64 wavefront tile.  The 32x32x16
+// bf16 MFMA is used because on gfx950 it sustains the full bf16 rate, about
+// twice what the 16x16x32 form reaches.
+//
+// Slabs of 32 K go global -> LDS with buffer_load_dwordx4 ... lds (no
+// register staging, no LDS write instructions): lane l of a wavefront
+// instruction lands its 16 bytes at M0 + 16 l, so one instruction fills 16
+// rows of 64 bytes.  Each lane's row offset sits in a VGPR for the whole
+// kernel and the slab's K offset goes in the scalar offset, so a refill costs
+// no vector ALU work.  Rows are unpadded; the 16-byte chunk c of row r is
+// stored at position c ^ (((r >> 1) ^ (r >> 2)) & 3), which keeps the
+// 32-row fragment reads conflict-free.  Four slab buffers (4 x 32 KB), loads
+// issued three slabs ahead.
+//
+// Software pipeline, two register sets of fragments: while the 32 MFMAs of
+// slab k run, slab k+1's fragments are read from LDS into the other set and
+// slab k+3's loads go out.  The instruction order within that stream is fixed
+// with scheduling groups: 8 MFMAs interleaved with half the loads, the wait
+// for slab k+1 and the barrier, then the 16 fragment reads one per MFMA, then
+// the other half of the loads spread over the last MFMAs.  One wavefront per
+// SIMD, so the MFMA pipe only stays fed if nothing in the stream stalls it.
+// Past the last slab the loads re-read the last slab into buffers no one
+// reads again (every access stays inside the operands).
 //
 // Tile order is XCD-aware: workgroups are dispatched round-robin over the 8
 // XCDs, so workgroup b runs on XCD b % 8; giving each XCD a contiguous range
-// of tiles, M-fastest, makes the 32 tiles an XCD runs at once share their B
+// of tiles, M-fastest, makes the tiles an XCD runs at once share their B
 // columns in that XCD's private L2 while walking down A.
+//
+// Addressing is 32-bit (buffer offsets): the host sends operands whose byte
+// span exceeds 4 GiB to the tiled kernel.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// s_waitcnt immediate: vmcnt(vm) lgkmcnt(lgkm), expcnt not waited on
+constexpr int waitcnt_imm(int vm, int lgkm) { return ((vm >> 4) << 14) | (lgkm << 8) | 0x70 | (vm & 15); }
+
+// scheduling-group instruction classes (AMDGPU sched_group_barrier masks)
+constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
+
+constexpr unsigned BUF_RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit dwords, no swizzle
+
 template <int EPI, typename OutT>
-__global__ void __launch_bounds__(512) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
+__global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
                                                        const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
                                                        void* __restrict__ Cv, int ldc) {
-  constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8;
-  constexpr int TM = 128, TN = 64, FM = 8, FN = 4, NT = 512;
+  constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
+  constexpr int TM = 128, TN = 128, FM = 4, FN = 4;  // 32 x 32 fragments
+  constexpr int ROWB = BK * 2;                  // bytes per LDS row
+  constexpr int STAGE = (BM + BN) * ROWB;       // bytes per slab buffer (A rows, then B rows)
+  constexpr int LOADS = (BM + BN) / 16 / 4;     // load instructions per wavefront per slab (8)
+  constexpr int PRE = 8;                        // MFMAs of a slab before its barrier
+  constexpr int LPRE = 4;                       // loads issued before the barrier
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? BN / 2 : BN;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (BM + BN) * LDK];  // 144 KB of the 160 KB
-  bf16_t* As = lds;                      // [2][BM * LDK]
-  bf16_t* Bs = lds + 2 * BM * LDK;       // [2][BN * LDK]
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];  // 128 KB
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int m_tiles = (M + BM - 1) / BM;
   const int n_tiles = (N + OUT_BN - 1) / OUT_BN;
   const int tiles = m_tiles * n_tiles;
@@ -228,100 +268,173 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(const bf16_t* __restrict_
   const int tile_m = tile % m_tiles, tile_n = tile / m_tiles;
   const int m0 = tile_m * BM, n0 = tile_n * OUT_BN;
 
-  auto a_row = [&](int r) { int m = m0 + r; return m < M ? m : M - 1; };
-  auto b_row = [&](int r) {
-    if constexpr (EPI == EPI_SILU_MUL) {
-      int n = n0 + (r < BN / 2 ? r : r - BN / 2);
-      n = n < N ? n : N - 1;
-      return r < BN / 2 ? n : N + n;
+  const unsigned a_bytes = (unsigned)((long)M * lda * 2);
+  const unsigned b_bytes = (unsigned)((long)((EPI == EPI_SILU_MUL) ? 2 * N : N) * ldb * 2);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)a_bytes, BUF_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)b_bytes, BUF_RSRC_WORD3);
+  // Load instruction j of wavefront w fills the 16 LDS rows of group
+  // g = w + 4 j (groups 0..15: A rows, 16..31: B rows); lane l loads row
+  // 16 (g mod 16) + l / 4, chunk (l & 3) ^ swz(row).  Rows past M or N
+  // repeat the last row (their results are never stored).
+  unsigned voff[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int g = wave + 4 * j;
+    const int r = (g & 15) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    if (g < 16) {
+      int m = m0 + r;
+      m = m < M ? m : M - 1;
+      voff[j] = (unsigned)(((long)m * lda + c * 8) * 2);
     } else {
-      int n = n0 + r;
-      return n < N ? n : N - 1;
+      int brow;
+      if constexpr (EPI == EPI_SILU_MUL) {
+        int n = n0 + (r < BN / 2 ? r : r - BN / 2);
+        n = n < N ? n : N - 1;
+        brow = r < BN / 2 ? n : N + n;
+      } else {
+        int n = n0 + r;
+        brow = n < N ? n : N - 1;
+      }
+      voff[j] = (unsigned)(((long)brow * ldb + c * 8) * 2);
     }
-  };
-  // 4 A chunks + 4 B chunks of 16 bytes per thread per slab
-  constexpr int PT = BM * BK / 8 / NT;
-  const bf16_t* ga[PT];
-  const bf16_t* gb[PT];
-  int la[PT];
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int c = tid + i * NT;
-    const int r = c >> 3, k8 = c & 7;
-    ga[i] = A + (long)a_row(r) * lda + k8 * 8;
-    gb[i] = B + (long)b_row(r) * ldb + k8 * 8;
-    la[i] = r * LDK + k8 * 8;
   }
-  u32x4_t ra[PT], rb[PT];
-  auto load_slab = [&](int k0) {
+  const int nk = K / BK;
+  // loads j0..j1-1 of slab kt into buffer kt % 4
+  auto issue = [&](int kt, int j0, int j1) {
+    const int ks = kt < nk ? kt : nk - 1;
+    const unsigned soff = (unsigned)ks * (BK * 2);
+    char* base = lds + (kt % NSTAGE) * STAGE;
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      ra[i] = *(const u32x4_t*)(ga[i] + k0);
-      rb[i] = *(const u32x4_t*)(gb[i] + k0);
+    for (int j = j0; j < j1; ++j) {
+      const int g = wave + 4 * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < 16 ? ra : rb, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j],
+                                               soff, 0, 0);
     }
   };
-  auto store_slab = [&](int buf) {
+  // v_mfma_f32_32x32x16_bf16 operands: lane l holds row (or column) l % 32
+  // of a fragment and the 8 K values 8 (l / 32) .. +8 of a 16-deep K step.
+  // Fragment read offsets within a slab buffer for K step s = 0 / 1.
+  const int fr = lane & 31, fq = lane >> 5;
+  int aoff[2][FM], boff[2][FN];
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      *(u32x4_t*)&As[buf * BM * LDK + la[i]] = ra[i];
-      *(u32x4_t*)&Bs[buf * BN * LDK + la[i]] = rb[i];
-    }
-  };
-  auto b_frag_row = [&](int f) {
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * TM + 32 * i + fr;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) aoff[st][i] = r * ROWB + (((2 * st + fq) ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    int r;
     if constexpr (EPI == EPI_SILU_MUL) {
       constexpr int HF = FN / 2;
-      return (f < HF ? 0 : BN / 2) + wn * (TN / 2) + 16 * (f % HF);
+      r = (j < HF ? 0 : BN / 2) + wn * (TN / 2) + 32 * (j % HF) + fr;
     } else {
-      return wn * TN + 16 * f;
+      r = wn * TN + 32 * j + fr;
     }
-  };
+#pragma unroll
+    for (int st = 0; st < 2; ++st) boff[st][j] = BM * ROWB + r * ROWB + (((2 * st + fq) ^ swz(r)) << 4);
+  }
 
-  f32x4_t acc[FM][FN];
+  f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = K / BK;
-  load_slab(0);
-  store_slab(0);
-  __syncthreads();
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_slab((kt + 1) * BK);
-    const bf16_t* Ab = As + buf * BM * LDK;
-    const bf16_t* Bb = Bs + buf * BN * LDK;
+  // A bare barrier: a workgroup fence here would also drain the later
+  // slabs' loads; the empty asm statements keep the compiler from moving LDS
+  // accesses across it.
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  bf16x8_t fa[2][2][FM], fb[2][2][FN];  // [register set][K step][fragment]
+  auto read_frags = [&](int kt, int set) {
+    const char* base = lds + (kt % NSTAGE) * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8_t af[FM], bfr[FN];
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8_t*)&Ab[(wm * TM + 16 * i + fr) * LDK + kk + fk];
+      for (int i = 0; i < FM; ++i) fa[set][st][i] = *(const bf16x8_t*)(base + aoff[st][i]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *(const bf16x8_t*)&Bb[(b_frag_row(j) + fr) * LDK + kk + fk];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j) fb[set][st][j] = *(const bf16x8_t*)(base + boff[st][j]);
     }
-    if (kt + 1 < nk) store_slab(buf ^ 1);
-    __syncthreads();
+  };
+  // MFMAs q in [lo, hi) of a slab: K step q / 16, fragment (q / 4 % 4, q % 4)
+  auto mfmas = [&](int set, int lo, int hi) {
+#pragma unroll
+    for (int q = lo; q < hi; ++q) {
+      const int st = q >> 4, i = (q >> 2) & 3, j = q & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][st][i], fb[set][st][j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // Slab kt, whose fragments are in register set `set`.
+  auto slab = [&](int kt, int set) {
+    // Buffer (kt+3) % 4 held slab kt-1: every wavefront completed its reads
+    // of it before the barrier of slab kt (lgkmcnt(0) below).
+    issue(kt + 3, 0, LPRE);
+    mfmas(set, 0, PRE);
+#pragma unroll
+    for (int q = 0; q < PRE; ++q) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      if (q * LPRE / PRE != (q + 1) * LPRE / PRE) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Slab kt+1 landed (the 8 loads of slab kt+2 and the LPRE of slab kt+3
+    // issued after it may still be in flight) and this wavefront's reads of
+    // slab kt completed; after the barrier, the same holds for every
+    // wavefront.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS + LPRE, 0));
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt + 1, set ^ 1);
+    issue(kt + 3, LPRE, LOADS);
+    mfmas(set, PRE, 32);
+    constexpr int NR = 32 - PRE;
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
+      if (q < 16) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 1);
+      else if ((q - 16) * (LOADS - LPRE) / (NR - 16) != (q - 15) * (LOADS - LPRE) / (NR - 16))
+        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p) issue(p, 0, LOADS);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LOADS, 0));  // slab 0 landed
+  barrier();
+  read_frags(0, 0);
+  // Two slabs per trip so the register sets are compile-time constants.
+  // Past the last slab, read_frags reads a buffer whose fragments go unused.
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    slab(kt, 0);
+    slab(kt + 1, 1);
   }
+  if (kt < nk) mfmas(0, 0, 32);  // odd slab count: the last slab is in set 0
+  // Drain the trailing loads before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
-  const int er = (lane >> 4) * 4, ec = lane & 15;
+  // Epilogue.  32 x 32 fragment element e of lane l: row 8 (e / 4) + 4 (l / 32)
+  // + e % 4, column l % 32.
+  const int ec = lane & 31, eq = (lane >> 5) * 4;
   if constexpr (EPI == EPI_SILU_MUL) {
     constexpr int HF = FN / 2;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < HF; ++j) {
-        const int col = n0 + wn * (TN / 2) + 16 * j + ec;
+        const int col = n0 + wn * (TN / 2) + 32 * j + ec;
         if (col >= N) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = m0 + wm * TM + 16 * i + er + r;
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm * TM + 32 * i + 8 * (e >> 2) + eq + (e & 3);
           if (row < M)
-            Elem<OutT>::store((OutT*)Cv, (long)row * ldc + col, silu_f(acc[i][j][r]) * acc[i][j + HF][r]);
+            Elem<OutT>::store((OutT*)Cv, (long)row * ldc + col, silu_f(acc[i][j][e]) * acc[i][j + HF][e]);
         }
       }
   } else {
@@ -330,15 +443,15 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(const bf16_t* __restrict_
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * TN + 16 * j + ec;
+        const int col = n0 + wn * TN + 32 * j + ec;
         if (col >= N) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = m0 + wm * TM + 16 * i + er + r;
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm * TM + 32 * i + 8 * (e >> 2) + eq + (e & 3);
           if (row >= M) continue;
           float* p = Cp + (long)row * ldc + col;
-          if constexpr (EPI == EPI_RESID_F32) *p += acc[i][j][r];
-          else *p = acc[i][j][r];
+          if constexpr (EPI == EPI_RESID_F32) *p += acc[i][j][e];
+          else *p = acc[i][j][e];
         }
       }
   }
@@ -556,10 +669,13 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
   if (M <= 32) return dispatch_gemv_m<2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   const bool k64 = (K % 64) == 0;
-  if (M >= 256 && k64 && N >= 256) {
+  // the big kernel addresses its operands with 32-bit buffer offsets
+  const long b_rows = (EPI == EPI_SILU_MUL) ? 2L * N : (long)N;
+  const bool fits32 = (long)M * lda * 2 < (1L << 32) && b_rows * ldb * 2 < (1L << 32);
+  if (M >= 256 && N >= 256 && fits32) {
     constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
     const long tiles = (long)((M + 255) / 256) * ((N + OUT_BN - 1) / OUT_BN);
-    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t>), dim3((unsigned)tiles), dim3(512), 0, st, (const bf16_t*)A,
+    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t>), dim3((unsigned)tiles), dim3(256), 0, st, (const bf16_t*)A,
                        lda, (const bf16_t*)B, ldb, M, N, K, C, ldc);
     return;
   }
