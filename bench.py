@@ -16,6 +16,11 @@ on, behind a queued busy-wait kernel so host launch gaps do not count):
     batch -- decode attention (512 rows x context 1024) against the HBM peak,
     the four projections against the bf16 MFMA peak, and the layer step with
     and without the nano-batch overlap;
+  * ``batch_sweep``: the same model under the continuous-batching mix
+    (batch 1..256, contexts 128..2048, fragmented tables, a graph per batch
+    size): tokens/s against the step's HBM floor, attention GB/s;
+  * ``llama70b_80l_b256``: the LLaMA-2-70B-shaped 80-layer step with 256
+    sequences (contexts 512..1536), with and without the nano-batch overlap;
   * ``cpu_baseline``: the CPU oracle timed on the host (bounded sample).
 """
 from __future__ import annotations
@@ -253,6 +258,102 @@ def dense_batch(stream, steps=10):
     return res
 
 
+# ---------------------------------------------------------------- batch sweep
+SWEEP = (1, 8, 32, 64, 128, 256)
+
+
+def _graph_rate(h, b, stream, steps, warm_seconds, sched=None):
+    """Device time per replay of the step's graph (median of 3 timings of
+    `steps` back-to-back replays)."""
+    if sched is not None:
+        ns.ns_engine_set_sched(h.eng, sched)
+    out = torch.empty((b.n_rows, h.shape.vocab or h.shape.hidden), device="cuda")
+    nb = ns.Batch(b.row_seq, b.row_pos, b.tokens)
+    g = ns.ns_graph_capture(h.eng, b.n_rows, out.data_ptr(), stream)
+    try:
+        t_end = time.time() + warm_seconds
+        while time.time() < t_end:
+            ns.ns_graph_replay(g, nb, stream)
+            stream.synchronize()
+        return time_launches(lambda i: ns.ns_graph_replay(g, nb, stream), steps, stream)
+    finally:
+        ns.ns_graph_destroy(g)
+
+
+def _step_row(h, b, t, stream):
+    s = h.shape
+    ctx = (b.row_pos + 1).astype(np.int64)
+    sb = rf.step_bytes(s, ctx)
+    kern = step_kernels(h, b, stream, reps=3)
+    att = kern.get("attention", {})
+    tot = sum(v["us_per_step"] for v in kern.values())
+    return {"tokens_per_s": b.n_rows / t, "ms_per_step": t * 1e3, "mean_ctx": float(ctx.mean()),
+            "algorithmic_bytes": sb, "hbm_floor_ms": rf.floor_seconds(sb) * 1e3,
+            "step_hbm_frac": sb / t / 1e9 / rf.HBM_PEAK_GBS,
+            "attention_gbs": att.get("gbs"), "attention_hbm_frac": (att.get("gbs") or 0) / rf.HBM_PEAK_GBS,
+            "attention_share_of_step": att.get("us_per_step", 0) / tot if tot else None,
+            "kernels_per_step": sum(v["launches_per_step"] for v in kern.values())}
+
+
+def batch_sweep(stream, dw, steps=100, warm_seconds=1.0):
+    """Qwen2.5-0.5B-shaped 24-layer step under the continuous-batching mix:
+    batch 1..256, contexts uniform in 128..2048, fragmented block tables, one
+    graph captured per batch size."""
+    res = {}
+    for B in SWEEP:
+        w = WORKLOADS[f"qwen05b_mix_b{B}"]
+        b = gen_batch(w, with_past=False)
+        maxb = blocks_for(b.seq_lens)
+        log(f"[bench] batch sweep B={B}")
+        h = create_engine(w.model, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, None,
+                          nan_poison=False)
+        try:
+            alloc_sequences(h, b.seq_lens)
+            fill_past_random_on_device(h, b.past_seq, b.past_pos, seed=w.seeds["kv"])
+            t = _graph_rate(h, b, stream, steps, warm_seconds)
+            res[str(B)] = _step_row(h, b, t, stream)
+        finally:
+            h.destroy()
+            torch.cuda.synchronize()
+    return res
+
+
+# ---------------------------------------------------------------- 80-layer 70B
+def llama80(stream, steps=10, warm_seconds=2.0):
+    """LLaMA-2-70B-shaped 80-layer step, 256 sequences at contexts uniform in
+    512..1536, weights and cache drawn on the device; the graph replayed with
+    the two-way nano-batch overlap and without it."""
+    w = WORKLOADS["llama70b_80l_b256"]
+    s = w.model
+    torch.cuda.empty_cache()
+    b = gen_batch(w, with_past=False, pool_slack=1.02)
+    maxb = blocks_for(b.seq_lens)
+    log("[bench] llama70b 80 layers: drawing weights and cache on the device")
+    t0 = time.time()
+    dw = DeviceWeights.random_on_device(s, seed=w.seeds["weights"])
+    h = create_engine(s, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, None, nan_poison=False)
+    res = {"weights_gb": dw.bytes() / 1e9, "kv_pool_gb": h.kv_mem.numel() / 1e9}
+    try:
+        alloc_sequences(h, b.seq_lens)
+        fill_past_random_on_device(h, b.past_seq, b.past_pos, seed=w.seeds["kv"])
+        res["setup_s"] = time.time() - t0
+        log("[bench] llama70b 80 layers: timing graph replays")
+        t_nano = _graph_rate(h, b, stream, steps, warm_seconds,
+                             ns.make_sched(nano_rows=w.nano_splits, overlap=True))
+        t_ser = _graph_rate(h, b, stream, steps, 0.5, ns.make_sched())
+        row = _step_row(h, b, t_nano, stream)
+        row["ms_per_step_unsplit"] = t_ser * 1e3
+        row["tokens_per_s_unsplit"] = b.n_rows / t_ser
+        row["nano_split"] = list(w.nano_splits)
+        res.update(row)
+    finally:
+        h.destroy()
+        del dw
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------- CPU oracle
 def cpu_baseline(w, weights, b, maxb, n_steps=3):
     from oracle import decoder as od
@@ -291,6 +392,8 @@ def main():
     ap.add_argument("--warm-seconds", type=float, default=3.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-llama80", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step is built and measured on a single MI355X "
@@ -308,9 +411,15 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
     w, weights, b, h, maxb = setup_step(WORKLOAD)
+    sweep = None
     try:
         runs, eager, launches = run_step_bench(h, b, args.steps, args.warmup, args.warm_seconds, stream)
         kern = step_kernels(h, b, stream)
+        if not args.no_sweep:
+            try:
+                sweep = json.loads(json.dumps(batch_sweep(stream, h.weights), default=_jsonable))
+            except Exception as e:  # report, do not hide
+                sweep = {"error": repr(e)}
     finally:
         h.destroy()
     step_s = runs[-1]
@@ -355,6 +464,13 @@ def main():
             result["dense_batch"] = json.loads(json.dumps(dense_batch(stream), default=_jsonable))
         except Exception as e:  # report, do not hide
             result["dense_batch"] = {"error": repr(e)}
+    if sweep is not None:
+        result["batch_sweep"] = sweep
+    if not args.no_llama80:
+        try:
+            result["llama70b_80l_b256"] = json.loads(json.dumps(llama80(stream), default=_jsonable))
+        except Exception as e:  # report, do not hide
+            result["llama70b_80l_b256"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, weights, b, maxb)
     print(json.dumps(result, default=_jsonable), flush=True)

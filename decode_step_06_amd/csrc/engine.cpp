@@ -37,7 +37,7 @@ size_t kv_layer_bytes(const ns_model_desc* d, int32_t num_blocks);
 namespace {
 
 constexpr int kMaxParts = 4;
-constexpr int kDecodeRows = 64;  // steps of at most this many rows use the weight-streaming split-K path
+constexpr int kSplitRows = 256;  // steps of at most this many rows use the split-K projections
 constexpr int kMaxSlices = 8;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -46,44 +46,48 @@ int elem_size(int32_t dtype) { return dtype == NS_BF16 ? 2 : 4; }
 // Attention launch shape for a batch of n_rows rows when sequences hold at
 // most cap_tokens tokens: partition size (tokens, a multiple of 64),
 // partitions per row, and wavefronts per work item (row, KV head,
-// partition).  When rows x KV heads alone fill the chip (>= 2048 items), one
-// wavefront per item streams the whole context; otherwise 4 wavefronts take
-// interleaved 64-token passes and the partition count minimises a simple
-// cost: passes per wavefront (each is mostly memory latency), scaled up when
-// the wavefronts exceed what the chip keeps resident (about 4096), plus the
-// combine launch when the context is split.  The shape depends only on the
-// whole batch's row count and the capacity, so nano-batched and unsplit
-// steps, eager and captured, compute identically.
-void attn_partition(int n_rows, int nkv, int cap_tokens, int* part_tokens, int* n_parts, int* waves) {
+// partition).  Each wavefront takes 64-token passes, and a pass is mostly
+// memory latency (about 2 us: block ids, then K/V, then the math), so a
+// launch costs roughly the larger of 2 us per pass of its busiest wavefront
+// and the cache bytes at the HBM rate, scaled down while fewer than about
+// 1024 wavefronts are in flight; splitting the context adds the combine
+// launch (about 3 us, a little more per partition).  The cheapest (waves,
+// partitions) wins, ties going to fewer wavefronts and partitions.  The shape
+// depends only on the whole batch's row count and the capacity, so
+// nano-batched and unsplit steps, eager and captured, compute identically.
+// (Fitted to timings of this kernel on MI355X over batch 1..512, contexts
+// 128..2048, head_dim 64 and 128.)
+void attn_partition(int n_rows, int nkv, int cap_tokens, int head_dim, int elem_bytes, int* part_tokens,
+                    int* n_parts, int* waves) {
   const int chunks = std::max(1, (cap_tokens + 63) / 64);
   const long items = std::max(1L, (long)n_rows * nkv);
-  if (items >= 2048) {
-    *waves = 1;
-    *part_tokens = 64 * chunks;
-    *n_parts = 1;
-    return;
-  }
-  *waves = 4;
-  int best_parts = 1;
+  const double bytes = (double)items * 64.0 * chunks * head_dim * 2 * elem_bytes;  // K and V
   double best = 1e30;
-  for (int parts = 1; parts <= chunks; parts *= 2) {
-    const int per = (chunks + parts - 1) / parts;
-    const double passes = std::ceil(per / 4.0);
-    const double wv = (double)items * 4 * parts;
-    const double cost = passes * std::max(1.0, wv / 4096.0) + (parts > 1 ? 2.0 : 0.0);
-    if (cost < best - 1e-9) {
-      best = cost;
-      best_parts = parts;
+  int best_w = 1, best_p = 1;
+  for (int w : {1, 4}) {
+    for (int parts = 1; parts <= chunks; parts *= 2) {
+      const int per = (chunks + parts - 1) / parts;
+      const int np = (chunks + per - 1) / per;
+      const double passes = std::ceil((double)per / w);
+      const double in_flight = (double)items * np * w;
+      const double mem_us = bytes / (8.0e6 * std::min(1.0, in_flight / 1024.0));
+      const double cost = std::max(2.0 * passes, mem_us) + (np > 1 ? 3.0 + 0.25 * np : 0.0);
+      if (cost < best - 1e-9) {
+        best = cost;
+        best_w = w;
+        best_p = parts;
+      }
     }
   }
-  const int per = (chunks + best_parts - 1) / best_parts;
+  const int per = (chunks + best_p - 1) / best_p;
+  *waves = best_w;
   *part_tokens = 64 * per;
   *n_parts = (chunks + per - 1) / per;
 }
 
 struct Plan {
   size_t x, h, qkv, q_att, o, act, cosb, sinb, meta, part_acc, part_ml, part_qkv, part_res, total;
-  int tdec;  // rows of the split-K slice buffers (decode steps: at most 64 rows)
+  int tdec;  // rows of the split-K slice buffers (steps of at most 256 rows)
   size_t meta_ints;  // int32 entries of the metadata block
 };
 
@@ -110,14 +114,14 @@ Plan make_plan(const ns_model_desc* d, int T, int maxb) {
   long items = 0;
   for (int n = 1; n <= T; ++n) {
     int P, np, nw;
-    attn_partition(n, d->n_kv_heads, maxb * NS_BLOCK_SIZE, &P, &np, &nw);
+    attn_partition(n, d->n_kv_heads, maxb * NS_BLOCK_SIZE, d->head_dim, (int)es, &P, &np, &nw);
     if (np > 1) items = std::max(items, (long)n * d->n_kv_heads * np);
   }
   p.part_acc = take((size_t)items * G * d->head_dim * 4);
   p.part_ml = take((size_t)items * G * 2 * 4);
-  // split-K slices of decode steps (bf16 models, <= 64 rows): the QKV result,
-  // and the O / down projections' residual adds (up to 8 slices each)
-  p.tdec = std::min(T, kDecodeRows);
+  // split-K slices of steps of at most 256 rows (bf16 models): the QKV
+  // result, and the O / down projections' residual adds (up to 8 slices each)
+  p.tdec = std::min(T, kSplitRows);
   const int qkv_w = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
   const bool dec = d->dtype == NS_BF16;
   p.part_qkv = take(dec ? (size_t)kMaxSlices * p.tdec * qkv_w * 4 : 0);
@@ -308,7 +312,8 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
   a->nq = e->d.n_q_heads;
   a->nkv = e->d.n_kv_heads;
   a->d = e->d.head_dim;
-  attn_partition(n_tok, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, &a->part_tokens, &a->n_parts, &a->waves);
+  attn_partition(n_tok, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, e->d.head_dim, (int)e->es, &a->part_tokens,
+                 &a->n_parts, &a->waves);
   a->wg_cap = e->sched.attn_wg_cap;
 }
 
@@ -361,16 +366,19 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   char* act = (char*)e->act();
   float* x = e->x();
   float* qkv = e->qkv();
-  // Decode steps (bf16, <= 64 rows): the projections stream their weights
-  // with K split across workgroups; each split writes an fp32 slice and the
-  // next kernel on those rows (RoPE/cache write, or the next RMSNorm, or the
-  // output) sums the slices in order -- the residual add of the O and down
-  // projections happens there.
+  // Steps of at most 256 rows (bf16): the QKV, O and down projections split
+  // K across workgroups so that their few output tiles still fill the chip
+  // (at <= 64 rows they stream the weights); each split writes an fp32 slice
+  // and the next kernel on those rows (RoPE/cache write, or the next
+  // RMSNorm, or the output) sums the slices in order -- the residual add of
+  // the O and down projections happens there.  The split counts follow the
+  // whole step's row count, so every nano-batch's slices match their
+  // consumers.
   const bool dec = dt == NS_DT_BF16 && n_tok <= e->plan.tdec;
   const long sq = (long)e->plan.tdec * QKV, sr = (long)e->plan.tdec * H;  // slice strides
-  const int S_qkv = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(QKV, H)) : 1;
-  const int S_o = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(H, DQ)) : 1;
-  const int S_d = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(H, F)) : 1;
+  const int S_qkv = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(n_tok, QKV, H)) : 1;
+  const int S_o = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(n_tok, H, DQ)) : 1;
+  const int S_d = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(n_tok, H, F)) : 1;
   float* pq = e->part_qkv();
   float* pr = e->part_res();
   for (int l = 0; l < d.n_layers; ++l) {
@@ -737,7 +745,8 @@ int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, cons
 size_t ns_op_attention_ws_bytes(const ns_model_desc* desc, int32_t n_rows, int32_t max_blocks_per_seq) {
   if (ns::check_desc(desc) != NS_OK || n_rows <= 0 || max_blocks_per_seq <= 0) return 0;
   int P, np, nw;
-  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &P, &np, &nw);
+  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, desc->head_dim,
+                 elem_size(desc->dtype), &P, &np, &nw);
   const int G = desc->n_q_heads / desc->n_kv_heads;
   const size_t items = (size_t)n_rows * desc->n_kv_heads * np;
   return align_up(items * G * desc->head_dim * 4, 256) + align_up(items * G * 2 * 4, 256);
@@ -772,8 +781,8 @@ int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att
   a.nq = desc->n_q_heads;
   a.nkv = desc->n_kv_heads;
   a.d = desc->head_dim;
-  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &a.part_tokens, &a.n_parts,
-                 &a.waves);
+  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, desc->head_dim,
+                 elem_size(desc->dtype), &a.part_tokens, &a.n_parts, &a.waves);
   const int G2 = G;
   const size_t items = (size_t)n_rows * desc->n_kv_heads * a.n_parts;
   a.part_acc = (float*)ws;

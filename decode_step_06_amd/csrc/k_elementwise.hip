@@ -73,10 +73,52 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
 
 // The split-K residual add fused in front of the norm: x[t] += the slices
 // of the previous projection (slice order), written back, then the norm.
-template <typename T>
+// 16-byte chunks, CH per thread held in registers between the two passes;
+// all of a chunk's slice loads are in flight together (a chain of
+// dependent loads would cost one memory latency per slice).
+template <typename T, int CH>
 __global__ void __launch_bounds__(256) rmsnorm_reduce_kernel(float* __restrict__ x, const float* __restrict__ P,
                                                              long slice_stride, int splits, const T* __restrict__ g,
                                                              T* __restrict__ h, int H, float eps) {
+  const int t = blockIdx.x, H4 = H >> 2;
+  float* xr = x + (long)t * H;
+  const float* pr = P + (long)t * H;
+  f32x4_t v[CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i4 = threadIdx.x + c * 256;
+    if (i4 < H4) {
+      const f32x4_t add = slice_sum4(pr + 4 * i4, slice_stride, splits);
+      f32x4_t xv = *(const f32x4_t*)(xr + 4 * i4);
+      xv += add;
+      *(f32x4_t*)(xr + 4 * i4) = xv;
+      v[c] = xv;
+      ss += xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3];
+    }
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  T* hr = h + (long)t * H;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i4 = threadIdx.x + c * 256;
+    if (i4 < H4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Elem<T>::store(hr, 4 * i4 + e, v[c][e] * r * Elem<T>::load(g, 4 * i4 + e));
+    }
+  }
+}
+
+// Any H: one element at a time.
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_reduce_any_kernel(float* __restrict__ x, const float* __restrict__ P,
+                                                                 long slice_stride, int splits,
+                                                                 const T* __restrict__ g, T* __restrict__ h, int H,
+                                                                 float eps) {
   const int t = blockIdx.x;
   float* xr = x + (long)t * H;
   const float* pr = P + (long)t * H;
@@ -102,6 +144,13 @@ __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restric
                                                           long slice_stride, int splits, float* __restrict__ out,
                                                           int H) {
   const int t = blockIdx.x;
+  if ((H & 3) == 0) {
+    for (int i4 = threadIdx.x; i4 < (H >> 2); i4 += 256) {
+      const long o = (long)t * H + 4 * i4;
+      *(f32x4_t*)(out + o) = *(const f32x4_t*)(x + o) + slice_sum4(P + o, slice_stride, splits);
+    }
+    return;
+  }
   for (int i = threadIdx.x; i < H; i += 256) {
     float add = 0.f;
     for (int sp = 0; sp < splits; ++sp) add += P[sp * slice_stride + (long)t * H + i];
@@ -164,8 +213,10 @@ __global__ void __launch_bounds__(256) step_prologue_kernel(const T* __restrict_
 // the rotated k and the v into the paged cache at the row's slot (padding
 // rows, slot < 0, write no K/V).
 //
-// With splits > 1 the projection result arrives as fp32 slices (split K); the
-// row is first summed in slice order into LDS.
+// The row is first staged in LDS -- summed in slice order when the projection
+// arrives as split-K slices, every slice's load of a chunk in flight at once.
+// Then each thread produces whole 16-byte chunks: E consecutive elements j of
+// one head and, for q and k, their rotation partners j + d/2.
 template <typename T>
 __global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ qkv, long slice_stride, int splits,
                                                       const float* __restrict__ cosb,
@@ -173,53 +224,54 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ 
                                                       T* __restrict__ q_att, T* __restrict__ kc, T* __restrict__ vc,
                                                       int nq, int nkv, int d) {
   constexpr int E = Elem<T>::per16;
-  extern __shared__ float rowbuf[];
+  extern __shared__ __attribute__((aligned(16))) float rowbuf[];
   const int t = blockIdx.x;
-  const int half = d >> 1, G = nq / nkv, nch = d / E;
+  const int half = d >> 1, G = nq / nkv, nch = d / E, hch = half / E;
   const int width = (nq + 2 * nkv) * d;
   const float* row = qkv + (long)t * width;
-  if (splits > 1) {
-    for (int i = threadIdx.x; i < width; i += 256) {
-      float v = 0.f;
-      for (int sp = 0; sp < splits; ++sp) v += row[sp * slice_stride + i];
-      rowbuf[i] = v;
-    }
-    __syncthreads();
-    row = rowbuf;
-  }
+  for (int i4 = threadIdx.x; i4 < (width >> 2); i4 += 256)
+    *(f32x4_t*)(rowbuf + 4 * i4) = slice_sum4(row + 4 * i4, slice_stride, splits);
+  __syncthreads();
   const float* cr = cosb + (long)t * half;
   const float* sr = sinb + (long)t * half;
   const int s = slot[t];
   const long blk = s >= 0 ? (long)(s / NS_BLOCK) : 0;
   const int tok = s >= 0 ? s % NS_BLOCK : 0;
-  // q heads
-  for (int i = threadIdx.x; i < nq * half; i += 256) {
-    const int hq = i / half, j = i % half;
-    const float x1 = row[hq * d + j], x2 = row[hq * d + j + half];
-    const float c = cr[j], sn = sr[j];
-    const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
-    const int g = hq / G, hh = hq % G;
-    const long base = ((long)t * nkv + g) * nch * G * E + (long)hh * E;
-    Elem<T>::store(q_att, base + (long)(j / E) * G * E + j % E, y1);
-    Elem<T>::store(q_att, base + (long)((j + half) / E) * G * E + (j + half) % E, y2);
-  }
-  if (s < 0) return;
-  // k heads (rotated) into the chunk-interleaved K layout
-  const float* kr = row + nq * d;
-  for (int i = threadIdx.x; i < nkv * half; i += 256) {
-    const int g = i / half, j = i % half;
-    const float x1 = kr[g * d + j], x2 = kr[g * d + j + half];
-    const float c = cr[j], sn = sr[j];
-    const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
-    const long base = (blk * nkv + g) * (long)nch * NS_BLOCK * E + (long)tok * E;
-    Elem<T>::store(kc, base + (long)(j / E) * NS_BLOCK * E + j % E, y1);
-    Elem<T>::store(kc, base + (long)((j + half) / E) * NS_BLOCK * E + (j + half) % E, y2);
-  }
-  // v heads into token rows
-  const float* vr = row + (nq + nkv) * d;
-  for (int i = threadIdx.x; i < nkv * d; i += 256) {
-    const int g = i / d, j = i % d;
-    Elem<T>::store(vc, ((blk * nkv + g) * NS_BLOCK + tok) * (long)d + j, vr[i]);
+  const int n_q = nq * hch, n_k = s >= 0 ? nkv * hch : 0, n_v = s >= 0 ? nkv * nch : 0;
+  for (int it = threadIdx.x; it < n_q + n_k + n_v; it += 256) {
+    if (it < n_q + n_k) {
+      // rotate chunk c (elements j0..j0+E) of head hd with its partners
+      const bool is_q = it < n_q;
+      const int w = is_q ? it : it - n_q;
+      const int hd = w / hch, c = w % hch, j0 = c * E;
+      const float* src = rowbuf + (is_q ? 0 : nq * d) + hd * d;
+      float y1[E], y2[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float x1 = src[j0 + e], x2 = src[j0 + half + e];
+        const float cs = cr[j0 + e], sn = sr[j0 + e];
+        y1[e] = x1 * cs - x2 * sn;
+        y2[e] = x2 * cs + x1 * sn;
+      }
+      if (is_q) {
+        const int g = hd / G, hh = hd % G;
+        T* base = q_att + ((long)t * nkv + g) * nch * G * E + (long)hh * E;
+        Chunk<T>::store(base + (long)c * G * E, y1);
+        Chunk<T>::store(base + (long)(c + hch) * G * E, y2);
+      } else {
+        T* base = kc + (blk * nkv + hd) * (long)nch * NS_BLOCK * E + (long)tok * E;
+        Chunk<T>::store(base + (long)c * NS_BLOCK * E, y1);
+        Chunk<T>::store(base + (long)(c + hch) * NS_BLOCK * E, y2);
+      }
+    } else {
+      // v chunk c of KV head g into its token row
+      const int w = it - n_q - n_k;
+      const int g = w / nch, c = w % nch;
+      float y[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) y[e] = rowbuf[(nq + nkv) * d + g * d + c * E + e];
+      Chunk<T>::store(vc + ((blk * nkv + g) * NS_BLOCK + tok) * (long)d + c * E, y);
+    }
   }
 }
 
@@ -313,7 +365,7 @@ void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, 
                     const float* sinb, const int32_t* slot, void* q_att, void* kc, void* vc, int T, int nq, int nkv,
                     int d, hipStream_t st) {
   if (T <= 0) return;
-  const size_t lds = splits > 1 ? (size_t)(nq + 2 * nkv) * d * sizeof(float) : 0;
+  const size_t lds = (size_t)(nq + 2 * nkv) * d * sizeof(float);
   if (dtype == NS_DT_BF16)
     hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb, sinb,
                        slot, (bf16_t*)q_att, (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
@@ -322,15 +374,34 @@ void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, 
                        slot, (float*)q_att, (float*)kc, (float*)vc, nq, nkv, d);
 }
 
+template <typename T>
+static void run_rmsnorm_reduce(float* x, const float* P, long slice_stride, int splits, const T* g, T* h, int T_,
+                               int H, float eps, hipStream_t st) {
+  const int ch = (H / 4 + 255) / 256;
+  if (H % 4 != 0 || ch > 8)
+    hipLaunchKernelGGL(rmsnorm_reduce_any_kernel<T>, dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
+                       H, eps);
+  else if (ch == 1)
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 1>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
+                       H, eps);
+  else if (ch == 2)
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 2>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
+                       H, eps);
+  else if (ch <= 4)
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 4>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
+                       H, eps);
+  else
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 8>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
+                       H, eps);
+}
+
 void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_stride, int splits, const void* g,
                            void* h, int T, int H, float eps, hipStream_t st) {
   if (T <= 0) return;
   if (dtype == NS_DT_BF16)
-    hipLaunchKernelGGL(rmsnorm_reduce_kernel<bf16_t>, dim3(T), dim3(256), 0, st, x, P, slice_stride, splits,
-                       (const bf16_t*)g, (bf16_t*)h, H, eps);
+    run_rmsnorm_reduce<bf16_t>(x, P, slice_stride, splits, (const bf16_t*)g, (bf16_t*)h, T, H, eps, st);
   else
-    hipLaunchKernelGGL(rmsnorm_reduce_kernel<float>, dim3(T), dim3(256), 0, st, x, P, slice_stride, splits,
-                       (const float*)g, (float*)h, H, eps);
+    run_rmsnorm_reduce<float>(x, P, slice_stride, splits, (const float*)g, (float*)h, T, H, eps, st);
 }
 
 void launch_reduce_rows(const float* x, const float* P, long slice_stride, int splits, float* out, int T, int H,

@@ -48,7 +48,8 @@ struct GemmCfg {
 template <int BM, int BN, int BK, int WM, int WN, int EPI, typename OutT>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                                  const bf16_t* __restrict__ B, int ldb, int M, int N,
-                                                                 int K, void* __restrict__ Cv, int ldc) {
+                                                                 int K, void* __restrict__ Cv, int ldc, int splits,
+                                                                 long slice_stride) {
   using C = GemmCfg<BM, BN, BK, WM, WN, EPI>;
   constexpr int LDK = C::LDK;
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDK];
@@ -134,14 +135,17 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
-  load_slab(0);
+  // K slabs [sb, se) of split blockIdx.y (all of K unless EPI_PARTIAL)
+  const int slabs = K / BK, split = blockIdx.y;
+  const int sb = (int)((long)split * slabs / splits), se = (int)((long)(split + 1) * slabs / splits);
+  const int nk = se - sb;
+  load_slab(sb * BK);
   store_slab(0);
   __syncthreads();
   const int fr = lane & 15, fk = (lane >> 4) * 8;  // fragment row / k offset of this lane
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_slab((kt + 1) * BK);
+    if (kt + 1 < nk) load_slab((sb + kt + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       bf16x8_t af[C::FM], bfr[C::FN];
@@ -177,7 +181,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
         }
       }
   } else {
-    float* Cp = (float*)Cv;
+    float* Cp = (float*)Cv + (EPI == EPI_PARTIAL ? split * slice_stride : 0);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -245,7 +249,7 @@ constexpr unsigned BUF_RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit dwords, n
 template <int EPI, typename OutT>
 __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
                                                        const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
-                                                       void* __restrict__ Cv, int ldc) {
+                                                       void* __restrict__ Cv, int ldc, int splits, long slice_stride) {
   constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
   constexpr int TM = 128, TN = 128, FM = 4, FN = 4;  // 32 x 32 fragments
   constexpr int ROWB = BK * 2;                  // bytes per LDS row
@@ -299,10 +303,14 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
       voff[j] = (unsigned)(((long)brow * ldb + c * 8) * 2);
     }
   }
-  const int nk = K / BK;
+  // K slabs [sb, sb + nk) of split blockIdx.y (all of K unless EPI_PARTIAL);
+  // kt below counts slabs from sb.
+  const int slabs = K / BK, split = blockIdx.y;
+  const int sb = (int)((long)split * slabs / splits);
+  const int nk = (int)((long)(split + 1) * slabs / splits) - sb;
   // loads j0..j1-1 of slab kt into buffer kt % 4
   auto issue = [&](int kt, int j0, int j1) {
-    const int ks = kt < nk ? kt : nk - 1;
+    const int ks = sb + (kt < nk ? kt : nk - 1);
     const unsigned soff = (unsigned)ks * (BK * 2);
     char* base = lds + (kt % NSTAGE) * STAGE;
 #pragma unroll
@@ -438,7 +446,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
         }
       }
   } else {
-    float* Cp = (float*)Cv;
+    float* Cp = (float*)Cv + (EPI == EPI_PARTIAL ? split * slice_stride : 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -546,15 +554,14 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
     for (int j = 0; j < NB; ++j) red[wave][i * NB + j][lane] = acc[i][j];
   __syncthreads();
   if (wave != 0) return;
+  // wavefront 0 adds the others' partials in wavefront order (the outer loop
+  // stays rolled so only the accumulators are live)
+#pragma unroll 1
+  for (int w = 1; w < NW; ++w)
 #pragma unroll
-  for (int i = 0; i < MF; ++i)
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      f32x4_t a = red[0][i * NB + j][lane];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) a += red[w][i * NB + j][lane];
-      acc[i][j] = a;
-    }
+      for (int j = 0; j < NB; ++j) acc[i][j] += red[w][i * NB + j][lane];
 
   // Epilogue.  Fragment element r of lane l is row 4*(l/16)+r, column l%16.
   const int er = (lane >> 4) * 4, ec = lane & 15;
@@ -613,11 +620,21 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
 
 template <int BM, int BN, int BK, int WM, int WN, int EPI>
 static void run_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
-                     hipStream_t st) {
+                     hipStream_t st, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? BN / 2 : BN;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t>), dim3((unsigned)tiles), dim3(64 * WM * WN),
-                     0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t>), dim3((unsigned)tiles, (unsigned)splits),
+                     dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc,
+                     splits, slice_stride);
+}
+
+template <int EPI>
+static void run_big(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
+                    hipStream_t st, int splits = 1, long slice_stride = 0) {
+  constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
+  const long tiles = (long)((M + 255) / 256) * ((N + OUT_BN - 1) / OUT_BN);
+  hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0, st,
+                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride);
 }
 
 template <int MF, int NF, int NW, int EPI>
@@ -630,19 +647,72 @@ static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B,
                      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride);
 }
 
-int gemm_partial_splits(int N, int K) {
-  const int steps = K / 32;
-  const int tiles = (N + 15) / 16;
-  return std::max(1, std::min(8, std::min(steps / 8, 512 / std::max(1, tiles))));
+// Tile shapes for M > 64 rows, largest first: 256 x 256 (the big kernel),
+// 128 x 128 and 64 x 64 (the LDS double-buffered kernel, 4 wavefronts).
+enum TileKind { TILE_BIG = 0, TILE_128 = 1, TILE_64 = 2 };
+constexpr int kTileRows[3] = {256, 128, 64};
+constexpr int kTileCols[3] = {256, 128, 64};
+constexpr int kFillTarget = 256;  // workgroups that fill the chip (one per CU)
+
+// The big kernel addresses its operands with 32-bit buffer offsets.
+static bool big_fits(int M, int lda, long b_rows, int ldb) {
+  return (long)M * lda * 2 < (1L << 32) && b_rows * ldb * 2 < (1L << 32);
+}
+
+// Output tiles of a launch; SwiGLU tiles hold gate and up columns, so they
+// cover 128, 64 and 64 output columns.
+static long tile_count(int kind, int M, int N, bool swiglu) {
+  const int cols = swiglu ? (kind == TILE_BIG ? 128 : 64) : kTileCols[kind];
+  return (long)((M + kTileRows[kind] - 1) / kTileRows[kind]) * ((N + cols - 1) / cols);
+}
+
+// Split-K plan for M > 64 rows: the largest tile whose tiles x splits fill
+// the chip with at least 4 K slabs of 32 per split; failing that, the one
+// with the most workgroups.
+struct PartialPlan {
+  int kind, splits;
+};
+static PartialPlan partial_plan(int M, int N, int K) {
+  const int slabs = K / 32;
+  const int max_s = std::max(1, std::min(8, slabs / 4));
+  PartialPlan best{TILE_64, 1};
+  long best_wg = -1;
+  for (int kind = (M > 128 ? TILE_BIG : TILE_128); kind <= TILE_64; ++kind) {
+    const long tiles = tile_count(kind, M, N, false);
+    const int s = (int)std::max(1L, std::min((long)max_s, (kFillTarget + tiles - 1) / tiles));
+    if (tiles * s >= kFillTarget) return {kind, s};
+    if (tiles * s > best_wg) {
+      best_wg = tiles * s;
+      best = {kind, s};
+    }
+  }
+  return best;
+}
+
+int gemm_partial_splits(int M, int N, int K) {
+  if (M <= 64) {  // weight-streaming kernel: 16-column tiles
+    const int steps = K / 32;
+    const int tiles = (N + 15) / 16;
+    return std::max(1, std::min(8, std::min(steps / 8, 512 / std::max(1, tiles))));
+  }
+  return partial_plan(M, N, K).splits;
 }
 
 int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* P, int ldp,
                         long slice_stride, int splits, hipStream_t st) {
   if (M <= 0 || N <= 0) return 0;
-  if (M > 64 || K % 32 != 0 || splits < 1) return -1;
+  if (K % 32 != 0 || splits < 1 || splits > K / 32) return -1;
   if (M <= 16) run_gemv<1, 1, 4, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
   else if (M <= 32) run_gemv<2, 1, 4, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
-  else run_gemv<4, 1, 4, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+  else if (M <= 64) run_gemv<4, 1, 4, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+  else {
+    int kind = partial_plan(M, N, K).kind;
+    if (kind == TILE_BIG && !big_fits(M, lda, N, ldb)) kind = TILE_128;
+    if (kind == TILE_BIG) run_big<EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+    else if (kind == TILE_128)
+      run_bf16<128, 128, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+    else run_bf16<64, 64, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+  }
   return 0;
 }
 
@@ -668,32 +738,25 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
   if (M <= 16) return dispatch_gemv_m<1, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   if (M <= 32) return dispatch_gemv_m<2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+  // M > 64: the largest tile shape that still gives the chip a workgroup
+  // per CU (the big kernel only past 128 rows and within 32-bit offsets);
+  // failing that, the one with the most workgroups.
   const bool k64 = (K % 64) == 0;
-  // the big kernel addresses its operands with 32-bit buffer offsets
   const long b_rows = (EPI == EPI_SILU_MUL) ? 2L * N : (long)N;
-  const bool fits32 = (long)M * lda * 2 < (1L << 32) && b_rows * ldb * 2 < (1L << 32);
-  if (M >= 256 && N >= 256 && fits32) {
-    constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
-    const long tiles = (long)((M + 255) / 256) * ((N + OUT_BN - 1) / OUT_BN);
-    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t>), dim3((unsigned)tiles), dim3(256), 0, st, (const bf16_t*)A,
-                       lda, (const bf16_t*)B, ldb, M, N, K, C, ldc);
-    return;
-  }
-  // The SwiGLU tile pairs gate and up fragments, so its wave tile needs at
-  // least two B fragments.
-  constexpr int BN16 = (EPI == EPI_SILU_MUL) ? 128 : 64;
-  if (M <= 16) {
-    if (k64) run_bf16<16, BN16, 64, 1, 4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-    else run_bf16<16, BN16, 32, 1, 4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  } else if (M <= 32) {
-    if (k64) run_bf16<32, 64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-    else run_bf16<32, 64, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  } else if (M <= 64) {
-    if (k64) run_bf16<64, 64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-    else run_bf16<64, 64, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  } else {
+  int kind = TILE_64;
+  for (int k = (M > 128 && big_fits(M, lda, b_rows, ldb) ? TILE_BIG : TILE_128); k <= TILE_64; ++k)
+    if (tile_count(k, M, N, EPI == EPI_SILU_MUL) >= kFillTarget) {
+      kind = k;
+      break;
+    }
+  if (kind == TILE_BIG) return run_big<EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+  if (kind == TILE_128) {
     if (k64) run_bf16<128, 128, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
     else run_bf16<128, 128, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+  } else {
+    constexpr int BN64 = (EPI == EPI_SILU_MUL) ? 128 : 64;
+    if (k64) run_bf16<64, BN64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+    else run_bf16<64, BN64, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   }
 }
 

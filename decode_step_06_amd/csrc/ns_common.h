@@ -51,6 +51,63 @@ template <> struct Elem<bf16_t> {
   __device__ static __forceinline__ void store(bf16_t* p, long i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// 16-byte chunks: E = Elem<T>::per16 values of a row as float, and back.
+template <typename T> struct Chunk;
+template <> struct Chunk<float> {
+  __device__ static __forceinline__ void load(const float* p, float* v) {
+    const f32x4_t a = *(const f32x4_t*)p;
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  }
+  __device__ static __forceinline__ void store(float* p, const float* v) {
+    *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]};
+  }
+};
+template <> struct Chunk<bf16_t> {
+  __device__ static __forceinline__ void load(const bf16_t* p, float* v) {
+    const u32x4_t a = *(const u32x4_t*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = a[i];
+      v[2 * i] = lo_bf16(w);
+      v[2 * i + 1] = hi_bf16(w);
+    }
+  }
+  __device__ static __forceinline__ void store(bf16_t* p, const float* v) {
+    *(u32x4_t*)p = u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
+                           pack_bf16(v[6], v[7])};
+  }
+};
+
+constexpr int kMaxSplits = 8;  // split-K slices a consumer sums
+
+// Sum of S fp32 slices (slice_stride floats apart) at one 16-byte position,
+// in slice order, every load issued before the first add.
+template <int S>
+__device__ __forceinline__ f32x4_t slice_sum4_n(const float* p, long slice_stride) {
+  f32x4_t v[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) v[s] = *(const f32x4_t*)(p + s * slice_stride);
+  f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < S; ++s) a += v[s];
+  return a;
+}
+
+// The same for a runtime count 1..8 (a uniform branch to straight-line code;
+// predicated loads would wait for each load in turn).
+__device__ __forceinline__ f32x4_t slice_sum4(const float* p, long slice_stride, int splits) {
+  switch (splits) {
+    case 1: return slice_sum4_n<1>(p, slice_stride);
+    case 2: return slice_sum4_n<2>(p, slice_stride);
+    case 3: return slice_sum4_n<3>(p, slice_stride);
+    case 4: return slice_sum4_n<4>(p, slice_stride);
+    case 5: return slice_sum4_n<5>(p, slice_stride);
+    case 6: return slice_sum4_n<6>(p, slice_stride);
+    case 7: return slice_sum4_n<7>(p, slice_stride);
+    default: return slice_sum4_n<kMaxSplits>(p, slice_stride);
+  }
+}
+
 // Wavefront (64-lane) reductions.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -24,12 +24,13 @@ int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda,
                 int ldc, hipStream_t st);
 int gemm_supported(int dtype, int K);
 
-// Split-K projection for decode batches (bf16, M <= 64): slice s of the
-// result (P + s * slice_stride, [M, N] with row stride ldp) holds the sum
-// over the s-th of `splits` contiguous K ranges; the consumer sums the
-// slices in order.  gemm_partial_splits picks the split count from N and K
-// alone.  Returns -1 for unsupported shapes.
-int gemm_partial_splits(int N, int K);
+// Split-K projection (bf16): slice s of the result (P + s * slice_stride,
+// [M, N] with row stride ldp) holds the sum over the s-th of `splits`
+// contiguous ranges of K's 32-wide slabs; the consumer sums the slices in
+// order.  gemm_partial_splits picks the split count that fills the chip for
+// this shape (for M <= 64 from N and K alone).  Any 1 <= splits <= K / 32
+// is accepted.  Returns -1 for unsupported shapes.
+int gemm_partial_splits(int M, int N, int K);
 int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* P, int ldp,
                         long slice_stride, int splits, hipStream_t st);
 

@@ -158,24 +158,40 @@ def fill_past(h: EngineHandle, past_seq, past_pos, past_k: List, past_v: List, d
 
 
 def fill_past_random_on_device(h: EngineHandle, past_seq, past_pos, seed: int = 4, device="cuda",
-                               chunk: int = 1 << 16) -> None:
+                               chunk: int = 1 << 16, keep=None):
     """Past K/V ~ N(0, 1) drawn on the device (large workloads), scattered
-    layer by layer in chunks of positions."""
+    layer by layer in chunks of positions.
+
+    ``keep``: optional boolean mask over the past positions; the drawn values
+    (on the model's storage grid) of the kept positions are copied back as
+    float32 host arrays and returned as (k_layers, v_layers), so a checker can
+    rebuild the same context for a sample of sequences without reading the
+    cache back through the library."""
     n = int(len(past_seq))
+    s = h.shape
+    kept_k = [[] for _ in range(s.n_layers)]
+    kept_v = [[] for _ in range(s.n_layers)]
     if n == 0:
-        return
+        return (kept_k, kept_v) if keep is not None else None
     slots = torch.from_numpy(ns.ns_slot_map(h.kv, past_seq, past_pos)).to(device)
     dt = torch_dtype(h.shape)
     g = torch.Generator(device=device)
     g.manual_seed(seed)
-    s = h.shape
+    keep_t = torch.from_numpy(np.asarray(keep, dtype=bool)).to(device) if keep is not None else None
     for layer in range(s.n_layers):
         for c0 in range(0, n, chunk):
             m = min(chunk, n - c0)
             k = torch.randn((m, s.n_kv_heads, s.head_dim), generator=g, device=device).to(dt)
             v = torch.randn((m, s.n_kv_heads, s.head_dim), generator=g, device=device).to(dt)
             ns.ns_kv_scatter(h.eng, layer, m, slots[c0:].data_ptr(), k.data_ptr(), v.data_ptr())
+            if keep_t is not None:
+                sel = keep_t[c0:c0 + m]
+                kept_k[layer].append(k[sel].float().cpu().numpy())
+                kept_v[layer].append(v[sel].float().cpu().numpy())
     torch.cuda.synchronize()
+    if keep is None:
+        return None
+    return ([np.concatenate(a) for a in kept_k], [np.concatenate(a) for a in kept_v])
 
 
 def alloc_sequences(h: EngineHandle, seq_lens) -> None:

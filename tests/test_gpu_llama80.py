@@ -1,0 +1,127 @@
+"""The LLaMA-2-70B-shaped 80-layer decode step at full size on one GPU:
+256 sequences, contexts uniform in 512..1536, untied vocabulary 32000,
+random weights and context drawn on the device (about 138 GB of weights and
+88 GB of cache), the two-way nano-batch split with GEMM || attention overlap,
+the whole step in one hipGraph -- the launch configuration the benchmark
+times.  Checked: graph replay = eager step bit for bit, overlap on = off bit
+for bit, unsplit = split within the stack bound, and the logits of a sample of
+rows against the oracle, which streams the weights to the host one layer at a
+time.
+
+The bound at 80 layers comes from the oracle itself.  GPU and oracle store
+bf16 at the same points, from fp32 vs fp64 values, so a few roundings land on
+neighbouring bf16 values; through 80 layers of random weights these
+differences grow until the two results are about as far apart as bf16 storage
+moves the result at all.  The oracle measures that distance on the same rows
+(its bf16-storage run against its all-fp64 run, D); two such independent
+roundings of one exact result differ by about sqrt(2) D, so the GPU must stay
+within 1.5 D of the bf16-storage oracle, and within the a-priori stack bound
+when that is looser."""
+import numpy as np
+import pytest
+import torch
+
+from decode_step_06_amd import ns
+from decode_step_06_amd.configs import LLAMA70B, WORKLOADS
+from decode_step_06_amd.inputs import gen_batch
+from decode_step_06_amd.runner import (DeviceWeights, alloc_sequences, blocks_for, create_engine,
+                                       fill_past_random_on_device)
+from gpu_helpers import assert_close, max_abs, oracle_sampled, rel_l2, sample_rows, say, stack_tol
+
+pytestmark = pytest.mark.gpu
+
+
+class _LayerStream:
+    """The oracle's per-layer weights, copied from the device one layer at a
+    time and widened to float64 (exact for bf16 values)."""
+
+    def __init__(self, dw):
+        self.dw = dw
+        self.idx = -1
+        self.cur = None
+
+    def __len__(self):
+        return len(self.dw.t["layers"])
+
+    def __getitem__(self, layer):
+        if layer != self.idx:
+            if layer % 10 == 0:
+                say(f"  oracle layer {layer}")
+            self.cur = None
+            self.cur = {k: v.cpu().double().numpy() for k, v in self.dw.t["layers"][layer].items()}
+            self.idx = layer
+        return self.cur
+
+
+@pytest.mark.timeout(900)
+def test_llama70b_80_layers_b256_graph_nano_and_sampled_oracle():
+    w = WORKLOADS["llama70b_80l_b256"]
+    shape = LLAMA70B
+    torch.cuda.empty_cache()
+    b = gen_batch(w, with_past=False, pool_slack=1.02)
+    rows = sample_rows(b.n_rows, 5)
+    seqs = sorted({int(b.row_seq[r]) for r in rows})
+    keep = np.isin(b.past_seq, seqs)
+    maxb = blocks_for(b.seq_lens)
+    say(f"llama70b 80 layers: B={b.n_rows}, contexts {int(b.seq_lens.min())}..{int(b.seq_lens.max())}, "
+        f"pool {b.num_blocks} blocks, nano {w.nano_splits}, sampled rows {rows}")
+    dw = DeviceWeights.random_on_device(shape, seed=w.seeds["weights"])
+    say(f"  weights on device: {dw.bytes() / 1e9:.1f} GB")
+    nano = ns.make_sched(nano_rows=w.nano_splits, overlap=True)
+    h = create_engine(shape, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, nano)
+    stream = torch.cuda.Stream()
+    try:
+        alloc_sequences(h, b.seq_lens)
+        kept_k, kept_v = fill_past_random_on_device(h, b.past_seq, b.past_pos, seed=w.seeds["kv"], keep=keep)
+        say(f"  cache filled: {h.kv_mem.numel() / 1e9:.1f} GB")
+        nb = ns.Batch(b.row_seq, b.row_pos, b.tokens)
+        out_g = torch.full((b.n_rows, shape.vocab), float("nan"), device="cuda")
+        out_e = torch.full_like(out_g, float("nan"))
+        g = ns.ns_graph_capture(h.eng, b.n_rows, out_g.data_ptr(), stream)
+        try:
+            ns.ns_graph_replay(g, nb, stream)
+            stream.synchronize()
+        finally:
+            ns.ns_graph_destroy(g)
+        ns.ns_decode_step(h.eng, nb, out_e.data_ptr(), stream)
+        stream.synchronize()
+        assert torch.equal(out_g, out_e), "graph replay differs from the eager step"
+        say("  graph replay == eager (bit-exact)")
+        ns.ns_engine_set_sched(h.eng, ns.make_sched(nano_rows=w.nano_splits, overlap=False))
+        ns.ns_decode_step(h.eng, nb, out_e.data_ptr(), stream)
+        stream.synchronize()
+        assert torch.equal(out_g, out_e), "overlapped nano-batches differ from serial nano-batches"
+        say("  overlap on == off (bit-exact)")
+        n_split = ns.ns_engine_last_launches(h.eng)
+        ns.ns_engine_set_sched(h.eng, ns.make_sched())
+        ns.ns_decode_step(h.eng, nb, out_e.data_ptr(), stream)
+        stream.synchronize()
+        n_unsplit = ns.ns_engine_last_launches(h.eng)
+        assert n_split > n_unsplit, "the nano-batch split did not take effect"
+        assert_close(out_e.cpu().numpy(), out_g.cpu().numpy(), "bf16_stack80", "unsplit vs nano split")
+        got = out_g[rows].cpu().numpy()
+        del out_g, out_e
+        weights = {"layers": _LayerStream(dw),
+                   "final_norm": dw.t["final_norm"].cpu().double().numpy(),
+                   "embed": dw.t["embed"].cpu().double().numpy(),
+                   "lm_head": dw.t["lm_head"].cpu().double().numpy()}
+        say("  oracle (bf16 storage points): streaming 80 layers")
+        ref = oracle_sampled(shape, weights, b, rows, keep, kept_k, kept_v, emulate=True)
+        say("  oracle (float64 throughout): streaming 80 layers")
+        exact = oracle_sampled(shape, weights, b, rows, keep, kept_k, kept_v, emulate=False)
+    finally:
+        h.destroy()
+        del dw
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    d_rel, d_abs = rel_l2(ref, exact), max_abs(ref, exact)
+    tr, ta = stack_tol(80)
+    tr, ta = max(tr, 1.5 * d_rel), max(ta, 1.5 * d_abs)
+    r, m = rel_l2(got, ref), max_abs(got, ref)
+    say(f"  bf16 storage moves the oracle by rel_l2={d_rel:.3e} max_abs={d_abs:.3e}")
+    say(f"  parity 80-layer logits of sampled rows: rel_l2={r:.3e} (<= {tr:.3e}) max_abs={m:.3e} (<= {ta:.3e}); "
+        f"GPU vs float64 oracle rel_l2={rel_l2(got, exact):.3e}")
+    assert np.isfinite(got).all()
+    assert r <= tr and m <= ta
+    agree = (np.argmax(got, 1) == np.argmax(ref, 1)).mean()
+    say(f"  argmax agreement {agree:.3f} over {len(rows)} rows")
