@@ -18,6 +18,8 @@
 // trip: fp32 store (QKV, logits), fp32 residual add (O and Down projections
 // write x += y), and the SwiGLU product (the tile loads gate rows and the
 // matching up rows, so silu(gate) * up is formed in registers).
+#include <type_traits>
+
 #include "ns_kernels.h"
 
 namespace ns {
@@ -487,7 +489,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
   constexpr int DUAL = (EPI == EPI_SILU_MUL) ? 2 : 1;
   constexpr int NB = NF * DUAL;  // B fragments per k-step (U k-steps in flight)
   __shared__ f32x4_t red[NW][MF * NB][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = blockIdx.x / splits, split = blockIdx.x % splits;
   const int n0 = tile * 16 * NF;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
@@ -519,33 +521,41 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  int s = s0;
-  for (; s + U <= s1; s += U) {
-    bf16x8_t bv[U][NB], av[U][MF];
+  // Rounds of up to U k-steps, every load of a round in flight before its
+  // first MFMA; a short last round takes exactly its remaining steps (a
+  // uniform switch into straight-line code -- predicated loads would be
+  // waited for one by one).
+  auto round = [&](auto r_const, int s) {
+    constexpr int R = decltype(r_const)::value;
+    bf16x8_t bv[R][NB], av[R][MF];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < R; ++u) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) bv[u][j] = *(const bf16x8_t*)(brow[j] + (s + u) * 32);
 #pragma unroll
       for (int i = 0; i < MF; ++i) av[u][i] = *(const bf16x8_t*)(arow[i] + (s + u) * 32);
     }
+    // keep the scheduler from trading loads in flight for registers
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < R; ++u)
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][i], bv[u][j], acc[i][j], 0, 0, 0);
-  }
-  for (; s < s1; ++s) {
-    bf16x8_t bv[NB], av[MF];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) bv[j] = *(const bf16x8_t*)(brow[j] + s * 32);
-#pragma unroll
-    for (int i = 0; i < MF; ++i) av[i] = *(const bf16x8_t*)(arow[i] + s * 32);
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][i], bv[u][j], acc[i][j], 0, 0, 0);
+  };
+  int s = s0;
+  for (; s + U <= s1; s += U) round(std::integral_constant<int, U>{}, s);
+  switch (s1 - s) {  // 0 .. U-1 steps left
+    case 1: round(std::integral_constant<int, 1>{}, s); break;
+    case 2: round(std::integral_constant<int, 2>{}, s); break;
+    case 3: round(std::integral_constant<int, 3>{}, s); break;
+    case 4: if constexpr (U > 4) round(std::integral_constant<int, (U > 4 ? 4 : 1)>{}, s); break;
+    case 5: if constexpr (U > 5) round(std::integral_constant<int, (U > 5 ? 5 : 1)>{}, s); break;
+    case 6: if constexpr (U > 6) round(std::integral_constant<int, (U > 6 ? 6 : 1)>{}, s); break;
+    case 7: if constexpr (U > 7) round(std::integral_constant<int, (U > 7 ? 7 : 1)>{}, s); break;
+    default: break;
   }
 
 #pragma unroll
@@ -641,7 +651,9 @@ template <int MF, int NF, int NW, int EPI>
 static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
                      hipStream_t st, int splits = 1, long slice_stride = 0) {
   constexpr int NB = NF * (EPI == EPI_SILU_MUL ? 2 : 1);
-  constexpr int U = (MF + NB) <= 4 ? 8 : 4;  // k-steps in flight, as registers allow
+  // k-steps in flight, as registers allow (1024-thread workgroups get 128
+  // VGPRs per lane)
+  constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 4 ? 8 : 4);
   const unsigned grid = (unsigned)((N + 16 * NF - 1) / (16 * NF) * splits);
   hipLaunchKernelGGL((gemv_bf16_kernel<MF, NF, NW, U, EPI, bf16_t>), dim3(grid), dim3(64 * NW), 0, st,
                      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride);
@@ -702,10 +714,21 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
                         long slice_stride, int splits, hipStream_t st) {
   if (M <= 0 || N <= 0) return 0;
   if (K % 32 != 0 || splits < 1 || splits > K / 32) return -1;
-  if (M <= 16) run_gemv<1, 1, 4, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
-  else if (M <= 32) run_gemv<2, 1, 4, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
-  else if (M <= 64) run_gemv<4, 1, 4, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
-  else {
+  if (M <= 64) {
+    // two wavefronts per workgroup; 32 output columns per workgroup when
+    // that still leaves a workgroup per CU (measured best on MI355X at
+    // decode sizes)
+    const bool nf2 = (long)((N + 31) / 32) * splits >= 256;
+#define NS_GEMV_PART(MF)                                                                             \
+  do {                                                                                               \
+    if (nf2) run_gemv<MF, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride); \
+    else run_gemv<MF, 1, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);     \
+  } while (0)
+    if (M <= 16) NS_GEMV_PART(1);
+    else if (M <= 32) NS_GEMV_PART(2);
+    else NS_GEMV_PART(4);
+#undef NS_GEMV_PART
+  } else {
     int kind = partial_plan(M, N, K).kind;
     if (kind == TILE_BIG && !big_fits(M, lda, N, ldb)) kind = TILE_128;
     if (kind == TILE_BIG) run_big<EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
@@ -729,7 +752,7 @@ static void dispatch_gemv_m(int M, int N, int K, const void* A, int lda, const v
     if (wide) return run_gemv<MF, 4, 4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   }
   if (K > 2048) run_gemv<MF, 1, NW_LONG, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  else run_gemv<MF, 1, 4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+  else run_gemv<MF, 1, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
 }
 
 template <int EPI>
