@@ -1,0 +1,145 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m decode_step_06_amd.prof_summary trace TRACE_CSV --title T --cmd C [--kernel K --last N]
+    python -m decode_step_06_amd.prof_summary traffic --fetch FETCH_CSV --write WRITE_CSV --kernel K --last N
+        --source SRC --calib-bytes B --algorithmic-bytes A --out OUT --cmd C [--cmd C ...]
+
+``trace`` prints a markdown table of a ``--kernel-trace`` CSV (per kernel:
+dispatches, mean and total duration), and for kernel name K the mean over
+its last N dispatches (the benchmark's isolated back-to-back launches).
+
+``traffic`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the
+same command into HBM bytes per launch of kernel K (mean over its last N
+dispatches).  Each counter is scaled by what it reads for the command's
+plain 256 MiB device copy (the largest-fetch dispatch before the library's
+first kernel; B bytes read and B written): the counters' KiB are
+converted to bytes and calibrated so that the copy reads and writes exactly
+B.  The output file records the kernel's source file and its SHA-256, so a
+later change of the kernel invalidates the figure.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import os
+import re
+import sys
+
+
+def _short(name: str) -> str:
+    n = re.sub(r"\(.*", "", name)
+    n = n.replace("unsigned short", "bf16").replace("void ", "")
+    return n[:90]
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def trace(args):
+    rows = _rows(args.csv)
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = collections.defaultdict(list)
+    for r in rows:
+        per[_short(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = [f"# {args.title}", "", f"Command: `{args.cmd}`", "",
+           "rocprofv3 kernel trace; durations from each dispatch's start and end timestamps.", "",
+           "| kernel | dispatches | mean us | total ms |", "|---|---:|---:|---:|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        if "ns::" not in k:
+            continue
+        out.append(f"| `{k}` | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {sum(v) / 1e6:.3f} |")
+    if args.kernel:
+        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows if args.kernel in r["Kernel_Name"]]
+        tail = d[-args.last:] if args.last else d
+        if tail:
+            out += ["", f"Last {len(tail)} dispatches of `{args.kernel}` (the isolated back-to-back launches): "
+                        f"mean {sum(tail) / len(tail) / 1e3:.3f} us."]
+    print("\n".join(out))
+
+
+def _counter(rows, name):
+    """Dispatch id -> (kernel name, counter value)."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != name:
+            continue
+        did = int(r["Dispatch_Id"])
+        prev = out.get(did, (r["Kernel_Name"], 0.0))[1]
+        out[did] = (r["Kernel_Name"], prev + float(r["Counter_Value"]))
+    return out
+
+
+def traffic(args):
+    fetch = _counter(_rows(args.fetch), "FETCH_SIZE")
+    write = _counter(_rows(args.write), "WRITE_SIZE")
+    # the copy runs first: the largest-fetch dispatch before the library's
+    # first kernel
+    first_ns = min((d for d, (n, v) in fetch.items() if "ns::" in n), default=max(fetch) + 1)
+    calib = max((d for d, (n, v) in fetch.items() if d < first_ns), key=lambda d: fetch[d][1])
+    f_calib_kib = fetch[calib][1]
+    w_calib_kib = write.get(calib, (None, 0.0))[1]
+    if f_calib_kib <= 0 or w_calib_kib <= 0:
+        sys.exit("calibration copy not found in both runs")
+    f_scale = args.calib_bytes / (f_calib_kib * 1024.0)
+    w_scale = args.calib_bytes / (w_calib_kib * 1024.0)
+    kf = [v for d, (n, v) in sorted(fetch.items()) if args.kernel in n][-args.last:]
+    kw = [v for d, (n, v) in sorted(write.items()) if args.kernel in n][-args.last:]
+    if not kf or not kw:
+        sys.exit(f"no dispatches of {args.kernel}")
+    fk, wk = sum(kf) / len(kf), sum(kw) / len(kw)
+    fb, wb = fk * 1024.0 * f_scale, wk * 1024.0 * w_scale
+    digest = hashlib.sha256(open(args.source, "rb").read()).hexdigest()
+    lines = [f"# HBM traffic of {args.kernel}: rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated",
+             *[f"# command: {c}" for c in args.cmd],
+             f"kernel: {args.kernel}",
+             f"source: {os.path.relpath(args.source)}",
+             f"source_sha256: {digest}",
+             f"dispatches_averaged: {len(kf)}",
+             f"fetch_kib_per_dispatch: {fk:.1f}",
+             f"write_kib_per_dispatch: {wk:.1f}",
+             f"calibration_copy_bytes: {args.calib_bytes}",
+             f"calibration_fetch_kib: {f_calib_kib:.1f}",
+             f"calibration_write_kib: {w_calib_kib:.1f}",
+             f"fetch_scale: {f_scale:.4f}",
+             f"write_scale: {w_scale:.4f}",
+             f"fetch_bytes_per_launch: {fb:.0f}",
+             f"write_bytes_per_launch: {wb:.0f}",
+             f"traffic_bytes_per_launch: {fb + wb:.0f}",
+             f"algorithmic_bytes_per_launch: {args.algorithmic_bytes}",
+             f"traffic_over_algorithmic: {(fb + wb) / max(1, args.algorithmic_bytes):.3f}"]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("csv")
+    t.add_argument("--title", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--kernel")
+    t.add_argument("--last", type=int, default=0)
+    t.set_defaults(fn=trace)
+    r = sub.add_parser("traffic")
+    r.add_argument("--fetch", required=True)
+    r.add_argument("--write", required=True)
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--last", type=int, required=True)
+    r.add_argument("--source", required=True)
+    r.add_argument("--calib-bytes", type=int, default=256 << 20)
+    r.add_argument("--algorithmic-bytes", type=int, required=True)
+    r.add_argument("--out", required=True)
+    r.add_argument("--cmd", action="append", default=[])
+    r.set_defaults(fn=traffic)
+    args = ap.parse_args(argv)
+    args.fn(args)
+
+
+if __name__ == "__main__":
+    main()
