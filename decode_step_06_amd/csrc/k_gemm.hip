@@ -761,17 +761,26 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
   if (M <= 16) return dispatch_gemv_m<1, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   if (M <= 32) return dispatch_gemv_m<2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  // M > 64: the largest tile shape that still gives the chip a workgroup
-  // per CU (the big kernel only past 128 rows and within 32-bit offsets);
-  // failing that, the one with the most workgroups.
+  // M > 64: the tile shape with the best estimated throughput -- its
+  // relative per-CU rate (measured on MI355X at 2048 rows: the 256 x 256
+  // kernel 1.0, 128 x 128 about 0.55, 64 x 64 about 0.35) times the fill of
+  // its last wave of workgroups (256 resident at a time for the big kernel,
+  // 512 and 1024 for the LDS-light ones).  The big kernel needs more than
+  // 128 rows and 32-bit offsets.
   const bool k64 = (K % 64) == 0;
   const long b_rows = (EPI == EPI_SILU_MUL) ? 2L * N : (long)N;
+  constexpr double kRate[3] = {1.0, 0.55, 0.35};
+  constexpr long kSlots[3] = {256, 512, 1024};
   int kind = TILE_64;
-  for (int k = (M > 128 && big_fits(M, lda, b_rows, ldb) ? TILE_BIG : TILE_128); k <= TILE_64; ++k)
-    if (tile_count(k, M, N, EPI == EPI_SILU_MUL) >= kFillTarget) {
+  double best = -1.0;
+  for (int k = (M > 128 && big_fits(M, lda, b_rows, ldb) ? TILE_BIG : TILE_128); k <= TILE_64; ++k) {
+    const long t = tile_count(k, M, N, EPI == EPI_SILU_MUL);
+    const double fill = (double)t / (double)(kSlots[k] * ((t + kSlots[k] - 1) / kSlots[k]));
+    if (kRate[k] * fill > best + 1e-9) {
+      best = kRate[k] * fill;
       kind = k;
-      break;
     }
+  }
   if (kind == TILE_BIG) return run_big<EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   if (kind == TILE_128) {
     if (k64) run_bf16<128, 128, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
