@@ -194,9 +194,9 @@ struct ns_engine {
   float* cosb() const { return (float*)(ws + plan.cosb); }
   float* sinb() const { return (float*)(ws + plan.sinb); }
   int32_t* meta() const { return (int32_t*)(ws + plan.meta); }
-  // metadata block: tokens[T] | row_bseq[T] | pos[T] | slot[T] | btab[T][maxb]
+  // metadata block: tokens[T] | row index (-1: padding)[T] | pos[T] | slot[T] | btab[T][maxb] (one block-table
+  // row per step row)
   int32_t* m_tok() const { return meta(); }
-  int32_t* m_rowb() const { return meta() + max_tokens; }
   int32_t* m_pos() const { return meta() + 2 * max_tokens; }
   int32_t* m_slot() const { return meta() + 3 * max_tokens; }
   int32_t* m_btab() const { return meta() + 4 * max_tokens; }
@@ -264,31 +264,28 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
   int32_t* pos = m + 2 * T;
   int32_t* slot = m + 3 * T;
   int32_t* btab = m + 4 * T;
-  std::vector<int32_t> bseq_of(e->kv->max_seqs, -1);
-  int n_bseq = 0;
+  // one block-table row per step row (attention then reads its blocks
+  // without first looking up the row's sequence)
   for (int i = 0; i < rows; ++i) {
     const bool real = i < b->n_tok && b->seq[i] != -1;
     tok[i] = (i < b->n_tok && b->token_ids) ? b->token_ids[i] : 0;
     pos[i] = real ? b->pos[i] : 0;
+    int32_t* row = btab + (size_t)i * e->maxb;
     if (!real) {
       rowb[i] = -1;
       slot[i] = -1;
+      std::fill(row, row + e->maxb, -1);
       continue;
     }
     const int32_t s = b->seq[i];
-    if (bseq_of[s] < 0) {
-      bseq_of[s] = n_bseq;
-      const auto& tab = e->kv->tables[s];
-      int32_t* row = btab + (size_t)n_bseq * e->maxb;
-      for (int j = 0; j < e->maxb; ++j) row[j] = j < (int)tab.size() ? tab[j] : -1;
-      ++n_bseq;
-    }
-    rowb[i] = bseq_of[s];
+    const auto& tab = e->kv->tables[s];
+    for (int j = 0; j < e->maxb; ++j) row[j] = j < (int)tab.size() ? tab[j] : -1;
+    rowb[i] = i;
     const int32_t p = b->pos[i];
-    slot[i] = e->kv->tables[s][p / NS_BLOCK_SIZE] * NS_BLOCK_SIZE + p % NS_BLOCK_SIZE;
+    slot[i] = tab[p / NS_BLOCK_SIZE] * NS_BLOCK_SIZE + p % NS_BLOCK_SIZE;
   }
   const size_t head = 4 * (size_t)T * sizeof(int32_t);
-  const size_t bytes = head + (size_t)n_bseq * e->maxb * sizeof(int32_t);
+  const size_t bytes = head + (size_t)rows * e->maxb * sizeof(int32_t);
   HIP_TRY(hipMemcpyAsync(e->meta(), m, bytes, hipMemcpyHostToDevice, st));
   HIP_TRY(hipEventRecord(e->staging_ev[k], st));
   e->staging_used[k] = true;
@@ -300,7 +297,7 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
   a->q_att = e->q_att();
   a->kc = e->k_layer(layer);
   a->vc = e->v_layer(layer);
-  a->row_bseq = e->m_rowb();
+  a->row_bseq = nullptr;  // the step's table has one row per row
   a->row_pos = e->m_pos();
   a->btab = e->m_btab();
   a->maxb = e->maxb;

@@ -116,9 +116,21 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_decode_kernel(
     const int rest = w / n_parts;
     const int g = rest % nkv;
     const int t = row0 + rest / nkv;
-    const int bs = row_bseq[t];
+    // The row's block-table row: btab[row_bseq[t]], or row t itself when
+    // the table is laid out per row (row_bseq null) -- one dependent load
+    // fewer before the K/V loads.  Padding rows have no blocks.
+    const int32_t* __restrict__ bt;
+    bool pad;
+    if (row_bseq) {
+      const int bs = row_bseq[t];
+      pad = bs < 0;
+      bt = btab + (long)(pad ? 0 : bs) * maxb;
+    } else {
+      bt = btab + (long)t * maxb;
+      pad = bt[0] < 0;
+    }
     T* outp = out + (long)t * nq * D + (long)g * G * D;
-    if (bs < 0) {  // padding row: zero output
+    if (pad) {  // padding row: zero output
       if (part == 0)
         for (int i = threadIdx.x; i < G * D; i += 64 * NWAVE) outp[i] = T(0);
       continue;
@@ -128,7 +140,6 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_decode_kernel(
     if (start >= ctx) continue;
     const int end = min(start + P, ctx);
     const int nparts_row = (ctx + P - 1) / P;
-    const int32_t* __restrict__ bt = btab + (long)bs * maxb;
     const u32x4_t* __restrict__ q4 = (const u32x4_t*)(qatt + ((long)t * nkv + g) * NCH * G * E);
 
     float m[G], l[G], acc[G][E];
@@ -293,7 +304,7 @@ template <typename T, int D, int G>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int t = a.row0 + blockIdx.x / a.nkv;
   const int g = blockIdx.x % a.nkv;
-  if (a.row_bseq[t] < 0) return;
+  if ((a.row_bseq ? a.row_bseq[t] : a.btab[(long)t * a.maxb]) < 0) return;
   const int ctx = a.row_pos[t] + 1;
   const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;

@@ -65,7 +65,8 @@ struct AttnArgs {
   const void* q_att;        // [T][nkv][d/E][G][E]
   const void* kc;           // this layer's K region
   const void* vc;           // this layer's V region
-  const int32_t* row_bseq;  // [T] row -> block-table row (-1: padding)
+  const int32_t* row_bseq;  // [T] row -> block-table row (-1: padding); null: btab has one row per row
+                            // (padding rows: first entry -1)
   const int32_t* row_pos;   // [T]
   const int32_t* btab;      // [n_bseq][maxb]
   int maxb;
