@@ -248,19 +248,23 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
 
 constexpr unsigned BUF_RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit dwords, no swizzle
 
-template <int EPI, typename OutT>
+template <int EPI, typename OutT, int BM = 256>
 __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
                                                        const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
                                                        void* __restrict__ Cv, int ldc, int splits, long slice_stride) {
-  constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
-  constexpr int TM = 128, TN = 128, FM = 4, FN = 4;  // 32 x 32 fragments
+  static_assert(BM == 256 || BM == 128, "tile rows");
+  constexpr int BN = 256, BK = 32, NSTAGE = 4;
+  constexpr int TM = BM / 2, TN = 128, FM = TM / 32, FN = 4;  // 32 x 32 fragments
   constexpr int ROWB = BK * 2;                  // bytes per LDS row
   constexpr int STAGE = (BM + BN) * ROWB;       // bytes per slab buffer (A rows, then B rows)
-  constexpr int LOADS = (BM + BN) / 16 / 4;     // load instructions per wavefront per slab (8)
-  constexpr int PRE = 8;                        // MFMAs of a slab before its barrier
-  constexpr int LPRE = 4;                       // loads issued before the barrier
+  constexpr int AG = BM / 16;                   // 16-row load groups of A (then BN / 16 of B)
+  constexpr int LOADS = (BM + BN) / 16 / 4;     // load instructions per wavefront per slab (8 or 6)
+  constexpr int NMF = 2 * FM * FN;              // MFMAs per wavefront per slab (32 or 16)
+  constexpr int NREAD = 2 * (FM + FN);          // fragment reads per wavefront per slab (16 or 12)
+  constexpr int PRE = NMF / 4;                  // MFMAs of a slab before its barrier
+  constexpr int LPRE = BM == 256 ? LOADS / 2 : LOADS;  // loads issued before the barrier
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? BN / 2 : BN;
-  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];  // 128 KB
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];  // 128 or 96 KB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -279,16 +283,20 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)a_bytes, BUF_RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)b_bytes, BUF_RSRC_WORD3);
   // Load instruction j of wavefront w fills the 16 LDS rows of group
-  // g = w + 4 j (groups 0..15: A rows, 16..31: B rows); lane l loads row
-  // 16 (g mod 16) + l / 4, chunk (l & 3) ^ swz(row).  Rows past M or N
-  // repeat the last row (their results are never stored).
-  unsigned voff[LOADS];
+  // g = w + 4 j (groups 0..AG-1: A rows, then B rows); lane l loads row
+  // 16 g' + l / 4 of its operand (g' the group within it), chunk
+  // (l & 3) ^ swz(row).  Rows past M or N repeat the last row (their results
+  // are never stored).
+  // (sized for the largest tile: a value-dependent array size captured by
+  // the nested lambdas below stops the host pass from emitting the kernel)
+  static_assert(LOADS <= 8, "load slots");
+  unsigned voff[8];
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
     const int g = wave + 4 * j;
-    const int r = (g & 15) * 16 + (lane >> 2);
+    const int r = (g < AG ? g : g - AG) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz(r);
-    if (g < 16) {
+    if (g < AG) {
       int m = m0 + r;
       m = m < M ? m : M - 1;
       voff[j] = (unsigned)(((long)m * lda + c * 8) * 2);
@@ -318,7 +326,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       const int g = wave + 4 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < 16 ? ra : rb, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < AG ? ra : rb, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j],
                                                soff, 0, 0);
     }
   };
@@ -373,11 +381,12 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
       for (int j = 0; j < FN; ++j) fb[set][st][j] = *(const bf16x8_t*)(base + boff[st][j]);
     }
   };
-  // MFMAs q in [lo, hi) of a slab: K step q / 16, fragment (q / 4 % 4, q % 4)
+  // MFMAs q in [lo, hi) of a slab: K step q / (FM FN), fragment
+  // (q / FN % FM, q % FN)
   auto mfmas = [&](int set, int lo, int hi) {
 #pragma unroll
     for (int q = lo; q < hi; ++q) {
-      const int st = q >> 4, i = (q >> 2) & 3, j = q & 3;
+      const int st = q / (FM * FN), i = (q / FN) % FM, j = q % FN;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][st][i], fb[set][st][j], acc[i][j], 0, 0, 0);
     }
   };
@@ -387,28 +396,34 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
     // of it before the barrier of slab kt (lgkmcnt(0) below).
     issue(kt + 3, 0, LPRE);
     mfmas(set, 0, PRE);
+    // MFMA q of them followed by its share of the LPRE loads
 #pragma unroll
     for (int q = 0; q < PRE; ++q) {
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      if (q * LPRE / PRE != (q + 1) * LPRE / PRE) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+#pragma unroll
+      for (int r = q * LPRE / PRE; r < (q + 1) * LPRE / PRE; ++r) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Slab kt+1 landed (the 8 loads of slab kt+2 and the LPRE of slab kt+3
-    // issued after it may still be in flight) and this wavefront's reads of
-    // slab kt completed; after the barrier, the same holds for every
+    // Slab kt+1 landed (the LOADS loads of slab kt+2 and the LPRE of slab
+    // kt+3 issued after it may still be in flight) and this wavefront's reads
+    // of slab kt completed; after the barrier, the same holds for every
     // wavefront.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS + LPRE, 0));
     barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(kt + 1, set ^ 1);
     issue(kt + 3, LPRE, LOADS);
-    mfmas(set, PRE, 32);
-    constexpr int NR = 32 - PRE;
+    mfmas(set, PRE, NMF);
+    // the NREAD fragment reads one per MFMA, then the remaining loads spread
+    // over the MFMAs left
+    constexpr int NR = NMF - PRE, LREST = LOADS - LPRE;
+    constexpr int DEN = NR > NREAD ? NR - NREAD : 1;
+    static_assert(NR >= NREAD && (LREST == 0 || NR > NREAD), "schedule slots");
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
-      if (q < 16) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 1);
-      else if ((q - 16) * (LOADS - LPRE) / (NR - 16) != (q - 15) * (LOADS - LPRE) / (NR - 16))
+      if (q < NREAD) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 1);
+      else if (LREST > 0 && (q - NREAD) * LREST / DEN != (q + 1 - NREAD) * LREST / DEN)
         __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -425,7 +440,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
     slab(kt, 0);
     slab(kt + 1, 1);
   }
-  if (kt < nk) mfmas(0, 0, 32);  // odd slab count: the last slab is in set 0
+  if (kt < nk) mfmas(0, 0, NMF);  // odd slab count: the last slab is in set 0
   // Drain the trailing loads before the workgroup's LDS is released.
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
@@ -638,12 +653,12 @@ static void run_bf16(int M, int N, int K, const void* A, int lda, const void* B,
                      splits, slice_stride);
 }
 
-template <int EPI>
+template <int EPI, int BM = 256>
 static void run_big(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
                     hipStream_t st, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
-  const long tiles = (long)((M + 255) / 256) * ((N + OUT_BN - 1) / OUT_BN);
-  hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0, st,
+  const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
+  hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0, st,
                      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride);
 }
 
@@ -659,11 +674,11 @@ static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B,
                      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride);
 }
 
-// Tile shapes for M > 64 rows, largest first: 256 x 256 (the big kernel),
-// 128 x 128 and 64 x 64 (the LDS double-buffered kernel, 4 wavefronts).
-enum TileKind { TILE_BIG = 0, TILE_128 = 1, TILE_64 = 2 };
-constexpr int kTileRows[3] = {256, 128, 64};
-constexpr int kTileCols[3] = {256, 128, 64};
+// Tile shapes for M > 64 rows, largest first: 256 x 256 and 128 x 256 (the
+// big kernel), 128 x 128 and 64 x 64 (the LDS double-buffered kernel).
+enum TileKind { TILE_BIG = 0, TILE_BIG128 = 1, TILE_128 = 2, TILE_64 = 3 };
+constexpr int kTileRows[4] = {256, 128, 128, 64};
+constexpr int kTileCols[4] = {256, 256, 128, 64};
 constexpr int kFillTarget = 256;  // workgroups that fill the chip (one per CU)
 
 // The big kernel addresses its operands with 32-bit buffer offsets.
@@ -672,9 +687,9 @@ static bool big_fits(int M, int lda, long b_rows, int ldb) {
 }
 
 // Output tiles of a launch; SwiGLU tiles hold gate and up columns, so they
-// cover 128, 64 and 64 output columns.
+// cover half as many output columns.
 static long tile_count(int kind, int M, int N, bool swiglu) {
-  const int cols = swiglu ? (kind == TILE_BIG ? 128 : 64) : kTileCols[kind];
+  const int cols = swiglu ? kTileCols[kind] / 2 : kTileCols[kind];
   return (long)((M + kTileRows[kind] - 1) / kTileRows[kind]) * ((N + cols - 1) / cols);
 }
 
@@ -689,7 +704,7 @@ static PartialPlan partial_plan(int M, int N, int K) {
   const int max_s = std::max(1, std::min(8, slabs / 4));
   PartialPlan best{TILE_64, 1};
   long best_wg = -1;
-  for (int kind = (M > 128 ? TILE_BIG : TILE_128); kind <= TILE_64; ++kind) {
+  for (int kind = (M > 128 ? TILE_BIG : TILE_BIG128); kind <= TILE_64; ++kind) {
     const long tiles = tile_count(kind, M, N, false);
     const int s = (int)std::max(1L, std::min((long)max_s, (kFillTarget + tiles - 1) / tiles));
     if (tiles * s >= kFillTarget) return {kind, s};
@@ -730,8 +745,10 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
 #undef NS_GEMV_PART
   } else {
     int kind = partial_plan(M, N, K).kind;
-    if (kind == TILE_BIG && !big_fits(M, lda, N, ldb)) kind = TILE_128;
+    if ((kind == TILE_BIG || kind == TILE_BIG128) && !big_fits(M, lda, N, ldb)) kind = TILE_128;
     if (kind == TILE_BIG) run_big<EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+    else if (kind == TILE_BIG128)
+      run_big<EPI_PARTIAL, 128>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
     else if (kind == TILE_128)
       run_bf16<128, 128, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
     else run_bf16<64, 64, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
@@ -762,18 +779,19 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
   if (M <= 32) return dispatch_gemv_m<2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   // M > 64: the tile shape with the best estimated throughput -- its
-  // relative per-CU rate (measured on MI355X at 2048 rows: the 256 x 256
-  // kernel 1.0, 128 x 128 about 0.55, 64 x 64 about 0.35) times the fill of
-  // its last wave of workgroups (256 resident at a time for the big kernel,
-  // 512 and 1024 for the LDS-light ones).  The big kernel needs more than
-  // 128 rows and 32-bit offsets.
+  // relative per-CU rate (measured on MI355X: the 256 x 256 kernel 1.0,
+  // 128 x 256 about 0.9, 128 x 128 about 0.55, 64 x 64 about 0.35) times the
+  // fill of its last wave of workgroups (256 resident at a time for the big
+  // kernel, 512 and 1024 for the LDS-light ones).  The big kernel needs
+  // 32-bit offsets, and 256-row tiles more than 128 rows.
   const bool k64 = (K % 64) == 0;
   const long b_rows = (EPI == EPI_SILU_MUL) ? 2L * N : (long)N;
-  constexpr double kRate[3] = {1.0, 0.55, 0.35};
-  constexpr long kSlots[3] = {256, 512, 1024};
+  constexpr double kRate[4] = {1.0, 0.9, 0.55, 0.35};
+  constexpr long kSlots[4] = {256, 256, 512, 1024};
+  const bool fits = big_fits(M, lda, b_rows, ldb);
   int kind = TILE_64;
   double best = -1.0;
-  for (int k = (M > 128 && big_fits(M, lda, b_rows, ldb) ? TILE_BIG : TILE_128); k <= TILE_64; ++k) {
+  for (int k = (fits ? (M > 128 ? TILE_BIG : TILE_BIG128) : TILE_128); k <= TILE_64; ++k) {
     const long t = tile_count(k, M, N, EPI == EPI_SILU_MUL);
     const double fill = (double)t / (double)(kSlots[k] * ((t + kSlots[k] - 1) / kSlots[k]));
     if (kRate[k] * fill > best + 1e-9) {
@@ -782,6 +800,7 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
     }
   }
   if (kind == TILE_BIG) return run_big<EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+  if (kind == TILE_BIG128) return run_big<EPI, 128>(M, N, K, A, lda, B, ldb, C, ldc, st);
   if (kind == TILE_128) {
     if (k64) run_bf16<128, 128, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
     else run_bf16<128, 128, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
