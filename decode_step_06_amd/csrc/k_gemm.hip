@@ -780,13 +780,13 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
   if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
   // M > 64: the tile shape with the best estimated throughput -- its
   // relative per-CU rate (measured on MI355X: the 256 x 256 kernel 1.0,
-  // 128 x 256 about 0.9, 128 x 128 about 0.55, 64 x 64 about 0.35) times the
+  // 128 x 256 about 0.72, 128 x 128 about 0.55, 64 x 64 about 0.35) times the
   // fill of its last wave of workgroups (256 resident at a time for the big
   // kernel, 512 and 1024 for the LDS-light ones).  The big kernel needs
   // 32-bit offsets, and 256-row tiles more than 128 rows.
   const bool k64 = (K % 64) == 0;
   const long b_rows = (EPI == EPI_SILU_MUL) ? 2L * N : (long)N;
-  constexpr double kRate[4] = {1.0, 0.9, 0.55, 0.35};
+  constexpr double kRate[4] = {1.0, 0.72, 0.55, 0.35};
   constexpr long kSlots[4] = {256, 256, 512, 1024};
   const bool fits = big_fits(M, lda, b_rows, ldb);
   int kind = TILE_64;
