@@ -132,6 +132,47 @@ def run_step_bench(h, b, steps, warmup, warm_seconds, stream):
     return runs, eager, launches
 
 
+# ---------------------------------------------------------------- greedy decoding
+def greedy_loop(h, b, stream, steps=100):
+    """Greedy decoding at the headline batch: the device argmax alone, and a
+    loop of steps whose tokens come from the previous step's argmax, either
+    on the device (graph replay + ns_sample_greedy, token ids fed back
+    through token_ids_dev: no host round trip) or through the host (replay,
+    copy the logits back, argmax in numpy, upload the tokens)."""
+    V, T = h.shape.vocab, b.n_rows
+    out = torch.empty((T, V), device="cuda")
+    tok_dev = torch.zeros((T,), dtype=torch.int32, device="cuda")
+    res = {"argmax_us": time_launches(lambda i: ns.ns_sample_greedy(out.data_ptr(), T, V, tok_dev.data_ptr(), stream),
+                                      50, stream) * 1e6}
+    g = ns.ns_graph_capture(h.eng, T, out.data_ptr(), stream)
+    try:
+        first = ns.Batch(b.row_seq, b.row_pos, b.tokens)
+        fed = ns.Batch(b.row_seq, b.row_pos, tokens_dev=tok_dev)
+        ns.ns_graph_replay(g, first, stream)
+        ns.ns_sample_greedy(out.data_ptr(), T, V, tok_dev.data_ptr(), stream)
+        stream.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ns.ns_graph_replay(g, fed, stream)
+            ns.ns_sample_greedy(out.data_ptr(), T, V, tok_dev.data_ptr(), stream)
+        stream.synchronize()
+        res["device_feedback_ms_per_step"] = (time.perf_counter() - t0) / steps * 1e3
+        host = np.empty((T, V), dtype=np.float32)
+        tok = b.tokens
+        t0 = time.perf_counter()
+        n_host = max(10, steps // 4)
+        for _ in range(n_host):
+            ns.ns_graph_replay(g, ns.Batch(b.row_seq, b.row_pos, tok), stream)
+            stream.synchronize()
+            host[:] = out.cpu().numpy()
+            tok = np.argmax(host, axis=1).astype(np.int32)
+        res["host_feedback_ms_per_step"] = (time.perf_counter() - t0) / n_host * 1e3
+    finally:
+        ns.ns_graph_destroy(g)
+    res["device_feedback_tokens_per_s"] = T / (res["device_feedback_ms_per_step"] * 1e-3)
+    return res
+
+
 # ---------------------------------------------------------------- kernels of the step
 def step_kernels(h, b, stream, reps=5):
     """Per-kernel device time inside the real step: an eager serial step with
@@ -469,6 +510,7 @@ def main():
             nano_ms = _graph_rate(h, b, stream, args.steps, 1.0,
                                   ns.make_sched(nano_rows=w.nano_splits, overlap=True)) * 1e3
             ns.ns_engine_set_sched(h.eng, ns.make_sched())
+        greedy = greedy_loop(h, b, stream)
         # last, so that a kernel trace of this run ends with these launches
         att = attention_isolated(h, b, maxb, stream)
         if not args.no_sweep:
@@ -518,6 +560,7 @@ def main():
                  "step_hbm_frac": round(sb / step_s / 1e9 / rf.HBM_PEAK_GBS, 4)},
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
+        "greedy_decoding": {k: round(v, 4) for k, v in greedy.items()},
     }
     if not args.no_dense:
         try:

@@ -231,7 +231,8 @@ int check_batch(const ns_engine* e, const ns_batch* b, int max_rows) {
   if (b->n_tok <= 0) NS_FAIL(NS_EINVAL, "batch must have at least one row");
   if (b->n_tok > max_rows) NS_FAIL(NS_ESHAPE, "batch of %d rows exceeds %d", b->n_tok, max_rows);
   if (!b->seq || !b->pos) NS_FAIL(NS_EINVAL, "null seq/pos arrays");
-  if (e->d.vocab > 0 && !b->token_ids) NS_FAIL(NS_EINVAL, "model has a vocabulary: token_ids required");
+  if (e->d.vocab > 0 && !b->token_ids && !b->token_ids_dev)
+    NS_FAIL(NS_EINVAL, "model has a vocabulary: token_ids or token_ids_dev required");
   if (e->d.vocab == 0 && !b->hidden_in) NS_FAIL(NS_EINVAL, "model has no vocabulary: hidden_in required");
   const ns_kv* kv = e->kv;
   std::vector<int32_t> last_pos(kv->max_seqs, -1);
@@ -245,7 +246,7 @@ int check_batch(const ns_engine* e, const ns_batch* b, int max_rows) {
       NS_FAIL(NS_ESHAPE, "sequence %d holds more blocks than the engine's table rows", s);
     if (p <= last_pos[s]) NS_FAIL(NS_EINVAL, "rows of sequence %d must have increasing positions", s);
     last_pos[s] = p;
-    if (e->d.vocab > 0 && (b->token_ids[i] < 0 || b->token_ids[i] >= e->d.vocab))
+    if (e->d.vocab > 0 && !b->token_ids_dev && (b->token_ids[i] < 0 || b->token_ids[i] >= e->d.vocab))
       NS_FAIL(NS_EINVAL, "row %d: token id %d out of range", i, b->token_ids[i]);
   }
   return NS_OK;
@@ -268,7 +269,7 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
   // without first looking up the row's sequence)
   for (int i = 0; i < rows; ++i) {
     const bool real = i < b->n_tok && b->seq[i] != -1;
-    tok[i] = (i < b->n_tok && b->token_ids) ? b->token_ids[i] : 0;
+    tok[i] = (i < b->n_tok && b->token_ids && !b->token_ids_dev) ? b->token_ids[i] : 0;
     pos[i] = real ? b->pos[i] : 0;
     int32_t* row = btab + (size_t)i * e->maxb;
     if (!real) {
@@ -289,6 +290,10 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
   HIP_TRY(hipMemcpyAsync(e->meta(), m, bytes, hipMemcpyHostToDevice, st));
   HIP_TRY(hipEventRecord(e->staging_ev[k], st));
   e->staging_used[k] = true;
+  // device-resident token ids (on-device feedback) overwrite the token slots
+  if (e->d.vocab > 0 && b->token_ids_dev)
+    HIP_TRY(hipMemcpyAsync(e->meta(), b->token_ids_dev, (size_t)b->n_tok * sizeof(int32_t), hipMemcpyDeviceToDevice,
+                           st));
   return NS_OK;
 }
 
@@ -668,6 +673,14 @@ int ns_graph_replay(ns_graph* g, const ns_batch* b, void* stream) {
   if (e->d.vocab == 0)
     HIP_TRY(hipMemcpyAsync(e->x(), b->hidden_in, (size_t)b->n_tok * e->d.hidden * 4, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipGraphLaunch(g->exec, st));
+  return NS_OK;
+}
+
+int ns_sample_greedy(const float* logits, int32_t n_rows, int32_t vocab, int32_t* tokens_out, void* stream) {
+  if (!logits || !tokens_out) NS_FAIL(NS_EINVAL, "null argument");
+  if (n_rows < 1 || vocab < 1) NS_FAIL(NS_EINVAL, "n_rows and vocab must be positive");
+  ns::launch_argmax_rows(logits, n_rows, vocab, tokens_out, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
   return NS_OK;
 }
 

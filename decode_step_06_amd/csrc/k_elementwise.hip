@@ -5,6 +5,8 @@
 // (section "Four resource classes, one serialized queue"): each moves a few
 // bytes per row, so the design goal is one launch per use and coalesced
 // row access, not arithmetic throughput.
+#include <climits>
+
 #include "ns_kernels.h"
 
 namespace ns {
@@ -203,6 +205,56 @@ __global__ void __launch_bounds__(256) step_prologue_kernel(const T* __restrict_
   const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
   T* hr = h + (long)t * H;
   for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(hr, i, xr[i] * r * Elem<T>::load(g0, i));
+}
+
+// ---------------------------------------------------------------- greedy sampling
+// Row argmax (lowest index among equal maxima; NaN never wins).  One
+// workgroup of 1024 threads per row; each thread keeps its best (value,
+// index) over a strided quarter of the row, four independent loads at a
+// time, then the pairs meet in wavefront shuffles and LDS.
+__device__ __forceinline__ bool argmax_better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ void __launch_bounds__(1024) argmax_rows_kernel(const float* __restrict__ logits, int V,
+                                                           int32_t* __restrict__ out) {
+  const float* row = logits + (long)blockIdx.x * V;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  int i = threadIdx.x;
+  for (; i + 3 * 1024 < V; i += 4 * 1024) {
+    const float v0 = row[i], v1 = row[i + 1024], v2 = row[i + 2048], v3 = row[i + 3072];
+    if (argmax_better(v0, i, bv, bi)) bv = v0, bi = i;
+    if (argmax_better(v1, i + 1024, bv, bi)) bv = v1, bi = i + 1024;
+    if (argmax_better(v2, i + 2048, bv, bi)) bv = v2, bi = i + 2048;
+    if (argmax_better(v3, i + 3072, bv, bi)) bv = v3, bi = i + 3072;
+  }
+  for (; i < V; i += 1024)
+    if (argmax_better(row[i], i, bv, bi)) bv = row[i], bi = i;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(bv, off, 64);
+    const int oi = __shfl_xor(bi, off, 64);
+    if (argmax_better(ov, oi, bv, bi)) bv = ov, bi = oi;
+  }
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[w] = bv;
+    si[w] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 16; ++k)
+      if (argmax_better(sv[k], si[k], bv, bi)) bv = sv[k], bi = si[k];
+    out[blockIdx.x] = bi == INT_MAX ? 0 : bi;
+  }
+}
+
+void launch_argmax_rows(const float* logits, int n_rows, int V, int32_t* out, hipStream_t st) {
+  if (n_rows <= 0) return;
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3(n_rows), dim3(1024), 0, st, logits, V, out);
 }
 
 // ---------------------------------------------------------------- RoPE + KV write

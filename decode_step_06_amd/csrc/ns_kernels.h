@@ -38,6 +38,9 @@ void launch_embed(int dtype, const void* E, const int32_t* tok, float* x, int T,
 void launch_copy_rows(const float* src, float* dst, long n, hipStream_t st);
 void launch_rope_table(const int32_t* pos, float* cosb, float* sinb, int T, int d, float base, hipStream_t st);
 void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st);
+// tokens out[r] = argmax of row r of fp32 logits [n_rows, V] (lowest index
+// among equal maxima, NaN never wins, a row of NaN only gives 0)
+void launch_argmax_rows(const float* logits, int n_rows, int V, int32_t* out, hipStream_t st);
 // x[t] += sum_s P[s][t] (slice order; the split-K residual add of the
 // previous projection), written back to x, then RMSNorm into h.
 void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_stride, int splits, const void* g,

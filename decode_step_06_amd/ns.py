@@ -52,7 +52,7 @@ class ns_sched(C.Structure):
 
 class ns_batch(C.Structure):
     _fields_ = [("n_tok", C.c_int32), ("token_ids", C.POINTER(C.c_int32)), ("hidden_in", C.c_void_p),
-                ("seq", C.POINTER(C.c_int32)), ("pos", C.POINTER(C.c_int32))]
+                ("seq", C.POINTER(C.c_int32)), ("pos", C.POINTER(C.c_int32)), ("token_ids_dev", C.c_void_p)]
 
 
 _P = C.c_void_p
@@ -79,6 +79,7 @@ SIGNATURES = {
     "ns_graph_capture": (C.c_int, [_P, _I, _P, _P, C.POINTER(_P)]),
     "ns_graph_replay": (C.c_int, [_P, C.POINTER(ns_batch), _P]),
     "ns_graph_destroy": (None, [_P]),
+    "ns_sample_greedy": (C.c_int, [_P, _I, _I, _P, _P]),
     "ns_kv_scatter": (C.c_int, [_P, _I, _I, _P, _P, _P, _P]),
     "ns_kv_gather": (C.c_int, [_P, _I, _I, _P, _P, _P, _P]),
     "ns_engine_last_launches": (C.c_int, [_P, _PI]),
@@ -210,13 +211,15 @@ def _stream_ptr(stream) -> Optional[int]:
 class Batch:
     """Host arrays of one step kept alive for the duration of a call."""
 
-    def __init__(self, seq, pos, tokens=None, hidden_in=None):
+    def __init__(self, seq, pos, tokens=None, hidden_in=None, tokens_dev=None):
         self.seq = _i32(seq)
         self.pos = _i32(pos)
         self.tokens = None if tokens is None else _i32(tokens)
         self.hidden_in = hidden_in  # device tensor (fp32 [n, H]) or None
+        self.tokens_dev = tokens_dev  # device int32 tensor [n] (on-device token feedback) or None
         self.c = ns_batch(self.seq.shape[0], None if self.tokens is None else _ptr(self.tokens),
-                          None if hidden_in is None else hidden_in.data_ptr(), _ptr(self.seq), _ptr(self.pos))
+                          None if hidden_in is None else hidden_in.data_ptr(), _ptr(self.seq), _ptr(self.pos),
+                          None if tokens_dev is None else tokens_dev.data_ptr())
 
 
 def ns_engine_create(desc, weights: ns_weights, kv, kv_dev: int, kv_bytes: int, ws_dev: int, ws_bytes: int,
@@ -237,6 +240,10 @@ def ns_engine_set_sched(eng, sched: ns_sched) -> None:
 
 def ns_decode_step(eng, batch: Batch, out_dev: int, stream=None) -> None:
     _check(lib().ns_decode_step(eng, C.byref(batch.c), out_dev, _stream_ptr(stream)))
+
+
+def ns_sample_greedy(logits_dev: int, n_rows: int, vocab: int, tokens_dev: int, stream=None) -> None:
+    _check(lib().ns_sample_greedy(logits_dev, n_rows, vocab, tokens_dev, _stream_ptr(stream)))
 
 
 def ns_graph_capture(eng, bucket: int, out_dev: int, stream) -> C.c_void_p:

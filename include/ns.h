@@ -186,13 +186,23 @@ typedef struct {
  * each row, -1 for a padding row; pos (host) its position.  A decode row has
  * pos = context length - 1; the row's own K/V are written to the cache
  * before attention, so attention covers positions 0..pos.  Rows of one
- * sequence must be in increasing position order. */
+ * sequence must be in increasing position order.
+ *
+ * token_ids_dev (device int32 [n_tok], may be NULL): when set, the step takes
+ * its token ids from this device buffer instead of token_ids, so the tokens
+ * a previous step sampled on the device (ns_sample_greedy) feed the next
+ * step with no host round trip, and the host can form step i+1's rows while
+ * step i still runs (NanoFlow review, "Runtime details that keep the
+ * pipeline fed").  The ids are copied on the step's stream after the
+ * metadata; the host cannot check them, so an id outside [0, vocab) gathers
+ * the nearest valid embedding row. */
 typedef struct {
   int32_t n_tok;
   const int32_t* token_ids;
   const void* hidden_in;
   const int32_t* seq;
   const int32_t* pos;
+  const int32_t* token_ids_dev;
 } ns_batch;
 
 typedef struct ns_engine ns_engine;
@@ -238,6 +248,18 @@ int ns_graph_capture(ns_engine* eng, int32_t bucket, void* out_dev, void* stream
 int ns_graph_replay(ns_graph* g, const ns_batch* batch, void* stream);
 
 void ns_graph_destroy(ns_graph* g);
+
+/* Greedy sampling on the device: the argmax of each row of the step's
+ * logits, one of the per-step pieces of fixed cost the roofline page lists
+ * beside the kernels ("The roofline flips", section "The point of the title:
+ * why it flips in SLMs": the argmax and the copy of the token back).
+ * logits: device fp32 [n_rows, vocab], row-major.  tokens_out: device int32
+ * [n_rows]; tokens_out[r] is the lowest index v with logits[r][v] equal to
+ * the row's maximum over its non-NaN entries (NaN never wins; a row of NaN
+ * only gives 0).  Enqueued on `stream`; nothing is synchronised or copied
+ * to the host.  Errors: NS_EINVAL (null pointer, n_rows or vocab < 1),
+ * NS_EHIP. */
+int ns_sample_greedy(const float* logits, int32_t n_rows, int32_t vocab, int32_t* tokens_out, void* stream);
 
 /* ------------------------------------------------------------ helpers */
 

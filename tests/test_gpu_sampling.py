@@ -1,0 +1,107 @@
+"""Greedy sampling on the device and on-device token feedback, through the
+C ABI: the argmax kernel against the oracle's definition (bit-exact, with
+ties, NaN and infinities planted), and greedy decoding where each step's
+tokens come from the previous step's device argmax (graph replays, no host
+round trip) against the same decoding driven from the host."""
+import numpy as np
+import pytest
+import torch
+
+from decode_step_06_amd import ns
+from decode_step_06_amd.inputs import gen_weights
+from decode_step_06_amd.runner import DeviceWeights, alloc_sequences, blocks_for, create_engine, \
+    fill_past_random_on_device
+from gpu_helpers import say
+from oracle.sampling import greedy_tokens
+from decode_step_06_amd.configs import ModelShape
+
+SMALL = ModelShape("small", 2, 256, 8, 2, 64, 512, 1000, True, "bf16")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n,v", [(1, 7), (5, 4097), (3, 151936), (32, 32000), (256, 1000), (2, 4096)])
+def test_argmax_matches_oracle(n, v):
+    say(f"greedy argmax n={n} vocab={v}")
+    rng = np.random.default_rng(n * 131 + v)
+    x = rng.standard_normal((n, v)).astype(np.float32)
+    # few distinct values in some rows so the maximum repeats
+    x[::2] = np.round(x[::2] * 2) / 2
+    x[rng.random((n, v)) < 0.01] = np.nan
+    if v > 10:
+        x[0, v // 3] = np.inf
+        x[0, v - 1] = np.inf
+    if n > 1:
+        x[1, :] = np.nan               # no valid entry: token 0
+    if n > 2:
+        x[2, :] = -np.inf
+        x[2, v // 2] = np.nan           # -inf is a valid value, lowest index wins
+    xd = torch.from_numpy(x).cuda()
+    tok = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    ns.ns_sample_greedy(xd.data_ptr(), n, v, tok.data_ptr())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(tok.cpu().numpy(), greedy_tokens(x))
+
+
+def test_argmax_rejects_bad_arguments():
+    with pytest.raises(ns.NSError):
+        ns.ns_sample_greedy(0, 1, 10, 0)
+    x = torch.zeros((2, 3), device="cuda")
+    t = torch.zeros((2,), dtype=torch.int32, device="cuda")
+    with pytest.raises(ns.NSError):
+        ns.ns_sample_greedy(x.data_ptr(), 0, 3, t.data_ptr())
+    with pytest.raises(ns.NSError):
+        ns.ns_sample_greedy(x.data_ptr(), 2, 0, t.data_ptr())
+
+
+def test_device_token_feedback_matches_host_driven_decoding():
+    shape = SMALL
+    B, S = 6, 5
+    rng = np.random.default_rng(5)
+    ctx = rng.integers(5, 60, size=B)
+    say(f"greedy decoding, {S} steps of {B} sequences, contexts {ctx.tolist()}")
+    weights = gen_weights(shape, seed=0)
+    dw = DeviceWeights.from_numpy(shape, weights)
+    lens = ctx + S
+    maxb = blocks_for(lens)
+    nblk = int(sum(-(-int(n) // 16) for n in lens)) + 3
+    h = create_engine(shape, dw, nblk, B, maxb, B, None, None)
+    stream = torch.cuda.Stream()
+    try:
+        alloc_sequences(h, lens)
+        past_seq = np.concatenate([np.full(c - 1, s, np.int32) for s, c in enumerate(ctx)])
+        past_pos = np.concatenate([np.arange(c - 1, dtype=np.int32) for c in ctx])
+        fill_past_random_on_device(h, past_seq, past_pos, seed=4)
+        seq = np.arange(B, dtype=np.int32)
+        tok0 = rng.integers(0, shape.vocab, size=B).astype(np.int32)
+
+        # host-driven: eager steps, logits to the host, argmax there
+        host_tok, host_logits = [], []
+        tok = tok0
+        for k in range(S):
+            out = torch.full((B, shape.vocab), float("nan"), device="cuda")
+            ns.ns_decode_step(h.eng, ns.Batch(seq, ctx - 1 + k, tok), out.data_ptr(), stream)
+            stream.synchronize()
+            lg = out.cpu().numpy()
+            tok = greedy_tokens(lg)
+            host_logits.append(lg)
+            host_tok.append(tok)
+
+        # device-driven: graph replays fed by the device argmax
+        out = torch.full((B, shape.vocab), float("nan"), device="cuda")
+        tok_dev = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+        g = ns.ns_graph_capture(h.eng, B, out.data_ptr(), stream)
+        try:
+            for k in range(S):
+                nb = ns.Batch(seq, ctx - 1 + k, tok0) if k == 0 else ns.Batch(seq, ctx - 1 + k, tokens_dev=tok_dev)
+                ns.ns_graph_replay(g, nb, stream)
+                ns.ns_sample_greedy(out.data_ptr(), B, shape.vocab, tok_dev.data_ptr(), stream)
+                stream.synchronize()
+                np.testing.assert_array_equal(out.cpu().numpy(), host_logits[k], err_msg=f"step {k} logits")
+                np.testing.assert_array_equal(tok_dev.cpu().numpy(), host_tok[k], err_msg=f"step {k} tokens")
+        finally:
+            ns.ns_graph_destroy(g)
+        say(f"  tokens per step: {[t.tolist() for t in host_tok]}")
+    finally:
+        h.destroy()
+        torch.cuda.synchronize()
