@@ -406,6 +406,59 @@ def batch_sweep(stream, dw, steps=100, warm_seconds=1.0):
     return res
 
 
+BUCKETS = (1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 192, 256)
+
+
+def bucket_capture(stream, dw, steps=50):
+    """Bucketed capture for the continuous-batching mix (Qwen2.5-0.5B-shaped,
+    24 layers, up to 256 rows): capture time and device memory of one graph
+    per bucket, and what padding costs -- a batch replayed on the next
+    bucket up against a graph captured for its exact size."""
+    w = WORKLOADS["qwen05b_mix_b256"]
+    b = gen_batch(w, with_past=False)
+    maxb = blocks_for(b.seq_lens)
+    log("[bench] bucketed capture")
+    h = create_engine(w.model, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, None, nan_poison=False)
+    res = {"buckets": list(BUCKETS)}
+    try:
+        alloc_sequences(h, b.seq_lens)
+        fill_past_random_on_device(h, b.past_seq, b.past_pos, seed=w.seeds["kv"])
+        out = torch.empty((b.n_rows, w.model.vocab), device="cuda")
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        t0 = time.perf_counter()
+        gs = ns.ns_graph_set_capture(h.eng, BUCKETS, out.data_ptr(), stream)
+        torch.cuda.synchronize()
+        res["capture_ms_total"] = (time.perf_counter() - t0) * 1e3
+        res["capture_ms_per_graph"] = res["capture_ms_total"] / len(BUCKETS)
+        try:
+            # graph memory is committed at the first launch: replay each once
+            for bk in BUCKETS:
+                nb = ns.Batch(b.row_seq[:bk], b.row_pos[:bk], b.tokens[:bk])
+                ns.ns_graph_set_replay(gs, nb, stream)
+            torch.cuda.synchronize()
+            res["device_mem_mb"] = (free0 - torch.cuda.mem_get_info()[0]) / 2 ** 20
+            pad = {}
+            for n in (33, 100, 200):
+                nb = ns.Batch(b.row_seq[:n], b.row_pos[:n], b.tokens[:n])
+                used = ns.ns_graph_set_replay(gs, nb, stream)
+                t_pad = time_launches(lambda i: ns.ns_graph_set_replay(gs, nb, stream), steps, stream)
+                g = ns.ns_graph_capture(h.eng, n, out.data_ptr(), stream)
+                try:
+                    t_exact = time_launches(lambda i: ns.ns_graph_replay(g, nb, stream), steps, stream)
+                finally:
+                    ns.ns_graph_destroy(g)
+                pad[str(n)] = {"bucket": used, "padded_ms": t_pad * 1e3, "exact_ms": t_exact * 1e3,
+                               "padding_overhead": t_pad / t_exact - 1.0}
+            res["padding"] = pad
+        finally:
+            ns.ns_graph_set_destroy(gs)
+    finally:
+        h.destroy()
+        torch.cuda.synchronize()
+    return res
+
+
 # ---------------------------------------------------------------- 80-layer 70B
 def llama80(stream, steps=10, warm_seconds=2.0):
     """LLaMA-2-70B-shaped 80-layer step, 256 sequences at contexts uniform in
@@ -499,7 +552,7 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
     w, weights, b, h, maxb = setup_step(WORKLOAD)
-    sweep = None
+    sweep = buckets = None
     try:
         runs, eager, launches = run_step_bench(h, b, args.steps, args.warmup, args.warm_seconds, stream)
         kern = step_kernels(h, b, stream)
@@ -518,6 +571,10 @@ def main():
                 sweep = json.loads(json.dumps(batch_sweep(stream, h.weights), default=_jsonable))
             except Exception as e:  # report, do not hide
                 sweep = {"error": repr(e)}
+            try:
+                buckets = json.loads(json.dumps(bucket_capture(stream, h.weights), default=_jsonable))
+            except Exception as e:  # report, do not hide
+                buckets = {"error": repr(e)}
     finally:
         h.destroy()
     step_s = runs[-1]
@@ -569,6 +626,8 @@ def main():
             result["dense_batch"] = {"error": repr(e)}
     if sweep is not None:
         result["batch_sweep"] = sweep
+    if buckets is not None:
+        result["bucketed_capture"] = buckets
     if not args.no_llama80:
         try:
             result["llama70b_80l_b256"] = json.loads(json.dumps(llama80(stream), default=_jsonable))

@@ -214,6 +214,10 @@ struct ns_graph {
   hipGraphExec_t exec = nullptr;
 };
 
+struct ns_graph_set {
+  std::vector<ns_graph*> graphs;  // increasing buckets
+};
+
 namespace {
 
 int check_sched(const ns_sched* s) {
@@ -674,6 +678,47 @@ int ns_graph_replay(ns_graph* g, const ns_batch* b, void* stream) {
     HIP_TRY(hipMemcpyAsync(e->x(), b->hidden_in, (size_t)b->n_tok * e->d.hidden * 4, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipGraphLaunch(g->exec, st));
   return NS_OK;
+}
+
+int ns_graph_set_capture(ns_engine* e, const int32_t* buckets, int32_t n, void* out, void* stream,
+                         ns_graph_set** sout) {
+  if (!e || !buckets || !out || !sout) NS_FAIL(NS_EINVAL, "null argument");
+  if (n < 1 || n > 64) NS_FAIL(NS_EINVAL, "bucket count %d outside 1..64", n);
+  for (int i = 0; i < n; ++i) {
+    if (buckets[i] < 1 || buckets[i] > e->max_tokens)
+      NS_FAIL(NS_EINVAL, "bucket %d outside 1..max_tokens (%d)", buckets[i], e->max_tokens);
+    if (i > 0 && buckets[i] <= buckets[i - 1]) NS_FAIL(NS_EINVAL, "buckets must be strictly increasing");
+  }
+  ns_graph_set* set = new ns_graph_set;
+  for (int i = 0; i < n; ++i) {
+    ns_graph* g = nullptr;
+    const int rc = ns_graph_capture(e, buckets[i], out, stream, &g);
+    if (rc != NS_OK) {
+      ns_graph_set_destroy(set);
+      return rc;
+    }
+    set->graphs.push_back(g);
+  }
+  *sout = set;
+  return NS_OK;
+}
+
+int ns_graph_set_replay(ns_graph_set* set, const ns_batch* b, void* stream, int32_t* bucket_used) {
+  if (!set || !b) NS_FAIL(NS_EINVAL, "null argument");
+  if (b->n_tok <= 0) NS_FAIL(NS_EINVAL, "batch must have at least one row");
+  for (ns_graph* g : set->graphs) {
+    if (g->bucket < b->n_tok) continue;
+    const int rc = ns_graph_replay(g, b, stream);
+    if (rc == NS_OK && bucket_used) *bucket_used = g->bucket;
+    return rc;
+  }
+  NS_FAIL(NS_ESHAPE, "batch of %d rows exceeds the largest bucket %d", b->n_tok, set->graphs.back()->bucket);
+}
+
+void ns_graph_set_destroy(ns_graph_set* set) {
+  if (!set) return;
+  for (ns_graph* g : set->graphs) ns_graph_destroy(g);
+  delete set;
 }
 
 int ns_sample_greedy(const float* logits, int32_t n_rows, int32_t vocab, int32_t* tokens_out, void* stream) {

@@ -80,6 +80,9 @@ SIGNATURES = {
     "ns_graph_replay": (C.c_int, [_P, C.POINTER(ns_batch), _P]),
     "ns_graph_destroy": (None, [_P]),
     "ns_sample_greedy": (C.c_int, [_P, _I, _I, _P, _P]),
+    "ns_graph_set_capture": (C.c_int, [_P, _PI, _I, _P, _P, C.POINTER(_P)]),
+    "ns_graph_set_replay": (C.c_int, [_P, C.POINTER(ns_batch), _P, _PI]),
+    "ns_graph_set_destroy": (None, [_P]),
     "ns_kv_scatter": (C.c_int, [_P, _I, _I, _P, _P, _P, _P]),
     "ns_kv_gather": (C.c_int, [_P, _I, _I, _P, _P, _P, _P]),
     "ns_engine_last_launches": (C.c_int, [_P, _PI]),
@@ -240,6 +243,23 @@ def ns_engine_set_sched(eng, sched: ns_sched) -> None:
 
 def ns_decode_step(eng, batch: Batch, out_dev: int, stream=None) -> None:
     _check(lib().ns_decode_step(eng, C.byref(batch.c), out_dev, _stream_ptr(stream)))
+
+
+def ns_graph_set_capture(eng, buckets, out_dev: int, stream) -> C.c_void_p:
+    b = _i32(buckets)
+    gs = C.c_void_p()
+    _check(lib().ns_graph_set_capture(eng, _ptr(b), len(b), out_dev, _stream_ptr(stream), C.byref(gs)))
+    return gs
+
+
+def ns_graph_set_replay(gs, batch: Batch, stream) -> int:
+    used = C.c_int32(0)
+    _check(lib().ns_graph_set_replay(gs, C.byref(batch.c), _stream_ptr(stream), C.byref(used)))
+    return used.value
+
+
+def ns_graph_set_destroy(gs) -> None:
+    lib().ns_graph_set_destroy(gs)
 
 
 def ns_sample_greedy(logits_dev: int, n_rows: int, vocab: int, tokens_dev: int, stream=None) -> None:

@@ -249,6 +249,23 @@ int ns_graph_replay(ns_graph* g, const ns_batch* batch, void* stream);
 
 void ns_graph_destroy(ns_graph* g);
 
+/* Bucketed capture ("The chef who calls out every order", CUDA graphs
+ * section and "Knob 3 — Capture buckets": one graph per batch-size bucket,
+ * the real batch padded up to the next bucket and the output trimmed).
+ * ns_graph_set_capture captures one graph per entry of `buckets` (strictly
+ * increasing, each in [1, max_tokens], at most 64 entries), all writing
+ * out_dev.  ns_graph_set_replay replays the smallest bucket >= batch->n_tok:
+ * rows n_tok..bucket-1 are padding, so only the first n_tok output rows are
+ * meaningful; *bucket_used (may be NULL) receives the bucket.  Errors:
+ * NS_EINVAL (bad bucket list, null argument), NS_ESHAPE (n_tok above the
+ * largest bucket), and those of ns_graph_capture / ns_graph_replay; a failed
+ * capture releases the graphs already captured. */
+typedef struct ns_graph_set ns_graph_set;
+int ns_graph_set_capture(ns_engine* eng, const int32_t* buckets, int32_t n_buckets, void* out_dev,
+                         void* stream, ns_graph_set** out);
+int ns_graph_set_replay(ns_graph_set* set, const ns_batch* batch, void* stream, int32_t* bucket_used);
+void ns_graph_set_destroy(ns_graph_set* set);
+
 /* Greedy sampling on the device: the argmax of each row of the step's
  * logits, one of the per-step pieces of fixed cost the roofline page lists
  * beside the kernels ("The roofline flips", section "The point of the title:

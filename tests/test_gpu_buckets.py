@@ -1,0 +1,83 @@
+"""Bucketed graph capture through the C ABI: one graph per batch-size
+bucket, a batch replayed on the smallest bucket that holds it with the rest
+as padding rows.  The real rows equal an eager step of the same padded batch
+bit for bit, and the oracle within the bf16 bound."""
+import numpy as np
+import pytest
+import torch
+
+from decode_step_06_amd import ns
+from decode_step_06_amd.configs import ModelShape
+from decode_step_06_amd.inputs import gen_weights
+from decode_step_06_amd.runner import DeviceWeights, alloc_sequences, blocks_for, create_engine, fill_past
+from decode_step_06_amd.inputs import Batch as InBatch
+from gpu_helpers import assert_close, oracle_run, say
+from oracle import decoder as od
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ModelShape("small", 2, 256, 8, 2, 64, 512, 1000, True, "bf16")
+BUCKETS = (1, 2, 4, 8, 16, 24)
+
+
+def test_bucketed_replay_pads_to_the_next_bucket():
+    shape, S = SMALL, 24
+    rng = np.random.default_rng(3)
+    ctx = rng.integers(1, 90, size=S)
+    tokens = rng.integers(0, shape.vocab, size=S).astype(np.int32)
+    weights = gen_weights(shape, seed=0)
+    maxb = blocks_for(ctx)
+    nblk = int(sum(-(-int(n) // 16) for n in ctx)) + 2
+    past_seq = np.concatenate([np.full(c - 1, s, np.int32) for s, c in enumerate(ctx)])
+    past_pos = np.concatenate([np.arange(c - 1, dtype=np.int32) for c in ctx])
+    n_past = len(past_seq)
+    prng = np.random.default_rng(4)
+    past_k = [od.round_bf16(prng.standard_normal((n_past, shape.n_kv_heads, shape.head_dim))).astype(np.float32)
+              for _ in range(shape.n_layers)]
+    past_v = [od.round_bf16(prng.standard_normal((n_past, shape.n_kv_heads, shape.head_dim))).astype(np.float32)
+              for _ in range(shape.n_layers)]
+    dw = DeviceWeights.from_numpy(shape, weights)
+    h = create_engine(shape, dw, nblk, S, maxb, S, None, None)
+    stream = torch.cuda.Stream()
+    try:
+        alloc_sequences(h, ctx)
+        fill_past(h, past_seq, past_pos, past_k, past_v)
+        out = torch.full((S, shape.vocab), float("nan"), device="cuda")
+        gs = ns.ns_graph_set_capture(h.eng, BUCKETS, out.data_ptr(), stream)
+        try:
+            for n in (1, 3, 5, 8, 13, 24):
+                seq = np.arange(n, dtype=np.int32)
+                pos = (ctx[:n] - 1).astype(np.int32)
+                used = ns.ns_graph_set_replay(gs, ns.Batch(seq, pos, tokens[:n]), stream)
+                stream.synchronize()
+                want_bucket = min(b for b in BUCKETS if b >= n)
+                assert used == want_bucket, (n, used)
+                got = out[:n].cpu().numpy()
+                # the same batch padded by hand, eager
+                pad = used - n
+                pseq = np.concatenate([seq, np.full(pad, -1, np.int32)])
+                ppos = np.concatenate([pos, np.zeros(pad, np.int32)])
+                ptok = np.concatenate([tokens[:n], np.zeros(pad, np.int32)])
+                ref = torch.full((used, shape.vocab), float("nan"), device="cuda")
+                ns.ns_decode_step(h.eng, ns.Batch(pseq, ppos, ptok), ref.data_ptr(), stream)
+                stream.synchronize()
+                np.testing.assert_array_equal(got, ref[:n].cpu().numpy(), err_msg=f"n_tok {n} bucket {used}")
+                say(f"  n_tok {n:2d} -> bucket {used:2d}: equal to the eager padded step")
+            # the largest case against the oracle
+            ib = InBatch(seq_lens=ctx.astype(np.int32), row_seq=np.arange(S, dtype=np.int32),
+                         row_pos=(ctx - 1).astype(np.int32), tokens=tokens, x=None, num_blocks=nblk,
+                         free_order=np.arange(nblk, dtype=np.int32), past_seq=past_seq, past_pos=past_pos,
+                         past_k=past_k, past_v=past_v)
+            ref, _, _ = oracle_run(shape, weights, ib, maxb)
+            assert_close(got, ref, "bf16", "bucketed replay vs oracle")
+            with pytest.raises(ns.NSError):
+                ns.ns_graph_set_replay(gs, ns.Batch(np.zeros(S + 1, np.int32), np.zeros(S + 1, np.int32),
+                                                    np.zeros(S + 1, np.int32)), stream)
+        finally:
+            ns.ns_graph_set_destroy(gs)
+        for bad in ((4, 2), (0, 1), (1, S + 1)):
+            with pytest.raises(ns.NSError):
+                ns.ns_graph_set_capture(h.eng, bad, out.data_ptr(), stream)
+    finally:
+        h.destroy()
+        torch.cuda.synchronize()
