@@ -794,6 +794,9 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
   for (int k = (fits ? (M > 128 ? TILE_BIG : TILE_BIG128) : TILE_128); k <= TILE_64; ++k) {
     const long t = tile_count(k, M, N, EPI == EPI_SILU_MUL);
     const double fill = (double)t / (double)(kSlots[k] * ((t + kSlots[k] - 1) / kSlots[k]));
+    // a big-tile launch that leaves most of the chip idle loses to smaller
+    // tiles spread over more CUs (measured: SwiGLU at 128-256 rows, K 896)
+    if (k <= TILE_BIG128 && 2 * t < kSlots[k]) continue;
     if (kRate[k] * fill > best + 1e-9) {
       best = kRate[k] * fill;
       kind = k;
