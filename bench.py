@@ -292,9 +292,10 @@ def dense_batch(stream, steps=10):
         x = torch.randn((T, H), device="cuda")
         out = torch.empty((T, H), device="cuda")
         nb = ns.Batch(b.row_seq, b.row_pos, None, x)
-        for label, sched in (("serial", ns.make_sched()),
-                             ("nano_overlap", ns.make_sched(nano_rows=w.nano_splits,
-                                                            qkv_rows=(512,) * w.qkv_splits, overlap=True))):
+        for label, sched in (("serial", ns.make_sched(prefill_tiles=True)),
+                             ("serial_decode_kernel_only", ns.make_sched()),
+                             ("nano_overlap", ns.make_sched(nano_rows=w.nano_splits, qkv_rows=(512,) * w.qkv_splits,
+                                                            overlap=True, prefill_tiles=True))):
             ns.ns_engine_set_sched(h.eng, sched)
             g = ns.ns_graph_capture(h.eng, T, out.data_ptr(), stream)
             try:

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libns.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["kv_host.cpp", "engine.cpp", "k_elementwise.hip", "k_attention.hip", "k_gemm.hip"]
+SOURCES = ["kv_host.cpp", "engine.cpp", "k_elementwise.hip", "k_attention.hip", "k_prefill.hip", "k_gemm.hip"]
 
 
 def hipcc() -> str:

@@ -197,6 +197,7 @@ struct ns_engine {
   // metadata block: tokens[T] | row index (-1: padding)[T] | pos[T] | slot[T] | btab[T][maxb] (one block-table
   // row per step row)
   int32_t* m_tok() const { return meta(); }
+  int32_t* m_seq() const { return meta() + max_tokens; }
   int32_t* m_pos() const { return meta() + 2 * max_tokens; }
   int32_t* m_slot() const { return meta() + 3 * max_tokens; }
   int32_t* m_btab() const { return meta() + 4 * max_tokens; }
@@ -226,6 +227,7 @@ int check_sched(const ns_sched* s) {
     NS_FAIL(NS_EINVAL, "at most %d nano-batches", kMaxParts);
   if (s->attn_wg_cap < 0) NS_FAIL(NS_EINVAL, "attn_wg_cap must be >= 0");
   if (s->cu_mask_frac < 0.f || s->cu_mask_frac > 1.f) NS_FAIL(NS_EINVAL, "cu_mask_frac must be in [0, 1]");
+  if (s->prefill_tiles != 0 && s->prefill_tiles != 1) NS_FAIL(NS_EINVAL, "prefill_tiles must be 0 or 1");
   return NS_OK;
 }
 
@@ -265,7 +267,7 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
   int32_t* m = e->staging[k];
   const int T = e->max_tokens;
   int32_t* tok = m;
-  int32_t* rowb = m + T;
+  int32_t* rowb = m + T;  // sequence of each row (-1: padding)
   int32_t* pos = m + 2 * T;
   int32_t* slot = m + 3 * T;
   int32_t* btab = m + 4 * T;
@@ -285,7 +287,7 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
     const int32_t s = b->seq[i];
     const auto& tab = e->kv->tables[s];
     for (int j = 0; j < e->maxb; ++j) row[j] = j < (int)tab.size() ? tab[j] : -1;
-    rowb[i] = i;
+    rowb[i] = s;
     const int32_t p = b->pos[i];
     slot[i] = tab[p / NS_BLOCK_SIZE] * NS_BLOCK_SIZE + p % NS_BLOCK_SIZE;
   }
@@ -321,6 +323,7 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
   attn_partition(n_tok, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, e->d.head_dim, (int)e->es, &a->part_tokens,
                  &a->n_parts, &a->waves);
   a->wg_cap = e->sched.attn_wg_cap;
+  a->row_seq = e->sched.prefill_tiles ? e->m_seq() : nullptr;
 }
 
 // The kernel sequence of one step over n_tok rows (metadata already on the
@@ -807,10 +810,11 @@ size_t ns_op_attention_ws_bytes(const ns_model_desc* desc, int32_t n_rows, int32
   return align_up(items * G * desc->head_dim * 4, 256) + align_up(items * G * 2 * 4, 256);
 }
 
-int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
-                    int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
-                    int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap,
-                    void* stream) {
+namespace {
+int op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                 int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
+                 int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap, void* stream,
+                 bool tiles) {
   int rc = ns::check_desc(desc);
   if (rc) return rc;
   if (n_rows <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || wg_cap < 0) NS_FAIL(NS_EINVAL, "bad sizes");
@@ -843,9 +847,27 @@ int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att
   a.part_acc = (float*)ws;
   a.part_ml = (float*)((char*)ws + align_up(items * G2 * desc->head_dim * 4, 256));
   a.wg_cap = wg_cap;
+  a.row_seq = tiles ? row_bseq : nullptr;  // row_bseq is the sequence of each row
   ns::launch_attention(a, (hipStream_t)stream);
   HIP_TRY(hipGetLastError());
   return NS_OK;
+}
+}  // namespace
+
+int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                    int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
+                    int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap,
+                    void* stream) {
+  return op_attention(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab, max_blocks_per_seq, out, ws,
+                      ws_bytes, wg_cap, stream, false);
+}
+
+int ns_op_attention_prefill(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                            int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos,
+                            const int32_t* btab, int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes,
+                            int32_t wg_cap, void* stream) {
+  return op_attention(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab, max_blocks_per_seq, out, ws,
+                      ws_bytes, wg_cap, stream, true);
 }
 
 }  // extern "C"

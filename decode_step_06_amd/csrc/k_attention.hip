@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_decode_kernel(
     const T* __restrict__ qatt, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ row_bseq, const int32_t* __restrict__ row_pos, const int32_t* __restrict__ btab,
     T* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml, int maxb, int row0, int n_rows,
-    int nq, int nkv, int P, int n_parts, float scale_log2) {
+    int nq, int nkv, int P, int n_parts, float scale_log2, const int32_t* __restrict__ skip_seq) {
   using Tr = AttnTraits<T, D, G>;
   constexpr int E = Tr::E, NCH = Tr::NCH, TL = Tr::TL;
   constexpr long HEAD_BLK = 16L * D;  // elements of one (block, KV head)
@@ -116,6 +116,10 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_decode_kernel(
     const int rest = w / n_parts;
     const int g = rest % nkv;
     const int t = row0 + rest / nkv;
+    if (skip_seq) {  // rows of prefill tiles belong to the prefill kernel
+      const int t0 = row0 + ((t - row0) & ~31);
+      if (t0 + 32 <= row0 + n_rows && prefill_tile(skip_seq, row_pos, t0, lane)) continue;
+    }
     // The row's block-table row: btab[row_bseq[t]], or row t itself when
     // the table is laid out per row (row_bseq null) -- one dependent load
     // fewer before the K/V loads.  Padding rows have no blocks.
@@ -304,6 +308,10 @@ template <typename T, int D, int G>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int t = a.row0 + blockIdx.x / a.nkv;
   const int g = blockIdx.x % a.nkv;
+  if (a.row_seq) {  // set only when the prefill kernel takes the prefill tiles
+    const int t0 = a.row0 + ((t - a.row0) & ~31);
+    if (t0 + 32 <= a.row0 + a.n_rows && prefill_tile(a.row_seq, a.row_pos, t0, threadIdx.x & 63)) return;
+  }
   if ((a.row_bseq ? a.row_bseq[t] : a.btab[(long)t * a.maxb]) < 0) return;
   const int ctx = a.row_pos[t] + 1;
   const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
@@ -325,7 +333,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
 }
 
 template <typename T, int D, int G>
-static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
+static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
+  AttnArgs a = a0;
+  if (!a.row_seq || !prefill_supported(a.dtype, D, G) || a.n_rows < 32) a.row_seq = nullptr;  // no prefill tiles
   const long total = (long)a.n_rows * a.nkv * a.n_parts;
   if (total <= 0) return;
   long grid = total;
@@ -335,12 +345,13 @@ static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((attn_decode_kernel<T, D, G, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st,               \
                      (const T*)a.q_att, (const T*)a.kc, (const T*)a.vc, a.row_bseq, a.row_pos, a.btab, (T*)a.out, \
                      a.part_acc, a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts,      \
-                     scale_log2)
+                     scale_log2, a.row_seq)
   if (a.waves == 1) NS_ATTN_LAUNCH(1);
   else NS_ATTN_LAUNCH(4);
 #undef NS_ATTN_LAUNCH
   if (a.n_parts > 1)
     hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3((unsigned)(a.n_rows * a.nkv)), dim3(256), 0, st, a);
+  if (a.row_seq) launch_attention_prefill(a, st);
 }
 
 #define NS_ATTN_CASES(X)                                                                               \

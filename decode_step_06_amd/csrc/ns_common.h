@@ -109,6 +109,17 @@ __device__ __forceinline__ f32x4_t slice_sum4(const float* p, long slice_stride,
 }
 
 // Wavefront (64-lane) reductions.
+// Step rows t0 .. t0+31 form a prefill tile: one sequence (row_seq >= 0) at
+// consecutive positions.  Lanes i and i + 32 both check row t0 + i; the
+// result is uniform over the wavefront.  The caller ensures the 32 rows exist.
+__device__ __forceinline__ bool prefill_tile(const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
+                                             int t0, int lane) {
+  const int i = lane & 31;
+  const int s0 = row_seq[t0], p0 = row_pos[t0];
+  const bool ok = s0 >= 0 && row_seq[t0 + i] == s0 && row_pos[t0 + i] == p0 + i;
+  return __all(ok);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -82,8 +82,15 @@ struct AttnArgs {
   int n_parts;              // partitions per row (max)
   int waves;                // wavefronts per work item: 1 or 4
   int wg_cap;               // 0 = one workgroup per work item
+  const int32_t* row_seq;   // [T] sequence of each row (-1: padding), or null: no prefill tiles
 };
 int attention_supported(int dtype, int d, int G);
+// Rows are taken in tiles of 32 from row0; a tile of one sequence at
+// consecutive positions (a prefill chunk) goes to the MFMA prefill kernel and
+// the decode kernel skips its rows (when row_seq is set and the shape is
+// supported), every other row to the decode kernel.
 void launch_attention(const AttnArgs& a, hipStream_t st);
+int prefill_supported(int dtype, int d, int G);
+void launch_attention_prefill(const AttnArgs& a, hipStream_t st);
 
 }  // namespace ns

@@ -47,7 +47,7 @@ class ns_weights(C.Structure):
 class ns_sched(C.Structure):
     _fields_ = [("n_nano", C.c_int32), ("nano_rows", C.c_int32 * 4), ("n_qkv", C.c_int32),
                 ("qkv_rows", C.c_int32 * 4), ("overlap", C.c_int32), ("attn_wg_cap", C.c_int32),
-                ("cu_mask_frac", C.c_float)]
+                ("cu_mask_frac", C.c_float), ("prefill_tiles", C.c_int32)]
 
 
 class ns_batch(C.Structure):
@@ -92,6 +92,8 @@ SIGNATURES = {
     "ns_op_attention_ws_bytes": (C.c_size_t, [C.POINTER(ns_model_desc), _I, _I]),
     "ns_op_attention": (C.c_int, [C.POINTER(ns_model_desc), _I, _P, _P, _I, _P, _P, _P, _I, _P, _P, C.c_size_t,
                                   _I, _P]),
+    "ns_op_attention_prefill": (C.c_int, [C.POINTER(ns_model_desc), _I, _P, _P, _I, _P, _P, _P, _I, _P, _P,
+                                          C.c_size_t, _I, _P]),
 }
 
 _LIB: Optional[C.CDLL] = None
@@ -133,7 +135,7 @@ def model_desc(shape) -> ns_model_desc:
 
 
 def make_sched(nano_rows: Sequence[int] = (), qkv_rows: Sequence[int] = (), overlap: bool = False,
-               attn_wg_cap: int = 0, cu_mask_frac: float = 0.0) -> ns_sched:
+               attn_wg_cap: int = 0, cu_mask_frac: float = 0.0, prefill_tiles: bool = False) -> ns_sched:
     s = ns_sched()
     s.n_nano = len(nano_rows)
     for i, r in enumerate(nano_rows):
@@ -144,6 +146,7 @@ def make_sched(nano_rows: Sequence[int] = (), qkv_rows: Sequence[int] = (), over
     s.overlap = int(bool(overlap))
     s.attn_wg_cap = int(attn_wg_cap)
     s.cu_mask_frac = float(cu_mask_frac)
+    s.prefill_tiles = int(bool(prefill_tiles))
     return s
 
 
@@ -325,3 +328,9 @@ def ns_op_attention(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos
                     ws, ws_bytes, wg_cap=0, stream=None) -> None:
     _check(lib().ns_op_attention(C.byref(desc), n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab,
                                  max_blocks_per_seq, out, ws, ws_bytes, wg_cap, _stream_ptr(stream)))
+
+
+def ns_op_attention_prefill(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab, max_blocks_per_seq,
+                            out, ws, ws_bytes, wg_cap=0, stream=None) -> None:
+    _check(lib().ns_op_attention_prefill(C.byref(desc), n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab,
+                                         max_blocks_per_seq, out, ws, ws_bytes, wg_cap, _stream_ptr(stream)))

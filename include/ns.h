@@ -170,7 +170,15 @@ int ns_slot_map(const ns_kv* kv, int32_t n_tok, const int32_t* seq, const int32_
  *     share of the GPU that attention takes.
  *   cu_mask_frac: 0 = none; else the second stream is created restricted to
  *     this fraction of the compute units (hipExtStreamCreateWithCUMask).
- *     Takes effect at engine creation only. */
+ *     Takes effect at engine creation only.
+ *   prefill_tiles: 0 = every row's attention on the decode kernel; 1 = rows
+ *     taken in tiles of 32 from the start of each attention launch, and a
+ *     tile of one sequence at 32 consecutive positions (a chunk of a prompt
+ *     topping up the dense batch: NanoFlow review, "Runtime details that keep
+ *     the pipeline fed") computed on matrix cores (fp16 probabilities);
+ *     costs an extra launch and a per-row check, so leave it 0 for batches
+ *     of decode rows only.  Captured graphs keep the value they were
+ *     captured with. */
 typedef struct {
   int32_t n_nano;
   int32_t nano_rows[4];
@@ -179,6 +187,7 @@ typedef struct {
   int32_t overlap;
   int32_t attn_wg_cap;
   float cu_mask_frac;
+  int32_t prefill_tiles;
 } ns_sched;
 
 /* One step's rows.  token_ids (host, [n_tok]) for models with a vocabulary,
@@ -334,6 +343,15 @@ int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, cons
  *   wg_cap: 0 or the maximum number of workgroups. */
 size_t ns_op_attention_ws_bytes(const ns_model_desc* desc, int32_t n_rows, int32_t max_blocks_per_seq);
 int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                    int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
+                    int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap,
+                    void* stream);
+
+/* The same with prefill tiles on (see ns_sched.prefill_tiles): rows are
+ * taken in tiles of 32 from row 0, and a tile whose rows are one sequence
+ * (row_bseq) at consecutive positions goes to the matrix-core prefill kernel.
+ * Arguments and errors as ns_op_attention. */
+int ns_op_attention_prefill(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
                     int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
                     int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap,
                     void* stream);

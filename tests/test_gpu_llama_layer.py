@@ -21,13 +21,15 @@ SAMPLE_ROWS = [0, 1, 255, 511,                 # decode rows (context 1024)
                1024 + 17, 1536 + 511]          # later chunks
 
 
-def test_llama70b_layer_dense_batch_sampled_rows():
+@pytest.mark.parametrize("prefill_tiles", [True, False], ids=["prefill-tiles", "decode-kernel-only"])
+def test_llama70b_layer_dense_batch_sampled_rows(prefill_tiles):
     w = WORKLOADS["llama70b_layer_t2048"]
     shape = w.model
     say("layer llama70b_layer_t2048: generating inputs")
     weights = gen_weights(shape, seed=0)
     b = gen_batch(w)
-    sched = ns.make_sched(nano_rows=w.nano_splits, qkv_rows=(512,) * w.qkv_splits, overlap=True)
+    sched = ns.make_sched(nano_rows=w.nano_splits, qkv_rows=(512,) * w.qkv_splits, overlap=True,
+                          prefill_tiles=prefill_tiles)
     c = Case(w, weights=weights, batch=b, sched=sched)
     try:
         say("  GPU step")
