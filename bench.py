@@ -311,8 +311,8 @@ def dense_batch(stream, steps=10):
         # under load
         t_end = time.time() + 1.5
         while time.time() < t_end:
-            ns.ns_op_gemm(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), lw["wgu"].data_ptr(), Cb.data_ptr(),
-                          stream=stream)
+            ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), lw["wgu"].data_ptr(),
+                                 Cb.data_ptr(), stream=stream)
             stream.synchronize()
         gem = {}
         for name, epi, N, K, Bw, C in (("qkv_proj", ns.NS_EPI_STORE, s.qkv_dim, H, lw["wqkv"], C32),
@@ -320,8 +320,9 @@ def dense_batch(stream, steps=10):
                                        ("gate_up_proj", ns.NS_EPI_SILU, F, H, lw["wgu"], Cb),
                                        ("down_proj", ns.NS_EPI_RESID, H, F, lw["wdown"], C32)):
             Ak = A[:, :K].contiguous()
-            t = time_launches(lambda i: ns.ns_op_gemm(ns.NS_BF16, epi, T, N, K, Ak.data_ptr(), Bw.data_ptr(),
-                                                      C.data_ptr(), stream), 5, stream)
+            # the engine's weights (K-slab-major), as the step reads them
+            t = time_launches(lambda i: ns.ns_op_gemm_packed(ns.NS_BF16, epi, T, N, K, Ak.data_ptr(), Bw.data_ptr(),
+                                                             C.data_ptr(), stream), 5, stream)
             fl = rf.gemm_flops(T, N, K, epi == ns.NS_EPI_SILU)
             gem[name] = dict(us=t * 1e6, tflops=fl / t / 1e12, frac=fl / t / 1e12 / rf.BF16_PEAK_TFLOPS)
         tot_fl = sum(rf.gemm_flops(T, N, K, sw) for N, K, sw in ((s.qkv_dim, H, False), (H, DQ, False),

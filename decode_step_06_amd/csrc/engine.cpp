@@ -390,6 +390,10 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   const int S_d = dec ? std::min(kMaxSlices, ns::gemm_partial_splits(n_tok, H, F)) : 1;
   float* pq = e->part_qkv();
   float* pr = e->part_res();
+  // bf16 models' projection weights are K-slab-major: their "leading
+  // dimension" is the row count; fp32 weights are row-major
+  const int pk = dt == NS_DT_BF16 ? 1 : 0;
+  auto wld = [&](int rows, int cols) { return pk ? rows : cols; };
   for (int l = 0; l < d.n_layers; ++l) {
     for (size_t j = 0; j < qparts.size(); ++j) {
       const int r0 = qparts[j].first, n = qparts[j].second - r0;
@@ -403,11 +407,11 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
         MARK(K_NORM);
       }
       if (dec) {
-        if (ns::launch_gemm_partial(n, QKV, H, h + r0 * H * es, H, e->wqkv[l], H, pq + (size_t)r0 * QKV, QKV, sq,
-                                    S_qkv, st))
+        if (ns::launch_gemm_partial(n, QKV, H, h + r0 * H * es, H, e->wqkv[l], QKV, pq + (size_t)r0 * QKV, QKV, sq,
+                                    S_qkv, st, 1))
           NS_FAIL(NS_ESHAPE, "unsupported QKV projection shape");
-      } else if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n, QKV, H, h + r0 * H * es, H, e->wqkv[l], H,
-                                 qkv + (size_t)r0 * QKV, QKV, st)) {
+      } else if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n, QKV, H, h + r0 * H * es, H, e->wqkv[l], wld(QKV, H),
+                                 qkv + (size_t)r0 * QKV, QKV, st, pk)) {
         NS_FAIL(NS_ESHAPE, "unsupported QKV projection shape");
       }
       MARK(K_QKV);
@@ -434,11 +438,11 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
         for (size_t j = 0; j < qparts.size(); ++j)
           if (qparts[j].first < r1 && qparts[j].second > r0) HIP_TRY(hipStreamWaitEvent(st, e->ev_att[j], 0));
       if (dec) {
-        if (ns::launch_gemm_partial(n, H, DQ, o + r0 * DQ * es, DQ, e->wo[l], DQ, pr + (size_t)r0 * H, H, sr, S_o,
-                                    st))
+        if (ns::launch_gemm_partial(n, H, DQ, o + r0 * DQ * es, DQ, e->wo[l], H, pr + (size_t)r0 * H, H, sr, S_o,
+                                    st, 1))
           NS_FAIL(NS_ESHAPE, "unsupported O projection shape");
-      } else if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, DQ, o + r0 * DQ * es, DQ, e->wo[l], DQ,
-                                 x + (size_t)r0 * H, H, st)) {
+      } else if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, DQ, o + r0 * DQ * es, DQ, e->wo[l], wld(H, DQ),
+                                 x + (size_t)r0 * H, H, st, pk)) {
         NS_FAIL(NS_ESHAPE, "unsupported O projection shape");
       }
       MARK(K_O);
@@ -448,16 +452,16 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
       else
         ns::launch_rmsnorm(dt, x + (size_t)r0 * H, e->mlp_norm[l], h + r0 * H * es, n, H, d.rms_eps, st);
       MARK(K_NORM);
-      if (ns::launch_gemm(dt, ns::EPI_SILU_MUL, n, F, H, h + r0 * H * es, H, e->wgu[l], H, act + r0 * F * es, F,
-                          st))
+      if (ns::launch_gemm(dt, ns::EPI_SILU_MUL, n, F, H, h + r0 * H * es, H, e->wgu[l], wld(2 * F, H),
+                          act + r0 * F * es, F, st, pk))
         NS_FAIL(NS_ESHAPE, "unsupported gate-up projection shape");
       MARK(K_GU);
       if (dec) {
-        if (ns::launch_gemm_partial(n, H, F, act + r0 * F * es, F, e->wdown[l], F, pr + (size_t)r0 * H, H, sr, S_d,
-                                    st))
+        if (ns::launch_gemm_partial(n, H, F, act + r0 * F * es, F, e->wdown[l], H, pr + (size_t)r0 * H, H, sr, S_d,
+                                    st, 1))
           NS_FAIL(NS_ESHAPE, "unsupported down projection shape");
-      } else if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, F, act + r0 * F * es, F, e->wdown[l], F,
-                                 x + (size_t)r0 * H, H, st)) {
+      } else if (ns::launch_gemm(dt, ns::EPI_RESID_F32, n, H, F, act + r0 * F * es, F, e->wdown[l], wld(H, F),
+                                 x + (size_t)r0 * H, H, st, pk)) {
         NS_FAIL(NS_ESHAPE, "unsupported down projection shape");
       }
       MARK(K_DOWN);
@@ -787,15 +791,37 @@ int ns_engine_last_launches(const ns_engine* e, int32_t* out) {
 }
 
 // ---------------------------------------------------------------- single ops
-int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, const void* B, void* C,
-               void* stream) {
+namespace {
+int op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, const void* B, void* C,
+            void* stream, bool packed) {
   if (dtype != NS_F32 && dtype != NS_BF16) NS_FAIL(NS_EINVAL, "bad dtype");
+  if (packed && dtype != NS_BF16) NS_FAIL(NS_EINVAL, "the K-slab-major layout is bf16 only");
   if (epi < 0 || epi > 2) NS_FAIL(NS_EINVAL, "bad epilogue");
   if (M < 0 || N < 0 || K <= 0) NS_FAIL(NS_EINVAL, "bad sizes");
   if ((M > 0 && N > 0) && (!A || !B || !C)) NS_FAIL(NS_EINVAL, "null matrix");
   const int dt = dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
   if (!ns::gemm_supported(dt, K)) NS_FAIL(NS_ESHAPE, "K = %d unsupported (bf16 needs K %% 32 == 0)", K);
-  ns::launch_gemm(dt, epi, M, N, K, A, K, B, K, C, N, (hipStream_t)stream);
+  const int b_rows = epi == NS_EPI_SILU ? 2 * N : N;
+  ns::launch_gemm(dt, epi, M, N, K, A, K, B, packed ? b_rows : K, C, N, (hipStream_t)stream, packed ? 1 : 0);
+  HIP_TRY(hipGetLastError());
+  return NS_OK;
+}
+}  // namespace
+
+int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, const void* B, void* C,
+               void* stream) {
+  return op_gemm(dtype, epi, M, N, K, A, B, C, stream, false);
+}
+
+int ns_op_gemm_packed(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
+                      void* C, void* stream) {
+  return op_gemm(dtype, epi, M, N, K, A, B, C, stream, true);
+}
+
+int ns_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols, void* stream) {
+  if (!src || !dst || src == dst) NS_FAIL(NS_EINVAL, "null or equal source and destination");
+  if (rows < 1 || cols < 32 || cols % 32 != 0) NS_FAIL(NS_EINVAL, "bad shape [%d, %d]", rows, cols);
+  ns::launch_pack_kslab(src, dst, rows, cols, (hipStream_t)stream);
   HIP_TRY(hipGetLastError());
   return NS_OK;
 }

@@ -51,7 +51,7 @@ template <int BM, int BN, int BK, int WM, int WN, int EPI, typename OutT>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                                  const bf16_t* __restrict__ B, int ldb, int M, int N,
                                                                  int K, void* __restrict__ Cv, int ldc, int splits,
-                                                                 long slice_stride) {
+                                                                 long slice_stride, int bpk) {
   using C = GemmCfg<BM, BN, BK, WM, WN, EPI>;
   constexpr int LDK = C::LDK;
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDK];
@@ -96,8 +96,9 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
     for (int i = 0; i < C::B_PT; ++i) {
       const int c = tid + i * C::NT;
       if (c < C::B_CH) {
-        const int r = c / (BK / 8), k8 = c % (BK / 8);
-        rb[i] = *(const u32x4_t*)(B + (long)b_row(r) * ldb + k0 + k8 * 8);
+        const int r = c / (BK / 8), k = k0 + (c % (BK / 8)) * 8;
+        rb[i] = bpk ? *(const u32x4_t*)(B + ((long)(k >> 5) * ldb + b_row(r)) * 32 + (k & 31))
+                    : *(const u32x4_t*)(B + (long)b_row(r) * ldb + k);
       }
     }
   };
@@ -251,7 +252,8 @@ constexpr unsigned BUF_RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit dwords, n
 template <int EPI, typename OutT, int BM = 256>
 __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
                                                        const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
-                                                       void* __restrict__ Cv, int ldc, int splits, long slice_stride) {
+                                                       void* __restrict__ Cv, int ldc, int splits, long slice_stride,
+                                                       int bpk) {
   static_assert(BM == 256 || BM == 128, "tile rows");
   constexpr int BN = 256, BK = 32, NSTAGE = 4;
   constexpr int TM = BM / 2, TN = 128, FM = TM / 32, FN = 4;  // 32 x 32 fragments
@@ -279,7 +281,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
   const int m0 = tile_m * BM, n0 = tile_n * OUT_BN;
 
   const unsigned a_bytes = (unsigned)((long)M * lda * 2);
-  const unsigned b_bytes = (unsigned)((long)((EPI == EPI_SILU_MUL) ? 2 * N : N) * ldb * 2);
+  const unsigned b_bytes = (unsigned)(bpk ? (long)K * ldb * 2 : (long)((EPI == EPI_SILU_MUL) ? 2 * N : N) * ldb * 2);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)a_bytes, BUF_RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)b_bytes, BUF_RSRC_WORD3);
   // Load instruction j of wavefront w fills the 16 LDS rows of group
@@ -310,7 +312,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
         int n = n0 + r;
         brow = n < N ? n : N - 1;
       }
-      voff[j] = (unsigned)(((long)brow * ldb + c * 8) * 2);
+      voff[j] = bpk ? (unsigned)(brow * 64 + c * 16) : (unsigned)(((long)brow * ldb + c * 8) * 2);
     }
   }
   // K slabs [sb, sb + nk) of split blockIdx.y (all of K unless EPI_PARTIAL);
@@ -322,12 +324,14 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
   auto issue = [&](int kt, int j0, int j1) {
     const int ks = sb + (kt < nk ? kt : nk - 1);
     const unsigned soff = (unsigned)ks * (BK * 2);
+    // packed B: slab ks is a contiguous [rows][32] block
+    const unsigned soff_b = bpk ? (unsigned)ks * (unsigned)ldb * (BK * 2) : soff;
     char* base = lds + (kt % NSTAGE) * STAGE;
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       const int g = wave + 4 * j;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(g < AG ? ra : rb, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j],
-                                               soff, 0, 0);
+                                               g < AG ? soff : soff_b, 0, 0);
     }
   };
   // v_mfma_f32_32x32x16_bf16 operands: lane l holds row (or column) l % 32
@@ -500,7 +504,7 @@ template <int MF, int NF, int NW, int U, int EPI, typename OutT>
 __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                             const bf16_t* __restrict__ B, int ldb, int M, int N,
                                                             int K, void* __restrict__ Cv, int ldc, int splits,
-                                                            long slice_stride) {
+                                                            long slice_stride, int bpk) {
   constexpr int DUAL = (EPI == EPI_SILU_MUL) ? 2 : 1;
   constexpr int NB = NF * DUAL;  // B fragments per k-step (U k-steps in flight)
   __shared__ f32x4_t red[NW][MF * NB][64];
@@ -515,8 +519,10 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
     int n = n0 + 16 * f + fr;
     n = n < N ? n : N - 1;
 #pragma unroll
-    for (int dd = 0; dd < DUAL; ++dd) brow[f * DUAL + dd] = B + (long)(dd ? N + n : n) * ldb + fk;
+    for (int dd = 0; dd < DUAL; ++dd) brow[f * DUAL + dd] = B + (long)(dd ? N + n : n) * (bpk ? 32 : ldb) + fk;
   }
+  // elements between k-steps of 32: row-major, or one packed slab of ldb rows
+  const long bstep = bpk ? (long)ldb * 32 : 32;
   const bf16_t* arow[MF];
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
@@ -546,7 +552,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
 #pragma unroll
     for (int u = 0; u < R; ++u) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bv[u][j] = *(const bf16x8_t*)(brow[j] + (s + u) * 32);
+      for (int j = 0; j < NB; ++j) bv[u][j] = *(const bf16x8_t*)(brow[j] + (s + u) * bstep);
 #pragma unroll
       for (int i = 0; i < MF; ++i) av[u][i] = *(const bf16x8_t*)(arow[i] + (s + u) * 32);
     }
@@ -645,33 +651,33 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
 
 template <int BM, int BN, int BK, int WM, int WN, int EPI>
 static void run_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
-                     hipStream_t st, int splits = 1, long slice_stride = 0) {
+                     hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? BN / 2 : BN;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t>), dim3((unsigned)tiles, (unsigned)splits),
                      dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc,
-                     splits, slice_stride);
+                     splits, slice_stride, bpk);
 }
 
 template <int EPI, int BM = 256>
 static void run_big(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
-                    hipStream_t st, int splits = 1, long slice_stride = 0) {
+                    hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
   hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0, st,
-                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride);
+                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
 }
 
 template <int MF, int NF, int NW, int EPI>
 static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
-                     hipStream_t st, int splits = 1, long slice_stride = 0) {
+                     hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
   constexpr int NB = NF * (EPI == EPI_SILU_MUL ? 2 : 1);
   // k-steps in flight, as registers allow (1024-thread workgroups get 128
   // VGPRs per lane)
   constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 4 ? 8 : 4);
   const unsigned grid = (unsigned)((N + 16 * NF - 1) / (16 * NF) * splits);
   hipLaunchKernelGGL((gemv_bf16_kernel<MF, NF, NW, U, EPI, bf16_t>), dim3(grid), dim3(64 * NW), 0, st,
-                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride);
+                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
 }
 
 // Tile shapes for M > 64 rows, largest first: 256 x 256 and 128 x 256 (the
@@ -682,8 +688,8 @@ constexpr int kTileCols[4] = {256, 256, 128, 64};
 constexpr int kFillTarget = 256;  // workgroups that fill the chip (one per CU)
 
 // The big kernel addresses its operands with 32-bit buffer offsets.
-static bool big_fits(int M, int lda, long b_rows, int ldb) {
-  return (long)M * lda * 2 < (1L << 32) && b_rows * ldb * 2 < (1L << 32);
+static bool big_fits(int M, int lda, long b_rows, int ldb, int K, int bpk) {
+  return (long)M * lda * 2 < (1L << 32) && (bpk ? (long)K * ldb : b_rows * ldb) * 2 < (1L << 32);
 }
 
 // Output tiles of a launch; SwiGLU tiles hold gate and up columns, so they
@@ -726,7 +732,8 @@ int gemm_partial_splits(int M, int N, int K) {
 }
 
 int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* P, int ldp,
-                        long slice_stride, int splits, hipStream_t st) {
+                        long slice_stride, int splits, hipStream_t st, int b_packed) {
+  const int bpk = b_packed ? 1 : 0;
   if (M <= 0 || N <= 0) return 0;
   if (K % 32 != 0 || splits < 1 || splits > K / 32) return -1;
   if (M <= 64) {
@@ -736,8 +743,8 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
     const bool nf2 = (long)((N + 31) / 32) * splits >= 256;
 #define NS_GEMV_PART(MF)                                                                             \
   do {                                                                                               \
-    if (nf2) run_gemv<MF, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride); \
-    else run_gemv<MF, 1, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);     \
+    if (nf2) run_gemv<MF, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride); \
+    else run_gemv<MF, 1, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);     \
   } while (0)
     if (M <= 16) NS_GEMV_PART(1);
     else if (M <= 32) NS_GEMV_PART(2);
@@ -745,13 +752,13 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
 #undef NS_GEMV_PART
   } else {
     int kind = partial_plan(M, N, K).kind;
-    if ((kind == TILE_BIG || kind == TILE_BIG128) && !big_fits(M, lda, N, ldb)) kind = TILE_128;
-    if (kind == TILE_BIG) run_big<EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+    if ((kind == TILE_BIG || kind == TILE_BIG128) && !big_fits(M, lda, N, ldb, K, bpk)) kind = TILE_128;
+    if (kind == TILE_BIG) run_big<EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
     else if (kind == TILE_BIG128)
-      run_big<EPI_PARTIAL, 128>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+      run_big<EPI_PARTIAL, 128>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
     else if (kind == TILE_128)
-      run_bf16<128, 128, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
-    else run_bf16<64, 64, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, splits, slice_stride);
+      run_bf16<128, 128, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
+    else run_bf16<64, 64, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
   }
   return 0;
 }
@@ -761,23 +768,23 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
 // K-splitting wavefronts as the LDS for their partial sums allows (<= 64 KB).
 template <int MF, int EPI>
 static void dispatch_gemv_m(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C, int ldc,
-                            hipStream_t st) {
+                            hipStream_t st, int bpk) {
   constexpr int NB1 = EPI == EPI_SILU_MUL ? 2 : 1;
   constexpr int NW_LONG = (64 / (MF * NB1)) < 16 ? (64 / (MF * NB1)) : 16;
   const bool wide = (long)N / 64 >= 1024;
   if constexpr (EPI != EPI_SILU_MUL) {
-    if (wide) return run_gemv<MF, 4, 4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+    if (wide) return run_gemv<MF, 4, 4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
   }
-  if (K > 2048) run_gemv<MF, 1, NW_LONG, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  else run_gemv<MF, 1, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+  if (K > 2048) run_gemv<MF, 1, NW_LONG, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+  else run_gemv<MF, 1, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
 }
 
 template <int EPI>
 static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C, int ldc,
-                          hipStream_t st) {
-  if (M <= 16) return dispatch_gemv_m<1, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  if (M <= 32) return dispatch_gemv_m<2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+                          hipStream_t st, int bpk) {
+  if (M <= 16) return dispatch_gemv_m<1, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+  if (M <= 32) return dispatch_gemv_m<2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+  if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
   // M > 64: the tile shape with the best estimated throughput -- its
   // relative per-CU rate (measured on MI355X: the 256 x 256 kernel 1.0,
   // 128 x 256 about 0.72, 128 x 128 about 0.55, 64 x 64 about 0.35) times the
@@ -788,7 +795,7 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
   const long b_rows = (EPI == EPI_SILU_MUL) ? 2L * N : (long)N;
   constexpr double kRate[4] = {1.0, 0.72, 0.55, 0.35};
   constexpr long kSlots[4] = {256, 256, 512, 1024};
-  const bool fits = big_fits(M, lda, b_rows, ldb);
+  const bool fits = big_fits(M, lda, b_rows, ldb, K, bpk);
   int kind = TILE_64;
   double best = -1.0;
   for (int k = (fits ? (M > 128 ? TILE_BIG : TILE_BIG128) : TILE_128); k <= TILE_64; ++k) {
@@ -802,24 +809,42 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
       kind = k;
     }
   }
-  if (kind == TILE_BIG) return run_big<EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-  if (kind == TILE_BIG128) return run_big<EPI, 128>(M, N, K, A, lda, B, ldb, C, ldc, st);
+  if (kind == TILE_BIG) return run_big<EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+  if (kind == TILE_BIG128) return run_big<EPI, 128>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
   if (kind == TILE_128) {
-    if (k64) run_bf16<128, 128, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-    else run_bf16<128, 128, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+    if (k64) run_bf16<128, 128, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+    else run_bf16<128, 128, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
   } else {
     constexpr int BN64 = (EPI == EPI_SILU_MUL) ? 128 : 64;
-    if (k64) run_bf16<64, BN64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
-    else run_bf16<64, BN64, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st);
+    if (k64) run_bf16<64, BN64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+    else run_bf16<64, BN64, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
   }
 }
 
 int gemm_supported(int dtype, int K) { return dtype == NS_DT_F32 ? K > 0 : (K > 0 && K % 32 == 0); }
 
+// Row-major [rows, cols] bf16 -> K-slab-major: thread = one 16-byte piece.
+__global__ void __launch_bounds__(256) pack_kslab_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
+                                                         int rows, int cols) {
+  const long c = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = cols / 8;
+  if (c >= (long)rows * per_row) return;
+  const int n = (int)(c / per_row), k = (int)(c % per_row) * 8;
+  *(u32x4_t*)(dst + ((long)(k >> 5) * rows + n) * 32 + (k & 31)) = *(const u32x4_t*)(src + (long)n * cols + k);
+}
+
+void launch_pack_kslab(const void* src, void* dst, int rows, int cols, hipStream_t st) {
+  const long pieces = (long)rows * (cols / 8);
+  if (pieces <= 0) return;
+  hipLaunchKernelGGL(pack_kslab_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st, (const bf16_t*)src,
+                     (bf16_t*)dst, rows, cols);
+}
+
 int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C,
-                int ldc, hipStream_t st) {
+                int ldc, hipStream_t st, int b_packed) {
   if (M <= 0 || N <= 0) return 0;
-  if (!gemm_supported(dtype, K)) return -1;
+  if (!gemm_supported(dtype, K) || (b_packed && dtype != NS_DT_BF16)) return -1;
+  const int bpk = b_packed ? 1 : 0;
   if (dtype == NS_DT_F32) {
     dim3 grid((N + 15) / 16, (M + 15) / 16);
     const float* a = (const float*)A;
@@ -833,9 +858,9 @@ int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda,
     return 0;
   }
   switch (epi) {
-    case EPI_STORE_F32: dispatch_bf16<EPI_STORE_F32>(M, N, K, A, lda, B, ldb, C, ldc, st); break;
-    case EPI_RESID_F32: dispatch_bf16<EPI_RESID_F32>(M, N, K, A, lda, B, ldb, C, ldc, st); break;
-    default: dispatch_bf16<EPI_SILU_MUL>(M, N, K, A, lda, B, ldb, C, ldc, st); break;
+    case EPI_STORE_F32: dispatch_bf16<EPI_STORE_F32>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk); break;
+    case EPI_RESID_F32: dispatch_bf16<EPI_RESID_F32>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk); break;
+    default: dispatch_bf16<EPI_SILU_MUL>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk); break;
   }
   return 0;
 }

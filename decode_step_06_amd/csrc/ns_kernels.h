@@ -20,8 +20,12 @@ enum GemmEpi {
 };
 
 // Returns 0, or -1 when the shape is unsupported (K % 32 != 0 for bf16).
+// b_packed (bf16 only): B is stored K-slab-major, element (n, k) at
+// ((k / 32) * ldb + n) * 32 + k % 32 with ldb = B's row count (N, or 2N for
+// SwiGLU), so each 32-wide K slab of every row is one 64-byte piece of a
+// contiguous [rows][32] block; otherwise row-major with row stride ldb.
 int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C,
-                int ldc, hipStream_t st);
+                int ldc, hipStream_t st, int b_packed = 0);
 int gemm_supported(int dtype, int K);
 
 // Split-K projection (bf16): slice s of the result (P + s * slice_stride,
@@ -32,7 +36,9 @@ int gemm_supported(int dtype, int K);
 // is accepted.  Returns -1 for unsupported shapes.
 int gemm_partial_splits(int M, int N, int K);
 int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* P, int ldp,
-                        long slice_stride, int splits, hipStream_t st);
+                        long slice_stride, int splits, hipStream_t st, int b_packed = 0);
+// Row-major bf16 [rows, cols] -> K-slab-major (cols % 32 == 0).
+void launch_pack_kslab(const void* src, void* dst, int rows, int cols, hipStream_t st);
 
 void launch_embed(int dtype, const void* E, const int32_t* tok, float* x, int T, int H, int V, hipStream_t st);
 void launch_copy_rows(const float* src, float* dst, long n, hipStream_t st);

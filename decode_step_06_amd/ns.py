@@ -89,6 +89,8 @@ SIGNATURES = {
     "ns_engine_profile": (C.c_int, [_P, _I]),
     "ns_engine_profile_read": (C.c_int, [_P, _I, _PI, C.POINTER(C.c_float), _PI]),
     "ns_op_gemm": (C.c_int, [_I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "ns_op_gemm_packed": (C.c_int, [_I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "ns_pack_weight": (C.c_int, [_P, _P, _I, _I, _P]),
     "ns_op_attention_ws_bytes": (C.c_size_t, [C.POINTER(ns_model_desc), _I, _I]),
     "ns_op_attention": (C.c_int, [C.POINTER(ns_model_desc), _I, _P, _P, _I, _P, _P, _P, _I, _P, _P, C.c_size_t,
                                   _I, _P]),
@@ -318,6 +320,14 @@ def ns_engine_profile_read(eng, cap: int = 8192):
 # ---------------------------------------------------------------- single kernels
 def ns_op_gemm(dtype: int, epi: int, M: int, N: int, K: int, A: int, B: int, Cp: int, stream=None) -> None:
     _check(lib().ns_op_gemm(dtype, epi, M, N, K, A, B, Cp, _stream_ptr(stream)))
+
+
+def ns_op_gemm_packed(dtype: int, epi: int, M: int, N: int, K: int, A: int, B: int, Cp: int, stream=None) -> None:
+    _check(lib().ns_op_gemm_packed(dtype, epi, M, N, K, A, B, Cp, _stream_ptr(stream)))
+
+
+def ns_pack_weight(src: int, dst: int, rows: int, cols: int, stream=None) -> None:
+    _check(lib().ns_pack_weight(src, dst, rows, cols, _stream_ptr(stream)))
 
 
 def ns_op_attention_ws_bytes(desc, n_rows: int, max_blocks_per_seq: int) -> int:

@@ -29,8 +29,24 @@ def nan_fill_(buf: torch.Tensor, shape: ModelShape) -> None:
         buf.view(torch.int32).fill_(0x7FC00000)
 
 
+PACKED = ("wqkv", "wo", "wgu", "wdown")  # K-slab-major in bf16 models (see ns_weights)
+
+
+def pack_kslab_host(w: np.ndarray) -> np.ndarray:
+    """Row-major [R, K] -> the K-slab-major layout (same bytes, reordered)."""
+    R, K = w.shape
+    return np.ascontiguousarray(w.reshape(R, K // 32, 32).transpose(1, 0, 2)).reshape(R, K)
+
+
+def unpack_kslab(t: torch.Tensor, R: int, K: int) -> torch.Tensor:
+    """K-slab-major device tensor -> row-major [R, K] (a copy)."""
+    return t.reshape(K // 32, R, 32).permute(1, 0, 2).reshape(R, K).contiguous()
+
+
 class DeviceWeights:
-    """Weights as device tensors plus the ns_weights struct pointing at them."""
+    """Weights as device tensors plus the ns_weights struct pointing at them.
+    In bf16 models the projection matrices are held K-slab-major, as the
+    engine reads them."""
 
     def __init__(self, shape: ModelShape, tensors: dict):
         self.shape = shape
@@ -54,7 +70,9 @@ class DeviceWeights:
         def up(a):
             return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
 
-        layers = [{k: up(v) for k, v in lw.items()} for lw in w["layers"]]
+        pk = shape.dtype == "bf16"
+        layers = [{k: up(pack_kslab_host(v) if (pk and k in PACKED) else v) for k, v in lw.items()}
+                  for lw in w["layers"]]
         emb = up(w["embed"])
         lm = emb if (shape.tied and w["embed"] is not None) else up(w["lm_head"])
         return cls(shape, {"layers": layers, "final_norm": up(w["final_norm"]), "embed": emb, "lm_head": lm})
@@ -74,15 +92,37 @@ class DeviceWeights:
         def gain(shp):
             return (1.0 + torch.randn(shp, generator=g, device=device, dtype=torch.float32) * GAIN_STD).to(dt)
 
+        def packed(shp):  # drawn row-major, stored K-slab-major
+            a = mat(shp)
+            if shape.dtype != "bf16":
+                return a
+            out = torch.empty_like(a)
+            ns.ns_pack_weight(a.data_ptr(), out.data_ptr(), shp[0], shp[1])
+            torch.cuda.synchronize()
+            return out
+
         layers = []
         for _ in range(shape.n_layers):
-            layers.append({n: (gain(s) if n.endswith("norm") else mat(s)) for n, s in weight_names(shape)})
+            layers.append({n: (gain(s) if n.endswith("norm") else packed(s) if n in PACKED else mat(s))
+                           for n, s in weight_names(shape)})
         fn = emb = lm = None
         if shape.vocab:
             fn = gain((shape.hidden,))
             emb = mat((shape.vocab, shape.hidden))
             lm = emb if shape.tied else mat((shape.vocab, shape.hidden))
         return cls(shape, {"layers": layers, "final_norm": fn, "embed": emb, "lm_head": lm})
+
+    def logical_layer(self, l: int) -> dict:
+        """Layer l's weights as row-major device tensors (copies)."""
+        from .inputs import weight_names
+        shapes = dict(weight_names(self.shape))
+        out = {}
+        for k, v in self.t["layers"][l].items():
+            if k in PACKED and self.shape.dtype == "bf16":
+                out[k] = unpack_kslab(v, *shapes[k])
+            else:
+                out[k] = v
+        return out
 
     def bytes(self) -> int:
         seen, total = set(), 0

@@ -80,15 +80,22 @@ typedef struct {
                            and KV cache (accumulation is always fp32)          */
 } ns_model_desc;
 
-/* Device pointers to the weights (element type = dtype), row-major [out, in]:
+/* Device pointers to the weights (element type = dtype), [out, in]:
  *   attn_norm[l], mlp_norm[l]: [H]
  *   wqkv[l]: [(nq + 2 nkv) d, H]   rows: all q heads, then k heads, then v heads
  *   wo[l]:   [H, nq d]
  *   wgu[l]:  [2F, H]               rows: gate (F rows) then up (F rows)
  *   wdown[l]:[H, F]
  *   final_norm: [H]; embed: [V, H]; lm_head: [V, H] (may equal embed).
- * The per-layer arrays are host arrays of n_layers device pointers; the
- * engine copies them at creation. */
+ * Layout: embed, lm_head and every fp32 model's matrices are row-major.  In
+ * a bf16 model wqkv, wo, wgu and wdown are K-slab-major instead: element
+ * (row r, column k) of a [R, K] matrix sits at ((k / 32) * R + r) * 32 +
+ * k % 32, so the 32 columns k0 .. k0+31 of all R rows form one contiguous
+ * [R][32] block and each row's piece of it is a whole 64-byte segment (the
+ * projection kernels then read whole cache lines; row-major rows of a
+ * 32-wide K slab cover half of each 128-byte line).  ns_pack_weight converts
+ * a row-major matrix.  The per-layer arrays are host arrays of n_layers
+ * device pointers; the engine copies them at creation. */
 typedef struct {
   const void* const* attn_norm;
   const void* const* wqkv;
@@ -330,6 +337,17 @@ enum { NS_EPI_STORE = 0, NS_EPI_RESID = 1, NS_EPI_SILU = 2 };
  * (NS_ESHAPE otherwise). */
 int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
                void* C, void* stream);
+
+/* The same with B K-slab-major (the layout of a bf16 model's projection
+ * weights, see ns_weights): bf16 only (NS_EINVAL otherwise). */
+int ns_op_gemm_packed(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A,
+                      const void* B, void* C, void* stream);
+
+/* Convert a row-major bf16 matrix [rows, cols] (device) into the K-slab-major
+ * layout of ns_weights (device, a separate buffer of the same size), on
+ * `stream`.  Errors: NS_EINVAL (null or equal pointers, rows < 1, cols not a
+ * positive multiple of 32). */
+int ns_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols, void* stream);
 
 /* Paged GQA decode attention (nanoserve notes, changes table; NanoFlow
  * review, operator table: decode attention).  Row i (query position

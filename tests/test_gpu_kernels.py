@@ -56,6 +56,45 @@ def test_gemm_bf16_matches_float64(M, N, K, epi):
     assert rel_l2(got, ref) < tol, (rel_l2(got, ref), max_abs(got, ref))
 
 
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES + [(2048, 1024, 8192), (256, 896, 4864), (128, 1152, 896)])
+@pytest.mark.parametrize("epi", [ns.NS_EPI_STORE, ns.NS_EPI_SILU])
+def test_gemm_kslab_major_weights_equal_row_major(M, N, K, epi):
+    """The engine's K-slab-major weights give the row-major result bit for
+    bit (same kernels, same accumulation order; only the addressing of B
+    differs), at every regime: weight streaming, split tiles, big tiles."""
+    from decode_step_06_amd.runner import pack_kslab_host
+    say(f"gemm packed B M={M} N={N} K={K} epi={epi}")
+    rng = np.random.default_rng(M + 3 * N + K + epi)
+    A = _bf16_grid(rng.standard_normal((M, K))).cuda()
+    Bn = 2 * N if epi == ns.NS_EPI_SILU else N
+    Bh = _bf16_grid(rng.standard_normal((Bn, K)) * 0.05)
+    Bp = torch.from_numpy(pack_kslab_host(Bh.view(torch.int16).numpy())).view(torch.bfloat16).cuda()
+    # the device packer agrees with the host reordering
+    Bd = Bh.cuda()
+    Bq = torch.empty_like(Bd)
+    ns.ns_pack_weight(Bd.data_ptr(), Bq.data_ptr(), Bn, K)
+    torch.cuda.synchronize()
+    assert torch.equal(Bq.view(torch.int16), Bp.view(torch.int16))
+    dt = torch.bfloat16 if epi == ns.NS_EPI_SILU else torch.float32
+    C1 = torch.zeros((M, N), dtype=dt, device="cuda")
+    C2 = torch.zeros((M, N), dtype=dt, device="cuda")
+    ns.ns_op_gemm(ns.NS_BF16, epi, M, N, K, A.data_ptr(), Bd.data_ptr(), C1.data_ptr())
+    ns.ns_op_gemm_packed(ns.NS_BF16, epi, M, N, K, A.data_ptr(), Bp.data_ptr(), C2.data_ptr())
+    torch.cuda.synchronize()
+    assert torch.equal(C1.cpu(), C2.cpu())
+
+
+def test_pack_weight_rejects_bad_shapes():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros_like(x)
+    for args in ((x.data_ptr(), x.data_ptr(), 4, 64), (x.data_ptr(), y.data_ptr(), 4, 48),
+                 (x.data_ptr(), y.data_ptr(), 0, 64), (0, y.data_ptr(), 4, 64)):
+        with pytest.raises(ns.NSError):
+            ns.ns_pack_weight(*args)
+    with pytest.raises(ns.NSError):  # the packed layout is bf16 only
+        ns.ns_op_gemm_packed(ns.NS_F32, ns.NS_EPI_STORE, 4, 4, 64, x.data_ptr(), x.data_ptr(), y.data_ptr())
+
+
 @pytest.mark.parametrize("epi", [ns.NS_EPI_STORE, ns.NS_EPI_RESID, ns.NS_EPI_SILU])
 def test_gemm_f32_matches_float64(epi):
     rng = np.random.default_rng(epi)

@@ -48,7 +48,7 @@ class _LayerStream:
             if layer % 10 == 0:
                 say(f"  oracle layer {layer}")
             self.cur = None
-            self.cur = {k: v.cpu().double().numpy() for k, v in self.dw.t["layers"][layer].items()}
+            self.cur = {k: v.cpu().double().numpy() for k, v in self.dw.logical_layer(layer).items()}
             self.idx = layer
         return self.cur
 
