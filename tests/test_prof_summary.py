@@ -1,0 +1,57 @@
+"""Host logic of the rocprofv3 summariser (profiles/ files): kernel-trace
+tables and the calibrated HBM-traffic figure, on small hand-made CSVs."""
+import csv
+import hashlib
+
+from decode_step_06_amd import prof_summary as ps
+
+
+def _write(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_trace_table_and_last_n_mean(tmp_path, capsys):
+    p = tmp_path / "trace.csv"
+    rows = [["void ns::gemv_bf16_kernel<1, unsigned short>(int)", 0, 4000],
+            ["void ns::attn_decode_kernel<unsigned short, 64, 7, 4>(int)", 5000, 17000],
+            ["void ns::attn_decode_kernel<unsigned short, 64, 7, 4>(int)", 20000, 30000],
+            ["void ns::attn_decode_kernel<unsigned short, 64, 7, 4>(int)", 31000, 39000],
+            ["void at::native::other(int)", 40000, 90000]]
+    _write(p, ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    ps.main(["trace", str(p), "--title", "T", "--cmd", "C", "--kernel", "attn_decode_kernel", "--last", "2"])
+    out = capsys.readouterr().out
+    assert "| `ns::attn_decode_kernel<bf16, 64, 7, 4>` | 3 | 10.00 | 0.030 |" in out
+    assert "other" not in out                       # only the library's kernels are tabled
+    assert "mean 9.000 us" in out                   # (10 + 8) / 2 over the last two dispatches
+
+
+def test_traffic_calibration(tmp_path):
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    calib = 256 << 20
+    # the copy's counters read half (fetch) and all (write) of its bytes, in KiB
+    f_rows = [[1, "copy_kernel", "FETCH_SIZE", calib / 2 / 1024],
+              [2, "ns::attn_decode_kernel<x>", "FETCH_SIZE", 100.0],
+              [3, "ns::attn_decode_kernel<x>", "FETCH_SIZE", 60.0],
+              [3, "ns::attn_decode_kernel<x>", "FETCH_SIZE", 40.0]]   # two rows of one dispatch add up
+    w_rows = [[1, "copy_kernel", "WRITE_SIZE", calib / 1024],
+              [2, "ns::attn_decode_kernel<x>", "WRITE_SIZE", 8.0],
+              [3, "ns::attn_decode_kernel<x>", "WRITE_SIZE", 8.0]]
+    _write(fetch, hdr, f_rows)
+    _write(write, hdr, w_rows)
+    src = tmp_path / "k.hip"
+    src.write_text("kernel source\n")
+    out = tmp_path / "traffic.txt"
+    ps.main(["traffic", "--fetch", str(fetch), "--write", str(write), "--kernel", "attn_decode_kernel", "--last", "2",
+             "--source", str(src), "--calib-bytes", str(calib), "--algorithmic-bytes", "409600", "--out", str(out),
+             "--cmd", "c1"])
+    vals = dict(line.split(": ", 1) for line in out.read_text().splitlines() if ": " in line and not line.startswith("#"))
+    assert float(vals["fetch_scale"]) == 2.0 and float(vals["write_scale"]) == 1.0
+    assert int(vals["fetch_bytes_per_launch"]) == 100 * 1024 * 2      # mean of 100 and 60 + 40, scaled
+    assert int(vals["write_bytes_per_launch"]) == 8 * 1024
+    assert int(vals["traffic_bytes_per_launch"]) == 100 * 1024 * 2 + 8 * 1024
+    assert vals["source_sha256"] == hashlib.sha256(b"kernel source\n").hexdigest()
+    assert abs(float(vals["traffic_over_algorithmic"]) - (100 * 1024 * 2 + 8 * 1024) / 409600) < 1e-3
