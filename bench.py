@@ -590,7 +590,7 @@ def main():
     # the step's device time; its average launch duration from the isolated
     # back-to-back launches (in-step event intervals also count dispatch gaps)
     share = kern["attention"]["us_per_step"] / sum(v["us_per_step"] for v in kern.values())
-    roof = {"kernel": "attention (attn_decode_kernel)", "bound": "hbm", "achieved": round(att["gbs"], 1),
+    roof = {"kernel": "attention (attn_mfma_kernel)", "bound": "hbm", "achieved": round(att["gbs"], 1),
             "peak": rf.HBM_PEAK_GBS, "unit": "GB/s", "frac": round(att["gbs"] / rf.HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("attention_qwen05b_b32_ctx512"),
             "bytes_per_launch": att["bytes"], "avg_launch_us": round(att["us"], 3),

@@ -46,41 +46,26 @@ int elem_size(int32_t dtype) { return dtype == NS_BF16 ? 2 : 4; }
 // Attention launch shape for a batch of n_rows rows when sequences hold at
 // most cap_tokens tokens: partition size (tokens, a multiple of 64),
 // partitions per row, and wavefronts per work item (row, KV head,
-// partition).  Each wavefront takes 64-token passes, and a pass is mostly
-// memory latency (about 2 us: block ids, then K/V, then the math), so a
-// launch costs roughly the larger of 2 us per pass of its busiest wavefront
-// and the cache bytes at the HBM rate, scaled down while fewer than about
-// 1024 wavefronts are in flight; splitting the context adds the combine
-// launch (about 3 us, a little more per partition).  The cheapest (waves,
-// partitions) wins, ties going to fewer wavefronts and partitions.  The shape
-// depends only on the whole batch's row count and the capacity, so
+// partition).  A wavefront's 64-token pass costs about 1 us of memory
+// latency and the combine launch of a split context about 6 us, so:
+// 8 wavefronts per item while items are few (<= 256, at most 2048
+// wavefronts: more passes in flight per row), 4 up to 2047 items, 1 once
+// the items alone fill the chip; the context is split (in halves, repeatedly) only while a wavefront would take
+// more than 8 passes and the split items stay within 4096 wavefronts.  The
+// shape depends only on the whole batch's row count and the capacity, so
 // nano-batched and unsplit steps, eager and captured, compute identically.
-// (Fitted to timings of this kernel on MI355X over batch 1..512, contexts
-// 128..2048, head_dim 64 and 128.)
-void attn_partition(int n_rows, int nkv, int cap_tokens, int head_dim, int elem_bytes, int* part_tokens,
-                    int* n_parts, int* waves) {
+// (Fitted to timings of the matrix-core kernel on MI355X: batch 1..512,
+// contexts 128..2048, head_dim 64 with 7 query heads per KV head and 128
+// with 8.)
+void attn_partition(int n_rows, int nkv, int cap_tokens, int* part_tokens, int* n_parts, int* waves) {
   const int chunks = std::max(1, (cap_tokens + 63) / 64);
   const long items = std::max(1L, (long)n_rows * nkv);
-  const double bytes = (double)items * 64.0 * chunks * head_dim * 2 * elem_bytes;  // K and V
-  double best = 1e30;
-  int best_w = 1, best_p = 1;
-  for (int w : {1, 4}) {
-    for (int parts = 1; parts <= chunks; parts *= 2) {
-      const int per = (chunks + parts - 1) / parts;
-      const int np = (chunks + per - 1) / per;
-      const double passes = std::ceil((double)per / w);
-      const double in_flight = (double)items * np * w;
-      const double mem_us = bytes / (8.0e6 * std::min(1.0, in_flight / 1024.0));
-      const double cost = std::max(2.0 * passes, mem_us) + (np > 1 ? 3.0 + 0.25 * np : 0.0);
-      if (cost < best - 1e-9) {
-        best = cost;
-        best_w = w;
-        best_p = parts;
-      }
-    }
-  }
-  const int per = (chunks + best_p - 1) / best_p;
-  *waves = best_w;
+  const int w = items >= 2048 ? 1 : (items <= 256 ? 8 : 4);
+  int parts = 1;
+  auto passes = [&](int p) { return ((chunks + p - 1) / p + w - 1) / w; };
+  while (parts < chunks && passes(parts) > 8 && items * parts * 2 * w <= 4096) parts *= 2;
+  const int per = (chunks + parts - 1) / parts;
+  *waves = w;
   *part_tokens = 64 * per;
   *n_parts = (chunks + per - 1) / per;
 }
@@ -114,7 +99,7 @@ Plan make_plan(const ns_model_desc* d, int T, int maxb) {
   long items = 0;
   for (int n = 1; n <= T; ++n) {
     int P, np, nw;
-    attn_partition(n, d->n_kv_heads, maxb * NS_BLOCK_SIZE, d->head_dim, (int)es, &P, &np, &nw);
+    attn_partition(n, d->n_kv_heads, maxb * NS_BLOCK_SIZE, &P, &np, &nw);
     if (np > 1) items = std::max(items, (long)n * d->n_kv_heads * np);
   }
   p.part_acc = take((size_t)items * G * d->head_dim * 4);
@@ -320,7 +305,7 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
   a->nq = e->d.n_q_heads;
   a->nkv = e->d.n_kv_heads;
   a->d = e->d.head_dim;
-  attn_partition(n_tok, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, e->d.head_dim, (int)e->es, &a->part_tokens,
+  attn_partition(n_tok, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, &a->part_tokens,
                  &a->n_parts, &a->waves);
   a->wg_cap = e->sched.attn_wg_cap;
   a->row_seq = e->sched.prefill_tiles ? e->m_seq() : nullptr;
@@ -829,8 +814,7 @@ int ns_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols, void*
 size_t ns_op_attention_ws_bytes(const ns_model_desc* desc, int32_t n_rows, int32_t max_blocks_per_seq) {
   if (ns::check_desc(desc) != NS_OK || n_rows <= 0 || max_blocks_per_seq <= 0) return 0;
   int P, np, nw;
-  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, desc->head_dim,
-                 elem_size(desc->dtype), &P, &np, &nw);
+  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &P, &np, &nw);
   const int G = desc->n_q_heads / desc->n_kv_heads;
   const size_t items = (size_t)n_rows * desc->n_kv_heads * np;
   return align_up(items * G * desc->head_dim * 4, 256) + align_up(items * G * 2 * 4, 256);
@@ -866,8 +850,8 @@ int op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, c
   a.nq = desc->n_q_heads;
   a.nkv = desc->n_kv_heads;
   a.d = desc->head_dim;
-  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, desc->head_dim,
-                 elem_size(desc->dtype), &a.part_tokens, &a.n_parts, &a.waves);
+  attn_partition(n_rows, desc->n_kv_heads, max_blocks_per_seq * NS_BLOCK_SIZE, &a.part_tokens, &a.n_parts,
+                 &a.waves);
   const int G2 = G;
   const size_t items = (size_t)n_rows * desc->n_kv_heads * a.n_parts;
   a.part_acc = (float*)ws;

@@ -1,4 +1,4 @@
-// Paged grouped-query decode attention for gfx950 (vector ALU; HBM-bound).
+// Paged grouped-query decode attention for gfx950 (HBM-bound).
 //
 // What it computes (nanoserve notes, changes table: GQA with no expanded K/V
 // copy, paged cache through block tables; NanoFlow review, operator table:
@@ -6,29 +6,39 @@
 // position pos of a sequence), each query head h attends with scale 1/sqrt(d)
 // over keys 0..pos of its sequence, reading KV head h / G.
 //
-// Design (MI355X-first):
-//  * one workgroup of 1 or 4 wavefronts per work item (row, KV head,
-//    partition of the context): 4 when there are few items (small batches),
-//    1 when items alone fill the chip; the wavefronts take interleaved
-//    64-token passes and each
-//    K/V block of the KV head is streamed exactly once for all G query heads
-//    of the group, so the HBM traffic is the cache bytes themselves;
-//  * QK: lane = token (64 tokens = 4 blocks per pass).  The K cache stores
-//    each block as 16-byte chunks interleaved over its 16 tokens, so for every
-//    chunk the 16 lanes of a block read 256 contiguous bytes.  The q values
-//    are wavefront-uniform (all lanes need the same q), loaded through the
-//    scalar cache, and each K pair feeds v_dot2_f32_bf16 for every head of
-//    the group;
-//  * online softmax in the log2 domain with wavefront max/sum reductions;
-//  * PV: lane = (token lane j, 16-byte chunk c of the head dim): each lane
-//    accumulates G x E outputs of its chunk over the tokens j, j+TL, ...;
-//    V rows are read 16 bytes per lane, a whole block row per 64/TL lanes;
-//  * all K and V loads of a pass are issued before any arithmetic, so each
-//    wavefront keeps 2 x 64 tokens of KV in flight;
-//  * the wavefronts of a workgroup merge their (max, sum, accumulator)
-//    triples in LDS; split context partitions (a multiple of 64 tokens, for
-//    long contexts with few rows) write partials that a combine kernel merges
-//    the same way.  A row that fits one partition writes its output directly.
+// Work decomposition (both kernels): a work item is (row, KV head, partition
+// of the context); a workgroup of 1 or 4 wavefronts owns one: 4 when there
+// are few items (small batches), 1 when items alone fill the chip.  The
+// wavefronts take interleaved 64-token passes (4 blocks), each K/V block of
+// the KV head is streamed exactly once for all G query heads of the group, so
+// the HBM traffic is the cache bytes themselves.  The wavefronts of a
+// workgroup merge their (max, sum, accumulator) triples in LDS; split context
+// partitions (a multiple of 64 tokens, for long contexts with few rows) write
+// partials that a combine kernel merges the same way.  A row that fits one
+// partition writes its output directly.
+//
+// bf16 cache: matrix cores (attn_mfma_kernel).  V is stored transposed within
+// each block ([block][nkv][d][16 tokens]), so the 8 consecutive tokens of one
+// head-dim element that an MFMA operand needs are one 16-byte load.  Per pass:
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: four tiles of 16 tokens x 16
+//    columns (the G query heads, zero-padded), d deep.  Row r of tile (s, u)
+//    is token 32 s + 8 (r / 4) + 4 u + r % 4, which leaves lane l (column =
+//    head l % 16) holding the scores of tokens 32 s + 8 (l / 16) + 0..7 of its
+//    head: exactly its k slots of the PV step s, so P never crosses lanes;
+//  * online softmax in the log2 domain, per head: one max and one sum over
+//    the four lanes of a head (l, l ^ 16, l ^ 32, l ^ 48) per pass;
+//  * O^T += V^T P^T on the same MFMA over 32 tokens per step, with P as a
+//    pair of bf16 terms (the value rounded, then its residual: about 16
+//    significant bits) and V^T fragments loaded straight from the cache.
+//
+// fp32 cache: vector ALU (attn_decode_kernel).  QK with lane = token (the K
+// cache interleaves 16-byte chunks over a block's 16 tokens, so for every
+// chunk the 16 lanes of a block read 256 contiguous bytes; q is wavefront-
+// uniform, read through the scalar cache); PV with lane = (token lane j,
+// 16-byte chunk c of the head dim) over V token rows; all K and V loads of a
+// pass are issued before any arithmetic.
+#include <type_traits>
+
 #include "ns_kernels.h"
 
 namespace ns {
@@ -44,22 +54,6 @@ struct AttnTraits {
   static_assert(TL <= 16, "PV token lanes must stay inside one block per iteration");
 };
 
-__device__ __forceinline__ float dot2(uint32_t q, uint32_t k, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q), __builtin_bit_cast(bf16x2_t, k), acc,
-                                         false);
-}
-// The vector elements are copied to scalars before the bit casts: with this
-// compiler, bit-casting q.y etc. of a vector read through a reference
-// silently yields q.x.
-__device__ __forceinline__ float dot_chunk(const u32x4_t& q, const u32x4_t& k, float acc, bf16_t) {
-  const uint32_t q0 = q.x, q1 = q.y, q2 = q.z, q3 = q.w;
-  const uint32_t k0 = k.x, k1 = k.y, k2 = k.z, k3 = k.w;
-  acc = dot2(q0, k0, acc);
-  acc = dot2(q1, k1, acc);
-  acc = dot2(q2, k2, acc);
-  acc = dot2(q3, k3, acc);
-  return acc;
-}
 __device__ __forceinline__ float dot_chunk(const u32x4_t& q, const u32x4_t& k, float acc, float) {
   acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
   acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
@@ -69,12 +63,6 @@ __device__ __forceinline__ float dot_chunk(const u32x4_t& q, const u32x4_t& k, f
 }
 
 // Unpack one 16-byte chunk into floats.
-__device__ __forceinline__ void unpack_chunk(const u32x4_t& v, float* f, bf16_t) {
-  f[0] = lo_bf16(v.x); f[1] = hi_bf16(v.x);
-  f[2] = lo_bf16(v.y); f[3] = hi_bf16(v.y);
-  f[4] = lo_bf16(v.z); f[5] = hi_bf16(v.z);
-  f[6] = lo_bf16(v.w); f[7] = hi_bf16(v.w);
-}
 __device__ __forceinline__ void unpack_chunk(const u32x4_t& v, float* f, float) {
   f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
   f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
@@ -332,6 +320,262 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ bf16 on matrix cores
+namespace {
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Registers of one 64-token pass: K fragments of QK tile (s, u) for each
+// k-step over d, and V^T fragments of PV step s for each 16-row d tile.
+template <int D>
+struct MfmaPass {
+  bf16x8_t k[2][2][D / 32];
+  u32x4_t v[D / 16][2];
+};
+
+// Issue every load of the pass starting at token c0 (c0 < end).  Blocks past
+// the context end are read as the pass's first block (written, in range);
+// their tokens are masked.
+template <int D>
+__device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restrict__ kc,
+                                           const bf16_t* __restrict__ vc, const int32_t* __restrict__ bt, int g,
+                                           int nkv, int c0, int end, int hc, int grp) {
+  constexpr long HEAD_BLK = 16L * D;
+  int blk[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) blk[b] = bt[(c0 + 16 * b < end) ? (c0 >> 4) + b : (c0 >> 4)];
+  // QK tile (s, u), A row hc: token 32 s + 8 (hc / 4) + 4 u + hc % 4, i.e.
+  // block 2 s + hc / 8, slot 8 ((hc / 4) % 2) + 4 u + hc % 4; k-step j reads
+  // the 16-byte chunk 4 j + grp of that token's K row.
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int b = (hc >> 3) ? blk[2 * s + 1] : blk[2 * s];
+    const bf16_t* kb = kc + ((long)b * nkv + g) * HEAD_BLK;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int slot = 8 * ((hc >> 2) & 1) + 4 * u + (hc & 3);
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j)
+        r.k[s][u][j] = *(const bf16x8_t*)(kb + ((long)(4 * j + grp) * 16 + slot) * 8);
+    }
+  }
+  // PV step s, d tile dt, A row hc: V^T row 16 dt + hc, tokens
+  // 32 s + 8 grp + 0..7 = block 2 s + grp / 2, slots 8 (grp % 2) + 0..7.
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int b = (grp >> 1) ? blk[2 * s + 1] : blk[2 * s];
+    const bf16_t* vb = vc + ((long)b * nkv + g) * HEAD_BLK + 8 * (grp & 1);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) r.v[dt][s] = *(const u32x4_t*)(vb + (long)(16 * dt + hc) * 16);
+  }
+}
+
+// The math of the pass at c0: scores, online softmax update of (m, l, acc).
+template <int D>
+__device__ __forceinline__ void mfma_compute(MfmaPass<D>& r, const bf16x8_t (&qf)[D / 32], f32x4_t (&acc)[D / 16],
+                                             float& m, float& l, int c0, int end, int grp, float scale_log2) {
+  const bool full = c0 + 64 <= end;
+  float sv[2][2][4];
+  float bm = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[s][u][j], qf[j], st, 0, 0, 0);
+      // element e: token c0 + 32 s + 8 grp + 4 u + e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = st[e] * scale_log2;
+        if (!full && c0 + 32 * s + 8 * grp + 4 * u + e >= end) x = -INFINITY;  // also drops unwritten slots
+        sv[s][u][e] = x;
+        bm = fmaxf(bm, x);
+      }
+    }
+  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+  const float mn = fmaxf(m, bm);  // finite: token c0 is in range
+  const float alpha = exp2f(m - mn);
+  m = mn;
+  l *= alpha;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
+  if (!full) {  // V of tokens past the end (possibly unwritten) must not meet P = 0 as NaN
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int nv = end - (c0 + 32 * s + 8 * grp);  // valid leading tokens of this lane's 8
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t mk = nv >= 2 * w + 2 ? 0xffffffffu : (nv == 2 * w + 1 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) r.v[dt][s][w] &= mk;
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    // k slots 8 grp + 0..7: tile (s, 0) elements 0..3, then tile (s, 1).  P
+    // enters as a bf16 pair hi + lo (lo = the rounding residual, so hi + lo
+    // carries about 16 significant bits) against the exact bf16 V.
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = exp2f(sv[s][w >> 1][2 * (w & 1)] - mn), p1 = exp2f(sv[s][w >> 1][2 * (w & 1) + 1] - mn);
+      ph[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t));  // RNE
+      const f32x2_t r = {p0 - lo_bf16(ph[w]), p1 - hi_bf16(ph[w])};
+      pl[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+      l += p0 + p1;
+    }
+    const bf16x8_t pbh = __builtin_bit_cast(bf16x8_t, (u32x4_t){ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8_t pbl = __builtin_bit_cast(bf16x8_t, (u32x4_t){pl[0], pl[1], pl[2], pl[3]});
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const bf16x8_t vt = __builtin_bit_cast(bf16x8_t, r.v[dt][s]);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pbh, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pbl, acc[dt], 0, 0, 0);
+    }
+  }
+}
+
+}  // namespace
+
+// Lane l of a wavefront: head column hc = l % 16 (heads >= G are zero
+// padding whose results are dropped), lane group grp = l / 16.  Arguments as
+// attn_decode_kernel.
+template <int D, int G, int NWAVE>
+__global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
+    const bf16_t* __restrict__ qatt, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    const int32_t* __restrict__ row_bseq, const int32_t* __restrict__ row_pos, const int32_t* __restrict__ btab,
+    bf16_t* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml, int maxb, int row0,
+    int n_rows, int nq, int nkv, int P, int n_parts, float scale_log2, const int32_t* __restrict__ skip_seq) {
+  static_assert(G <= 16 && D % 32 == 0, "heads must fit the 16 MFMA columns, d whole k-steps");
+  constexpr int NCH = D / 8;  // 16-byte chunks per head row
+  constexpr int KS = D / 32, DT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hc = lane & 15, grp = lane >> 4;
+  const int total = n_rows * nkv * n_parts;
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int part = w % n_parts;
+    const int rest = w / n_parts;
+    const int g = rest % nkv;
+    const int t = row0 + rest / nkv;
+    if (skip_seq) {  // rows of prefill tiles belong to the prefill kernel
+      const int t0 = row0 + ((t - row0) & ~31);
+      if (t0 + 32 <= row0 + n_rows && prefill_tile(skip_seq, row_pos, t0, lane)) continue;
+    }
+    const int32_t* __restrict__ bt;
+    bool pad;
+    if (row_bseq) {
+      const int bs = row_bseq[t];
+      pad = bs < 0;
+      bt = btab + (long)(pad ? 0 : bs) * maxb;
+    } else {
+      bt = btab + (long)t * maxb;
+      pad = bt[0] < 0;
+    }
+    bf16_t* outp = out + (long)t * nq * D + (long)g * G * D;
+    if (pad) {  // padding row: zero output
+      if (part == 0)
+        for (int i = threadIdx.x; i < G * D; i += 64 * NWAVE) outp[i] = 0;
+      continue;
+    }
+    const int ctx = row_pos[t] + 1;
+    const int start = part * P;
+    if (start >= ctx) continue;
+    const int end = min(start + P, ctx);
+    const int nparts_row = (ctx + P - 1) / P;
+
+    // Q^T fragments (B operand of QK): head hc, d chunk 4 j + grp
+    bf16x8_t qf[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      u32x4_t q = *(const u32x4_t*)(qatt + ((((long)t * nkv + g) * NCH + 4 * j + grp) * G + (hc < G ? hc : 0)) * 8);
+      if (hc >= G) q = (u32x4_t){0u, 0u, 0u, 0u};
+      qf[j] = __builtin_bit_cast(bf16x8_t, q);
+    }
+    float m = -INFINITY, l = 0.f;
+    f32x4_t acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = start + 64 * wave; c0 < end; c0 += 64 * NWAVE) {
+      MfmaPass<D> pr;
+      mfma_issue<D>(pr, kc, vc, bt, g, nkv, c0, end, hc, grp);
+      mfma_compute<D>(pr, qf, acc, m, l, c0, end, grp, scale_log2);
+    }
+    // the four lanes of a head hold disjoint tokens: sum their denominators
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+
+    // lane (hc, grp) owns O^T rows 16 dt + 4 grp + 0..3 of head hc
+    const long item = ((long)t * nkv + g) * n_parts + part;
+    if constexpr (NWAVE == 1) {
+      if (hc < G) {
+        if (nparts_row == 1) {
+          const float inv = 1.f / l;
+          bf16_t* op = outp + (long)hc * D + 4 * grp;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            uint2 o2;
+            o2.x = pack_bf16(acc[dt][0] * inv, acc[dt][1] * inv);
+            o2.y = pack_bf16(acc[dt][2] * inv, acc[dt][3] * inv);
+            *(uint2*)(op + 16 * dt) = o2;
+          }
+        } else {
+          float* pa = part_acc + (item * G + hc) * D + 4 * grp;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) *(f32x4_t*)(pa + 16 * dt) = acc[dt];
+          if (grp == 0) {
+            part_ml[(item * G + hc) * 2] = m;
+            part_ml[(item * G + hc) * 2 + 1] = l;
+          }
+        }
+      }
+    } else {
+      // Merge the wavefronts: M = max m_w, L = sum l_w 2^(m_w - M),
+      // acc = sum acc_w 2^(m_w - M), in wavefront order.  A wavefront that
+      // had no pass contributes m = -inf, l = 0, acc = 0 (weight 0).
+      __shared__ float macc[NWAVE][G][D];
+      __shared__ float mml[NWAVE][G][2];
+      if (hc < G) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4_t*)&macc[wave][hc][16 * dt + 4 * grp] = acc[dt];
+        if (grp == 0) {
+          mml[wave][hc][0] = m;
+          mml[wave][hc][1] = l;
+        }
+      }
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < G * D; idx += 64 * NWAVE) {
+        const int h = idx / D, dd = idx % D;
+        float M = mml[0][h][0];
+#pragma unroll
+        for (int v = 1; v < NWAVE; ++v) M = fmaxf(M, mml[v][h][0]);
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int v = 0; v < NWAVE; ++v) {
+          const float wgt = exp2f(mml[v][h][0] - M);
+          L += mml[v][h][1] * wgt;
+          o += macc[v][h][dd] * wgt;
+        }
+        if (nparts_row == 1) {
+          outp[(long)h * D + dd] = f32_to_bf16(o / L);
+        } else {
+          part_acc[item * G * D + idx] = o;
+          if (dd == 0) {
+            part_ml[(item * G + h) * 2] = M;
+            part_ml[(item * G + h) * 2 + 1] = L;
+          }
+        }
+      }
+      __syncthreads();  // the LDS is reused by the next work item
+    }
+  }
+}
+
 template <typename T, int D, int G>
 static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
   AttnArgs a = a0;
@@ -341,14 +585,23 @@ static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
   long grid = total;
   if (a.wg_cap > 0 && grid > a.wg_cap) grid = a.wg_cap;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-#define NS_ATTN_LAUNCH(NW)                                                                                         \
-  hipLaunchKernelGGL((attn_decode_kernel<T, D, G, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st,               \
-                     (const T*)a.q_att, (const T*)a.kc, (const T*)a.vc, a.row_bseq, a.row_pos, a.btab, (T*)a.out, \
-                     a.part_acc, a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts,      \
-                     scale_log2, a.row_seq)
-  if (a.waves == 1) NS_ATTN_LAUNCH(1);
-  else NS_ATTN_LAUNCH(4);
-#undef NS_ATTN_LAUNCH
+#define NS_ATTN_ARGS                                                                                             \
+  (const T*)a.q_att, (const T*)a.kc, (const T*)a.vc, a.row_bseq, a.row_pos, a.btab, (T*)a.out, a.part_acc,       \
+      a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts, scale_log2, a.row_seq
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (a.waves == 1)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS);
+    else if (a.waves == 8)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS);
+  } else {
+    if (a.waves == 1)
+      hipLaunchKernelGGL((attn_decode_kernel<T, D, G, 1>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS);
+    else
+      hipLaunchKernelGGL((attn_decode_kernel<T, D, G, 4>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS);
+  }
+#undef NS_ATTN_ARGS
   if (a.n_parts > 1)
     hipLaunchKernelGGL((attn_combine_kernel<T, D, G>), dim3((unsigned)(a.n_rows * a.nkv)), dim3(256), 0, st, a);
   if (a.row_seq) launch_attention_prefill(a, st);

@@ -258,6 +258,15 @@ void launch_argmax_rows(const float* logits, int n_rows, int V, int32_t* out, hi
 }
 
 // ---------------------------------------------------------------- RoPE + KV write
+// Element j of head g's V at slot tok of block blk: fp32 caches keep token
+// rows ([blk][nkv][16][d]); bf16 caches store each block transposed
+// ([blk][nkv][d][16]) for the matrix-core attention kernel.
+template <typename T>
+__device__ __forceinline__ long v_index(long blk, int g, int tok, int j, int nkv, int d) {
+  if constexpr (sizeof(T) == 2) return ((blk * nkv + g) * d + j) * (long)NS_BLOCK + tok;
+  return ((blk * nkv + g) * NS_BLOCK + tok) * (long)d + j;
+}
+
 // From the QKV projection (fp32 [T, (nq + 2 nkv) d]) for one row per
 // workgroup: rotate-half RoPE on q and k with the step's table, store q in
 // the attention layout [T][nkv][d/E][G][E] (the G query heads of one KV head
@@ -322,7 +331,12 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ 
       float y[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) y[e] = rowbuf[(nq + nkv) * d + g * d + c * E + e];
-      Chunk<T>::store(vc + ((blk * nkv + g) * NS_BLOCK + tok) * (long)d + c * E, y);
+      if constexpr (sizeof(T) == 2) {  // bf16: V^T within the block, one element per head-dim row
+#pragma unroll
+        for (int e = 0; e < E; ++e) Elem<T>::store(vc, v_index<T>(blk, g, tok, c * E + e, nkv, d), y[e]);
+      } else {
+        Chunk<T>::store(vc + v_index<T>(blk, g, tok, c * E, nkv, d), y);
+      }
     }
   }
 }
@@ -343,7 +357,7 @@ __global__ void __launch_bounds__(256) kv_scatter_kernel(const int32_t* __restri
   for (int e = threadIdx.x; e < nkv * d; e += 256) {
     const int g = e / d, j = e % d;
     kc[((blk * nkv + g) * nch + j / E) * (long)NS_BLOCK * E + (long)tok * E + j % E] = k[(long)i * nkv * d + e];
-    vc[((blk * nkv + g) * NS_BLOCK + tok) * (long)d + j] = v[(long)i * nkv * d + e];
+    vc[v_index<T>(blk, g, tok, j, nkv, d)] = v[(long)i * nkv * d + e];
   }
 }
 
@@ -365,7 +379,7 @@ __global__ void __launch_bounds__(256) kv_gather_kernel(const int32_t* __restric
     const int tok = s % NS_BLOCK;
     const int g = e / d, j = e % d;
     k[(long)i * nkv * d + e] = kc[((blk * nkv + g) * nch + j / E) * (long)NS_BLOCK * E + (long)tok * E + j % E];
-    v[(long)i * nkv * d + e] = vc[((blk * nkv + g) * NS_BLOCK + tok) * (long)d + j];
+    v[(long)i * nkv * d + e] = vc[v_index<T>(blk, g, tok, j, nkv, d)];
   }
 }
 

@@ -18,8 +18,8 @@
 //                 as fp16 (exact for bf16 values in fp16 range) and P goes
 //                 to fp16 (11 significant bits); the softmax denominator sums
 //                 the same rounded P, so the weights of every row sum to 1.
-// Keys past the tile's last position are read at that position (written,
-// finite) and masked.
+// K of keys past the tile's last position is read at that position
+// (written, finite) and masked; their V is zeroed.
 #include "ns_kernels.h"
 
 namespace ns {
@@ -28,11 +28,6 @@ namespace {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  const f16x2_t v = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 }  // namespace
 
@@ -77,17 +72,23 @@ __global__ void __launch_bounds__(64 * G) attn_prefill_kernel(
   for (int kb = 0; kb < nkb; ++kb) {
     const int k0 = 32 * kb;
     _Float16(*vb)[VP] = vt[kb & 1];
-    // stage V^T of keys k0 .. k0+31 (fp16) in LDS
-    for (int it = threadIdx.x; it < 32 * NCH; it += 64 * G) {
-      const int key = it / NCH, c = it % NCH;
-      const int kk = min(k0 + key, last);
-      const uint4 w = *(const uint4*)(vc + ((long)bt[kk >> 4] * nkv + g) * HEAD_BLK + (long)(kk & 15) * D + c * 8);
+    // stage V^T of keys k0 .. k0+31 (fp16) in LDS: the cache holds each
+    // block transposed, so a head-dim row's 8 keys are one 16-byte load;
+    // keys past the tile's last position are zeroed (they may be unwritten)
+    for (int it = threadIdx.x; it < 4 * D; it += 64 * G) {
+      const int dd = it >> 2, kg = it & 3;
+      const int key0 = k0 + 8 * kg;
+      const int kr = min(key0, last);
+      const uint4 w = *(const uint4*)(vc + ((long)bt[kr >> 4] * nkv + g) * HEAD_BLK + (long)dd * 16 + (kr & 8));
+      const int nvalid = last - key0 + 1;
       const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+      f16x8_t h;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        vb[8 * c + 2 * i][key] = (_Float16)lo_bf16(wv[i]);
-        vb[8 * c + 2 * i + 1][key] = (_Float16)hi_bf16(wv[i]);
+        h[2 * i] = 2 * i < nvalid ? (_Float16)lo_bf16(wv[i]) : (_Float16)0.f;
+        h[2 * i + 1] = 2 * i + 1 < nvalid ? (_Float16)hi_bf16(wv[i]) : (_Float16)0.f;
       }
+      *(f16x8_t*)&vb[dd][8 * kg] = h;
     }
     // K fragments (A operand): key k0 + q, d chunk 2 s + hl
     const int kk = min(k0 + q, last);

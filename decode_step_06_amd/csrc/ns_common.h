@@ -108,7 +108,6 @@ __device__ __forceinline__ f32x4_t slice_sum4(const float* p, long slice_stride,
   }
 }
 
-// Wavefront (64-lane) reductions.
 // Step rows t0 .. t0+31 form a prefill tile: one sequence (row_seq >= 0) at
 // consecutive positions.  Lanes i and i + 32 both check row t0 + i; the
 // result is uniform over the wavefront.  The caller ensures the 32 rows exist.
@@ -120,6 +119,7 @@ __device__ __forceinline__ bool prefill_tile(const int32_t* __restrict__ row_seq
   return __all(ok);
 }
 
+// Wavefront (64-lane) reductions.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -86,7 +86,7 @@ struct AttnArgs {
   int nq, nkv, d;
   int part_tokens;          // P, multiple of 64
   int n_parts;              // partitions per row (max)
-  int waves;                // wavefronts per work item: 1 or 4
+  int waves;                // wavefronts per work item: 1, 4 or 8 (fp32: 8 runs as 4)
   int wg_cap;               // 0 = one workgroup per work item
   const int32_t* row_seq;   // [T] sequence of each row (-1: padding), or null: no prefill tiles
 };

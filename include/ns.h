@@ -119,7 +119,9 @@ typedef struct {
  *   K: [num_blocks][nkv][d / E][16][E]  (16-byte chunks of a block's 16
  *      tokens interleaved, so one wavefront reads a whole block's chunk
  *      contiguously);
- *   V: [num_blocks][nkv][16][d]         (token rows).
+ *   V, fp32: [num_blocks][nkv][16][d]   (token rows);
+ *   V, bf16: [num_blocks][nkv][d][16]   (each block transposed, so the 16
+ *      tokens of one head-dim element are 32 contiguous bytes).
  * Slot s lives in block s / 16 at row s % 16. */
 typedef struct ns_kv ns_kv;
 

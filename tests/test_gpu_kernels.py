@@ -146,6 +146,7 @@ def _attn_setup(shape: ModelShape, ctx, seed, shuffle=True, nan_poison=True):
     # physical layout (documented in ns.h), built on the host: unused slots NaN
     fill = float("nan") if nan_poison else 0.0
     kphys = torch.full((nb, nkv, d // E, 16, E), fill, dtype=dt)
+    # V: token rows for fp32, each block transposed ([d][16]) for bf16
     vphys = torch.full((nb, nkv, 16, d), fill, dtype=dt)
     K, V = {}, {}
     for s, c in enumerate(ctx):
@@ -156,6 +157,8 @@ def _attn_setup(shape: ModelShape, ctx, seed, shuffle=True, nan_poison=True):
             blk, tok = int(btab[s, p // 16]), p % 16
             kphys[blk, :, :, tok, :] = kk[p].reshape(nkv, d // E, E)
             vphys[blk, :, tok, :] = vv[p]
+    if shape.dtype == "bf16":
+        vphys = vphys.transpose(2, 3).contiguous()
     kv = torch.cat([kphys.reshape(-1).view(torch.uint8), vphys.reshape(-1).view(torch.uint8)]).cuda()
     assert kv.numel() == kvb
     q = torch.from_numpy(rng.standard_normal((S, shape.n_q_heads, d)).astype(np.float32)).to(dt)
@@ -225,3 +228,22 @@ def test_attention_workgroup_cap_is_bit_exact():
     a = _attn_run(shape, st, ctx, wg_cap=0)
     b = _attn_run(shape, st, ctx, wg_cap=7)
     np.testing.assert_array_equal(a, b)
+
+
+# Launch shapes the engine picks from the batch: 8 wavefronts per work item
+# for few items, 4 for a few hundred, 1 once items fill the chip, and a split
+# context with the combine launch for a long context at a small batch.
+@pytest.mark.parametrize("shape_i,n_rows,ctx_hi", [(0, 300, 300), (0, 1100, 80), (0, 1, 9000), (1, 1, 4100)],
+                         ids=["qwen-300rows-4waves", "qwen-1100rows-1wave", "qwen-ctx9000-split",
+                              "llama-ctx4100-split"])
+def test_attention_launch_shapes_match_oracle(shape_i, n_rows, ctx_hi):
+    shape = ATTN_SHAPES[shape_i]
+    rng = np.random.default_rng(11 + n_rows)
+    ctx = [ctx_hi] if n_rows == 1 else [int(c) for c in rng.integers(1, ctx_hi + 1, n_rows)]
+    say(f"attention launch shape {shape.name} rows={n_rows} ctx<={ctx_hi}")
+    st = _attn_setup(shape, ctx, seed=5)
+    got = _attn_run(shape, st, ctx)
+    for s, c in enumerate(ctx):
+        ref, _ = od.attention_row(st["q"][s].double().numpy(), st["K"][s].double().numpy(),
+                                  st["V"][s].double().numpy(), shape.group)
+        assert rel_l2(got[s], ref) < 4e-3, (s, c, rel_l2(got[s], ref))   # output stored in bf16

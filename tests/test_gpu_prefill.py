@@ -46,6 +46,7 @@ def _run(shape, ctx, rows, seed):
             blk, tok = int(btab[s, p // 16]), p % 16
             kphys[blk, :, :, tok, :] = kk[p].reshape(nkv, d // E, E)
             vphys[blk, :, tok, :] = vv[p]
+    vphys = vphys.transpose(2, 3).contiguous()  # bf16 cache: each V block stored [d][16]
     kv = torch.cat([kphys.reshape(-1).view(torch.uint8), vphys.reshape(-1).view(torch.uint8)]).cuda()
     n = len(rows)
     q = torch.from_numpy(rng.standard_normal((n, shape.n_q_heads, d)).astype(np.float32)).to(torch.bfloat16)
