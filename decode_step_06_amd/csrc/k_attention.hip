@@ -333,23 +333,38 @@ struct MfmaPass {
   u32x4_t v[D / 16][2];
 };
 
-// Issue every load of the pass starting at token c0 (c0 < end).  Blocks past
-// the context end are read as the pass's first block (written, in range);
-// their tokens are masked.
+// Issue every K and V load of the pass (tokens past the context end are
+// masked by the math).
+// Block ids of the pass's 4 blocks, wave-uniform scalars (never an indexed
+// array: a lane-dependent pick between two entries of one made the compiler
+// keep the array in LDS, a store and a load between the block ids and every
+// K/V address).
+struct Blk4 {
+  int b[4];
+};
+
+// The block ids of the pass at c0 (c0 < end); blocks past the context end
+// are read as the pass's first block (written, in range).
+__device__ __forceinline__ Blk4 pass_blocks(const int32_t* __restrict__ bt, int c0, int end) {
+  Blk4 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    r.b[b] = __builtin_amdgcn_readfirstlane(bt[(c0 + 16 * b < end) ? (c0 >> 4) + b : (c0 >> 4)]);
+  return r;
+}
+
 template <int D>
 __device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restrict__ kc,
-                                           const bf16_t* __restrict__ vc, const int32_t* __restrict__ bt, int g,
-                                           int nkv, int c0, int end, int hc, int grp) {
+                                           const bf16_t* __restrict__ vc, const Blk4& blk, int g, int nkv, int hc,
+                                           int grp) {
   constexpr long HEAD_BLK = 16L * D;
-  int blk[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) blk[b] = bt[(c0 + 16 * b < end) ? (c0 >> 4) + b : (c0 >> 4)];
+  const int b0 = blk.b[0], b1 = blk.b[1], b2 = blk.b[2], b3 = blk.b[3];
   // QK tile (s, u), A row hc: token 32 s + 8 (hc / 4) + 4 u + hc % 4, i.e.
   // block 2 s + hc / 8, slot 8 ((hc / 4) % 2) + 4 u + hc % 4; k-step j reads
   // the 16-byte chunk 4 j + grp of that token's K row.
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int b = (hc >> 3) ? blk[2 * s + 1] : blk[2 * s];
+    const int b = (hc >> 3) ? (s ? b3 : b1) : (s ? b2 : b0);
     const bf16_t* kb = kc + ((long)b * nkv + g) * HEAD_BLK;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -363,7 +378,7 @@ __device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restr
   // 32 s + 8 grp + 0..7 = block 2 s + grp / 2, slots 8 (grp % 2) + 0..7.
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int b = (grp >> 1) ? blk[2 * s + 1] : blk[2 * s];
+    const int b = (grp >> 1) ? (s ? b3 : b1) : (s ? b2 : b0);
     const bf16_t* vb = vc + ((long)b * nkv + g) * HEAD_BLK + 8 * (grp & 1);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) r.v[dt][s] = *(const u32x4_t*)(vb + (long)(16 * dt + hc) * 16);
@@ -476,6 +491,15 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
       bt = btab + (long)t * maxb;
       pad = bt[0] < 0;
     }
+    // The first pass's block ids, read before the context length is known
+    // (indices clamped into the row) so that they arrive with it; the empty
+    // asm keeps the loads ahead of the branches below.
+    const int cf = part * P + 64 * wave;
+    const int f0 = __builtin_amdgcn_readfirstlane(bt[min((cf >> 4), maxb - 1)]);
+    const int f1 = __builtin_amdgcn_readfirstlane(bt[min((cf >> 4) + 1, maxb - 1)]);
+    const int f2 = __builtin_amdgcn_readfirstlane(bt[min((cf >> 4) + 2, maxb - 1)]);
+    const int f3 = __builtin_amdgcn_readfirstlane(bt[min((cf >> 4) + 3, maxb - 1)]);
+    asm volatile("" : : "s"(f0), "s"(f1), "s"(f2), "s"(f3));
     bf16_t* outp = out + (long)t * nq * D + (long)g * G * D;
     if (pad) {  // padding row: zero output
       if (part == 0)
@@ -501,9 +525,18 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = start + 64 * wave; c0 < end; c0 += 64 * NWAVE) {
+    // blocks past the context end are read as the pass's first block
+    Blk4 cur;
+    cur.b[0] = f0;
+    cur.b[1] = cf + 16 < end ? f1 : f0;
+    cur.b[2] = cf + 32 < end ? f2 : f0;
+    cur.b[3] = cf + 48 < end ? f3 : f0;
+    for (int c0 = cf; c0 < end; c0 += 64 * NWAVE) {
       MfmaPass<D> pr;
-      mfma_issue<D>(pr, kc, vc, bt, g, nkv, c0, end, hc, grp);
+      mfma_issue<D>(pr, kc, vc, cur, g, nkv, hc, grp);
+      // the next pass's block ids load while this pass's K/V are in flight
+      const int cn = c0 + 64 * NWAVE;
+      if (cn < end) cur = pass_blocks(bt, cn, end);
       mfma_compute<D>(pr, qf, acc, m, l, c0, end, grp, scale_log2);
     }
     // the four lanes of a head hold disjoint tokens: sum their denominators
