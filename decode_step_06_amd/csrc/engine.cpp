@@ -213,6 +213,7 @@ int check_sched(const ns_sched* s) {
   if (s->attn_wg_cap < 0) NS_FAIL(NS_EINVAL, "attn_wg_cap must be >= 0");
   if (s->cu_mask_frac < 0.f || s->cu_mask_frac > 1.f) NS_FAIL(NS_EINVAL, "cu_mask_frac must be in [0, 1]");
   if (s->prefill_tiles != 0 && s->prefill_tiles != 1) NS_FAIL(NS_EINVAL, "prefill_tiles must be 0 or 1");
+  if (s->decode_rows_first != 0 && s->decode_rows_first != 1) NS_FAIL(NS_EINVAL, "decode_rows_first must be 0 or 1");
   return NS_OK;
 }
 
@@ -379,7 +380,27 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   // dimension" is the row count; fp32 weights are row-major
   const int pk = dt == NS_DT_BF16 ? 1 : 0;
   auto wld = [&](int rows, int cols) { return pk ? rows : cols; };
+  // decode rows first (the dense batch's order): the first QKV part's long
+  // attention is queued after the other parts' and the O/MLP nano-batches
+  // run last-first, so the later rows' projections run beside it.  Attention
+  // part j reads only K/V written by parts <= j, all finished before QKV part
+  // j's event, so any launch order of the attention parts is valid.
+  const bool late_first = sc.decode_rows_first != 0 && nano.size() > 1;
+  const bool defer0 = sc.decode_rows_first != 0 && qparts.size() > 1;
+  int layer = 0;
+  auto attend = [&](size_t j) -> int {
+    const int r0 = qparts[j].first, n = qparts[j].second - r0;
+    ns::AttnArgs a;
+    attn_args(e, layer, r0, r0 + n, n_tok, &a);
+    if (overlap) HIP_TRY(hipStreamWaitEvent(sa, e->ev_qkv[j], 0));
+    ns::launch_attention(a, sa);
+    launches += a.n_parts > 1 ? 2 : 1;
+    MARK(K_ATTN);
+    if (overlap) HIP_TRY(hipEventRecord(e->ev_att[j], sa));
+    return NS_OK;
+  };
   for (int l = 0; l < d.n_layers; ++l) {
+    layer = l;
     for (size_t j = 0; j < qparts.size(); ++j) {
       const int r0 = qparts[j].first, n = qparts[j].second - r0;
       if (l > 0) {  // layer 0's norm ran in the prologue
@@ -406,18 +427,19 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
                          st);
       MARK(K_ROPE_KV);
       launches += 2;
-      ns::AttnArgs a;
-      attn_args(e, l, r0, r0 + n, n_tok, &a);
-      if (overlap) {
-        HIP_TRY(hipEventRecord(e->ev_qkv[j], st));
-        HIP_TRY(hipStreamWaitEvent(sa, e->ev_qkv[j], 0));
+      if (overlap) HIP_TRY(hipEventRecord(e->ev_qkv[j], st));
+      // the decode part's attention waits until the other parts' is queued
+      if (!(defer0 && j == 0)) {
+        int rc = attend(j);
+        if (rc) return rc;
       }
-      ns::launch_attention(a, sa);
-      launches += a.n_parts > 1 ? 2 : 1;
-      MARK(K_ATTN);
-      if (overlap) HIP_TRY(hipEventRecord(e->ev_att[j], sa));
     }
-    for (size_t i = 0; i < nano.size(); ++i) {
+    if (defer0) {
+      int rc = attend(0);
+      if (rc) return rc;
+    }
+    for (size_t ii = 0; ii < nano.size(); ++ii) {
+      const size_t i = late_first ? nano.size() - 1 - ii : ii;
       const int r0 = nano[i].first, r1 = nano[i].second, n = r1 - r0;
       if (overlap)
         for (size_t j = 0; j < qparts.size(); ++j)

@@ -187,7 +187,15 @@ int ns_slot_map(const ns_kv* kv, int32_t n_tok, const int32_t* seq, const int32_
  *     the pipeline fed") computed on matrix cores (fp16 probabilities);
  *     costs an extra launch and a per-row check, so leave it 0 for batches
  *     of decode rows only.  Captured graphs keep the value they were
- *     captured with. */
+ *     captured with.
+ *   decode_rows_first: 0 = nano-ops in row order; 1 = the batch holds its
+ *     decode rows (long cached contexts) first and prompt chunks after them
+ *     (NanoFlow review, "Runtime details that keep the pipeline fed"): the
+ *     first QKV part's attention is queued after the other parts' and the
+ *     O projection + MLP nano-batches run last-first, so the prompt rows'
+ *     projections run beside the decode rows' memory-bound attention
+ *     ("Nano-batching: manufacturing independence").  Results are
+ *     bit-identical either way. */
 typedef struct {
   int32_t n_nano;
   int32_t nano_rows[4];
@@ -197,6 +205,7 @@ typedef struct {
   int32_t attn_wg_cap;
   float cu_mask_frac;
   int32_t prefill_tiles;
+  int32_t decode_rows_first;
 } ns_sched;
 
 /* One step's rows.  token_ids (host, [n_tok]) for models with a vocabulary,

@@ -54,6 +54,13 @@ def test_llama70b_layer_dense_batch_sampled_rows(prefill_tiles):
         for i, s in enumerate(slots):
             kcache[s] = k[i]
             vcache[s] = v[i]
+        if prefill_tiles:
+            # decode rows' attention queued last, prompt nano-batch's projections
+            # first: the same work in another order, bit-exact
+            ns.ns_engine_set_sched(c.h.eng, ns.make_sched(nano_rows=w.nano_splits, qkv_rows=(512,) * w.qkv_splits,
+                                                          overlap=True, prefill_tiles=True, decode_rows_first=True))
+            c.reset_cache()
+            np.testing.assert_array_equal(c.step().cpu().numpy(), got)
         rows = np.array(SAMPLE_ROWS)
         o = np.zeros((len(rows), shape.n_q_heads, shape.head_dim))
         for j, t in enumerate(rows):

@@ -182,6 +182,13 @@ def test_overlap_equals_serial_and_split_matches_unsplit():
             c.reset_cache()
             over = c.step().cpu()
             torch.testing.assert_close(over, serial, rtol=0, atol=0)
+            # the first part's attention queued last and the O/MLP nano-batches
+            # run last-first: the same work in another order
+            for ov in (False, True):
+                ns.ns_engine_set_sched(c.h.eng, ns.make_sched(nano_rows=rows, qkv_rows=qrows, overlap=ov,
+                                                              decode_rows_first=True))
+                c.reset_cache()
+                torch.testing.assert_close(c.step().cpu(), serial, rtol=0, atol=0)
             assert_close(serial.numpy(), base.numpy(), "bf16", f"split {rows} vs unsplit")
     finally:
         c.close()
