@@ -48,6 +48,12 @@ from decode_step_06_amd.runner import (DeviceWeights, alloc_sequences, blocks_fo
 WORKLOAD = "qwen05b_b32_ctx512"
 
 
+def decode_sched(**kw):
+    """Schedule of the decode-only workloads (one row per sequence): RoPE and
+    the cache write fused into the attention kernel."""
+    return ns.make_sched(fuse_rope_attention=True, **kw)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -84,7 +90,7 @@ def setup_step(wname):
     b = gen_batch(w)
     maxb = blocks_for(b.seq_lens)
     h = create_engine(shape, DeviceWeights.from_numpy(shape, weights), b.num_blocks, b.n_seqs, maxb, b.n_rows,
-                      b.free_order, None)
+                      b.free_order, decode_sched())
     alloc_sequences(h, b.seq_lens)
     fill_past(h, b.past_seq, b.past_pos, b.past_k, b.past_v)
     return w, weights, b, h, maxb
@@ -412,7 +418,7 @@ def batch_sweep(stream, dw, steps=100, warm_seconds=1.0):
         b = gen_batch(w, with_past=False)
         maxb = blocks_for(b.seq_lens)
         log(f"[bench] batch sweep B={B}")
-        h = create_engine(w.model, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, None,
+        h = create_engine(w.model, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, decode_sched(),
                           nan_poison=False)
         try:
             alloc_sequences(h, b.seq_lens)
@@ -437,7 +443,8 @@ def bucket_capture(stream, dw, steps=50):
     b = gen_batch(w, with_past=False)
     maxb = blocks_for(b.seq_lens)
     log("[bench] bucketed capture")
-    h = create_engine(w.model, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, None, nan_poison=False)
+    h = create_engine(w.model, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, decode_sched(),
+                      nan_poison=False)
     res = {"buckets": list(BUCKETS)}
     try:
         alloc_sequences(h, b.seq_lens)
@@ -498,9 +505,8 @@ def llama80(stream, steps=10, warm_seconds=2.0):
         fill_past_random_on_device(h, b.past_seq, b.past_pos, seed=w.seeds["kv"])
         res["setup_s"] = time.time() - t0
         log("[bench] llama70b 80 layers: timing graph replays")
-        t_nano = _graph_rate(h, b, stream, steps, warm_seconds,
-                             ns.make_sched(nano_rows=w.nano_splits, overlap=True))
-        t_ser = _graph_rate(h, b, stream, steps, 0.5, ns.make_sched())
+        t_nano = _graph_rate(h, b, stream, steps, warm_seconds, decode_sched(nano_rows=w.nano_splits, overlap=True))
+        t_ser = _graph_rate(h, b, stream, steps, 0.5, decode_sched())
         row = _step_row(h, b, t_nano, stream)
         row["ms_per_step_unsplit"] = t_ser * 1e3
         row["tokens_per_s_unsplit"] = b.n_rows / t_ser
@@ -580,8 +586,10 @@ def main():
         nano_ms = None
         if w.nano_splits:
             nano_ms = _graph_rate(h, b, stream, args.steps, 1.0,
-                                  ns.make_sched(nano_rows=w.nano_splits, overlap=True)) * 1e3
-            ns.ns_engine_set_sched(h.eng, ns.make_sched())
+                                  decode_sched(nano_rows=w.nano_splits, overlap=True)) * 1e3
+        # the same step with RoPE and the cache write as their own kernel
+        separate_ms = _graph_rate(h, b, stream, args.steps, 1.0, ns.make_sched()) * 1e3
+        ns.ns_engine_set_sched(h.eng, decode_sched())
         greedy = greedy_loop(h, b, stream)
         # last, so that a kernel trace of this run ends with these launches
         att = attention_isolated(h, b, maxb, stream)
@@ -604,6 +612,8 @@ def main():
     # the step's device time; its average launch duration from the isolated
     # back-to-back launches (in-step event intervals also count dispatch gaps)
     share = kern["attention"]["us_per_step"] / sum(v["us_per_step"] for v in kern.values())
+    # (isolated launches of the paged-attention op; inside the step the same
+    # kernel runs with RoPE and the cache write fused in)
     roof = {"kernel": "attention (attn_mfma_kernel)", "bound": "hbm", "achieved": round(att["gbs"], 1),
             "peak": rf.HBM_PEAK_GBS, "unit": "GB/s", "frac": round(att["gbs"] / rf.HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("attention_qwen05b_b32_ctx512"),
@@ -624,7 +634,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded random-init weights and cached context)",
         "config": {"workload": w.name, "batch": b.n_rows, "context": int(w.decode_ctx), "layers": w.model.n_layers,
-                   "kv_block": 16, "mode": "hipGraph replay", "parallelism": "single GPU"},
+                   "kv_block": 16, "mode": "hipGraph replay", "rope_fused_into_attention": True,
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "calibration_copy_bytes": calib_bytes,
         "step": {"runs_ms": [round(r * 1e3, 4) for r in runs],
@@ -632,6 +643,7 @@ def main():
                  "eager_ms": round(eager * 1e3, 4), "fixed_cost_ms": round((eager - step_s) * 1e3, 4),
                  "kernels_per_step": launches, "algorithmic_bytes": sb,
                  "nano_overlap_ms": nano_ms, "nano_split": list(w.nano_splits),
+                 "separate_rope_kernel_ms": round(separate_ms, 4),
                  "hbm_floor_ms": round(rf.floor_seconds(sb) * 1e3, 4),
                  "step_hbm_frac": round(sb / step_s / 1e9 / rf.HBM_PEAK_GBS, 4)},
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -195,6 +195,7 @@ struct ns_engine {
 struct ns_graph {
   ns_engine* e = nullptr;
   int bucket = 0;
+  bool fused_rope = false;  // captured with RoPE fused into attention: one row per sequence
   void* out = nullptr;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
@@ -214,11 +215,18 @@ int check_sched(const ns_sched* s) {
   if (s->cu_mask_frac < 0.f || s->cu_mask_frac > 1.f) NS_FAIL(NS_EINVAL, "cu_mask_frac must be in [0, 1]");
   if (s->prefill_tiles != 0 && s->prefill_tiles != 1) NS_FAIL(NS_EINVAL, "prefill_tiles must be 0 or 1");
   if (s->decode_rows_first != 0 && s->decode_rows_first != 1) NS_FAIL(NS_EINVAL, "decode_rows_first must be 0 or 1");
+  if (s->fuse_rope_attention != 0 && s->fuse_rope_attention != 1)
+    NS_FAIL(NS_EINVAL, "fuse_rope_attention must be 0 or 1");
+  if (s->fuse_rope_attention && s->prefill_tiles)
+    NS_FAIL(NS_EINVAL, "fuse_rope_attention and prefill_tiles exclude each other");
   return NS_OK;
 }
 
+// RoPE + the row's own K/V write run inside the bf16 attention kernel.
+bool fused_rope(const ns_engine* e, const ns_sched& s) { return s.fuse_rope_attention != 0 && e->d.dtype == NS_BF16; }
+
 // Validate a batch against the engine and the KV manager; no side effects.
-int check_batch(const ns_engine* e, const ns_batch* b, int max_rows) {
+int check_batch(const ns_engine* e, const ns_batch* b, int max_rows, bool one_row_per_seq) {
   if (!b) NS_FAIL(NS_EINVAL, "null batch");
   if (b->n_tok <= 0) NS_FAIL(NS_EINVAL, "batch must have at least one row");
   if (b->n_tok > max_rows) NS_FAIL(NS_ESHAPE, "batch of %d rows exceeds %d", b->n_tok, max_rows);
@@ -236,6 +244,8 @@ int check_batch(const ns_engine* e, const ns_batch* b, int max_rows) {
       NS_FAIL(NS_ESHAPE, "row %d: position %d not covered by sequence %d's blocks", i, p, s);
     if ((int)kv->tables[s].size() > e->maxb)
       NS_FAIL(NS_ESHAPE, "sequence %d holds more blocks than the engine's table rows", s);
+    if (one_row_per_seq && last_pos[s] >= 0)
+      NS_FAIL(NS_EINVAL, "sequence %d has more than one row; the fused RoPE/attention schedule takes one", s);
     if (p <= last_pos[s]) NS_FAIL(NS_EINVAL, "rows of sequence %d must have increasing positions", s);
     last_pos[s] = p;
     if (e->d.vocab > 0 && !b->token_ids_dev && (b->token_ids[i] < 0 || b->token_ids[i] >= e->d.vocab))
@@ -385,6 +395,7 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   // run last-first, so the later rows' projections run beside it.  Attention
   // part j reads only K/V written by parts <= j, all finished before QKV part
   // j's event, so any launch order of the attention parts is valid.
+  const bool fuse = fused_rope(e, sc);
   const bool late_first = sc.decode_rows_first != 0 && nano.size() > 1;
   const bool defer0 = sc.decode_rows_first != 0 && qparts.size() > 1;
   int layer = 0;
@@ -392,6 +403,15 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
     const int r0 = qparts[j].first, n = qparts[j].second - r0;
     ns::AttnArgs a;
     attn_args(e, layer, r0, r0 + n, n_tok, &a);
+    if (fuse) {
+      a.rope_qkv = dec ? pq : qkv;
+      a.rope_slice_stride = dec ? sq : 0;
+      a.rope_splits = S_qkv;
+      a.cosb = e->cosb();
+      a.sinb = e->sinb();
+      a.slot = e->m_slot();
+      a.row_seq = nullptr;
+    }
     if (overlap) HIP_TRY(hipStreamWaitEvent(sa, e->ev_qkv[j], 0));
     ns::launch_attention(a, sa);
     launches += a.n_parts > 1 ? 2 : 1;
@@ -421,12 +441,15 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
         NS_FAIL(NS_ESHAPE, "unsupported QKV projection shape");
       }
       MARK(K_QKV);
-      ns::launch_rope_kv(dt, (dec ? pq : qkv) + (size_t)r0 * QKV, dec ? sq : 0, S_qkv,
-                         e->cosb() + (size_t)r0 * hd / 2, e->sinb() + (size_t)r0 * hd / 2, e->m_slot() + r0,
-                         (char*)e->q_att() + (size_t)r0 * DQ * es, e->k_layer(l), e->v_layer(l), n, nq, nkv, hd,
-                         st);
-      MARK(K_ROPE_KV);
-      launches += 2;
+      ++launches;
+      if (!fuse) {
+        ns::launch_rope_kv(dt, (dec ? pq : qkv) + (size_t)r0 * QKV, dec ? sq : 0, S_qkv,
+                           e->cosb() + (size_t)r0 * hd / 2, e->sinb() + (size_t)r0 * hd / 2, e->m_slot() + r0,
+                           (char*)e->q_att() + (size_t)r0 * DQ * es, e->k_layer(l), e->v_layer(l), n, nq, nkv, hd,
+                           st);
+        MARK(K_ROPE_KV);
+        ++launches;
+      }
       if (overlap) HIP_TRY(hipEventRecord(e->ev_qkv[j], st));
       // the decode part's attention waits until the other parts' is queued
       if (!(defer0 && j == 0)) {
@@ -639,7 +662,7 @@ int ns_engine_set_sched(ns_engine* e, const ns_sched* sched) {
 
 int ns_decode_step(ns_engine* e, const ns_batch* b, void* out, void* stream) {
   if (!e || !out) NS_FAIL(NS_EINVAL, "null engine or output");
-  int rc = check_batch(e, b, e->max_tokens);
+  int rc = check_batch(e, b, e->max_tokens, fused_rope(e, e->sched));
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   if ((rc = upload_meta(e, b, b->n_tok, st))) return rc;
@@ -658,6 +681,7 @@ int ns_graph_capture(ns_engine* e, int32_t bucket, void* out, void* stream, ns_g
   g->e = e;
   g->bucket = bucket;
   g->out = out;
+  g->fused_rope = fused_rope(e, e->sched);
   hipError_t he = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
   if (he != hipSuccess) {
     delete g;
@@ -684,7 +708,7 @@ int ns_graph_capture(ns_engine* e, int32_t bucket, void* out, void* stream, ns_g
 int ns_graph_replay(ns_graph* g, const ns_batch* b, void* stream) {
   if (!g) NS_FAIL(NS_EINVAL, "null graph");
   ns_engine* e = g->e;
-  int rc = check_batch(e, b, g->bucket);
+  int rc = check_batch(e, b, g->bucket, g->fused_rope);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   if ((rc = upload_meta(e, b, g->bucket, st))) return rc;

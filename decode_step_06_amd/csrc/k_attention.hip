@@ -325,6 +325,16 @@ namespace {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// Inputs of the fused RoPE prologue (see AttnArgs).
+struct RopeIn {
+  const float* qkv;
+  long slice_stride;
+  int splits;
+  const float* cosb;
+  const float* sinb;
+  const int32_t* slot;
+};
+
 // Registers of one 64-token pass: K fragments of QK tile (s, u) for each
 // k-step over d, and V^T fragments of PV step s for each 16-row d tile.
 template <int D>
@@ -455,15 +465,107 @@ __device__ __forceinline__ void mfma_compute(MfmaPass<D>& r, const bf16x8_t (&qf
 
 }  // namespace
 
+// Fused RoPE prologue of a work item (row t, KV head g): stage the G query
+// heads of this KV head, its k and its v from the QKV projection (summing
+// split-K slices in slice order) in LDS, rotate q and k (rotate-half, the
+// step's cos/sin table), round to bf16 into rq / rv.  The workgroup whose
+// partition holds the row's last position writes the row's k and v into the
+// paged cache at its slot (rows of other sequences never read that slot; this
+// row's own passes take the token from LDS).  Same arithmetic as the separate
+// RoPE / cache-write kernel, so the results are the same bits.
+template <int D, int G, int NWAVE>
+__device__ __forceinline__ void rope_prologue(const RopeIn& ra, int t, int g, int nq, int nkv, int ctx, int start,
+                                              int end, bf16_t* kcw, bf16_t* vcw, bf16_t* rq, bf16_t* rv) {
+  constexpr int HALF = D / 2, NCH = D / 8;
+  __shared__ __attribute__((aligned(16))) float rbuf[(G + 2) * D];
+  const int width = (nq + 2 * nkv) * D;
+  const float* row = ra.qkv + (long)t * width;
+  for (int i4 = threadIdx.x; i4 < (G + 2) * D / 4; i4 += 64 * NWAVE) {
+    const int e = 4 * i4;
+    const int src = e < G * D ? g * G * D + e
+                              : (e < (G + 1) * D ? nq * D + g * D + (e - G * D) : (nq + nkv) * D + g * D + (e - (G + 1) * D));
+    *(f32x4_t*)(rbuf + e) = slice_sum4(row + src, ra.slice_stride, ra.splits);
+  }
+  __syncthreads();
+  const float* cr = ra.cosb + (long)t * HALF;
+  const float* sr = ra.sinb + (long)t * HALF;
+  for (int i = threadIdx.x; i < (G + 1) * HALF + D; i += 64 * NWAVE) {
+    if (i < (G + 1) * HALF) {
+      const int hh = i / HALF, j = i % HALF;
+      float y1, y2;
+      rope_pair(rbuf[hh * D + j], rbuf[hh * D + j + HALF], cr[j], sr[j], y1, y2);
+      rq[hh * D + j] = f32_to_bf16(y1);
+      rq[hh * D + j + HALF] = f32_to_bf16(y2);
+    } else {
+      const int j = i - (G + 1) * HALF;
+      rv[j] = f32_to_bf16(rbuf[(G + 1) * D + j]);
+    }
+  }
+  __syncthreads();
+  const int own = ctx - 1;
+  if (own >= start && own < end) {
+    const int s = ra.slot[t];
+    if (s >= 0) {
+      const long blk = s / NS_BLOCK;
+      const int tok = s % NS_BLOCK;
+      for (int j = threadIdx.x; j < D; j += 64 * NWAVE) {
+        // K rows chunk-major within the block ([blk][nkv][d/8][16][8]), V
+        // transposed ([blk][nkv][d][16])
+        kcw[(((blk * nkv + g) * NCH + j / 8) * NS_BLOCK + tok) * 8 + (j & 7)] = rq[G * D + j];
+        vcw[((blk * nkv + g) * D + j) * NS_BLOCK + tok] = rv[j];
+      }
+    }
+  }
+}
+
+// Replace the row's own token (pass offset o) in the pass registers: K
+// fragments of lanes with head column 4 (o%32/8) + o%4 (tile (o/32,
+// o%8/4), chunk 4 j + grp) and element o%8 of the V^T fragments of lanes
+// with grp = o%32/8 (head-dim row 16 dt + hc).
+template <int D, int G>
+__device__ __forceinline__ void patch_own_token(MfmaPass<D>& r, int o, int hc, int grp, const bf16_t* rq,
+                                                const bf16_t* rv) {
+  const int ss = o >> 5, rem = o & 31;
+  if (hc == 4 * (rem >> 3) + (rem & 3)) {
+    const int uu = (rem >> 2) & 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (s == ss && u == uu) {
+#pragma unroll
+          for (int j = 0; j < D / 32; ++j) r.k[s][u][j] = *(const bf16x8_t*)(rq + G * D + (4 * j + grp) * 8);
+        }
+  }
+  if (grp == (rem >> 3)) {
+    const int e = o & 7;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s == ss) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const uint32_t val = rv[16 * dt + hc];
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            if (w == (e >> 1)) {
+              const uint32_t x = r.v[dt][s][w];
+              r.v[dt][s][w] = (e & 1) ? ((x & 0x0000ffffu) | (val << 16)) : ((x & 0xffff0000u) | val);
+            }
+        }
+      }
+  }
+}
+
 // Lane l of a wavefront: head column hc = l % 16 (heads >= G are zero
 // padding whose results are dropped), lane group grp = l / 16.  Arguments as
 // attn_decode_kernel.
-template <int D, int G, int NWAVE>
+template <int D, int G, int NWAVE, bool ROPE>
 __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
-    const bf16_t* __restrict__ qatt, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    const bf16_t* __restrict__ qatt, const bf16_t* kc, const bf16_t* vc,
     const int32_t* __restrict__ row_bseq, const int32_t* __restrict__ row_pos, const int32_t* __restrict__ btab,
     bf16_t* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml, int maxb, int row0,
-    int n_rows, int nq, int nkv, int P, int n_parts, float scale_log2, const int32_t* __restrict__ skip_seq) {
+    int n_rows, int nq, int nkv, int P, int n_parts, float scale_log2, const int32_t* __restrict__ skip_seq,
+    RopeIn ra) {
   static_assert(G <= 16 && D % 32 == 0, "heads must fit the 16 MFMA columns, d whole k-steps");
   constexpr int NCH = D / 8;  // 16-byte chunks per head row
   constexpr int KS = D / 32, DT = D / 16;
@@ -514,11 +616,26 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
 
     // Q^T fragments (B operand of QK): head hc, d chunk 4 j + grp
     bf16x8_t qf[KS];
+    // fused RoPE: the rotated q heads of this KV head and the rotated k (bf16
+    // [G + 1][D]) and v (bf16 [D]) of the row's own token, in LDS
+    __shared__ __attribute__((aligned(16))) bf16_t rq[ROPE ? (G + 1) * D : 8];
+    __shared__ __attribute__((aligned(16))) bf16_t rv[ROPE ? D : 8];
+    if constexpr (ROPE) {
+      rope_prologue<D, G, NWAVE>(ra, t, g, nq, nkv, ctx, start, end, const_cast<bf16_t*>(kc), const_cast<bf16_t*>(vc),
+                                 rq, rv);
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      u32x4_t q = *(const u32x4_t*)(qatt + ((((long)t * nkv + g) * NCH + 4 * j + grp) * G + (hc < G ? hc : 0)) * 8);
-      if (hc >= G) q = (u32x4_t){0u, 0u, 0u, 0u};
-      qf[j] = __builtin_bit_cast(bf16x8_t, q);
+      for (int j = 0; j < KS; ++j) {
+        u32x4_t q = *(const u32x4_t*)(rq + (hc < G ? hc : 0) * D + (4 * j + grp) * 8);
+        if (hc >= G) q = (u32x4_t){0u, 0u, 0u, 0u};
+        qf[j] = __builtin_bit_cast(bf16x8_t, q);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        u32x4_t q = *(const u32x4_t*)(qatt + ((((long)t * nkv + g) * NCH + 4 * j + grp) * G + (hc < G ? hc : 0)) * 8);
+        if (hc >= G) q = (u32x4_t){0u, 0u, 0u, 0u};
+        qf[j] = __builtin_bit_cast(bf16x8_t, q);
+      }
     }
     float m = -INFINITY, l = 0.f;
     f32x4_t acc[DT];
@@ -537,6 +654,12 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
       // the next pass's block ids load while this pass's K/V are in flight
       const int cn = c0 + 64 * NWAVE;
       if (cn < end) cur = pass_blocks(bt, cn, end);
+      if constexpr (ROPE) {
+        // the row's own token: its K/V from LDS (the cache copy is written
+        // by this workgroup, not necessarily visible to these loads)
+        const int o = ctx - 1 - c0;
+        if (o >= 0 && o < 64) patch_own_token<D, G>(pr, o, hc, grp, rq, rv);
+      }
       mfma_compute<D>(pr, qf, acc, m, l, c0, end, grp, scale_log2);
     }
     // the four lanes of a head hold disjoint tokens: sum their denominators
@@ -613,6 +736,7 @@ template <typename T, int D, int G>
 static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
   AttnArgs a = a0;
   if (!a.row_seq || !prefill_supported(a.dtype, D, G) || a.n_rows < 32) a.row_seq = nullptr;  // no prefill tiles
+  if (a.rope_qkv) a.row_seq = nullptr;  // fused RoPE: rows of distinct sequences, no q_att for prefill tiles
   const long total = (long)a.n_rows * a.nkv * a.n_parts;
   if (total <= 0) return;
   long grid = total;
@@ -622,12 +746,22 @@ static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
   (const T*)a.q_att, (const T*)a.kc, (const T*)a.vc, a.row_bseq, a.row_pos, a.btab, (T*)a.out, a.part_acc,       \
       a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts, scale_log2, a.row_seq
   if constexpr (std::is_same<T, bf16_t>::value) {
-    if (a.waves == 1)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS);
-    else if (a.waves == 8)
-      hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS);
-    else
-      hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS);
+    const RopeIn ra{a.rope_qkv, a.rope_slice_stride, a.rope_splits, a.cosb, a.sinb, a.slot};
+    if (a.rope_qkv) {
+      if (a.waves == 1)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1, true>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS, ra);
+      else if (a.waves == 8)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, true>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra);
+      else
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, true>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra);
+    } else {
+      if (a.waves == 1)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1, false>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS, ra);
+      else if (a.waves == 8)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, false>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra);
+      else
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, false>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra);
+    }
   } else {
     if (a.waves == 1)
       hipLaunchKernelGGL((attn_decode_kernel<T, D, G, 1>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS);

@@ -309,10 +309,7 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ 
       float y1[E], y2[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float x1 = src[j0 + e], x2 = src[j0 + half + e];
-        const float cs = cr[j0 + e], sn = sr[j0 + e];
-        y1[e] = x1 * cs - x2 * sn;
-        y2[e] = x2 * cs + x1 * sn;
+        rope_pair(src[j0 + e], src[j0 + half + e], cr[j0 + e], sr[j0 + e], y1[e], y2[e]);
       }
       if (is_q) {
         const int g = hd / G, hh = hd % G;

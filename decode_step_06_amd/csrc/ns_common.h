@@ -30,6 +30,15 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// Rotate-half RoPE of one pair (x1 = element j, x2 = element j + d/2) by the
+// angle with cosine cs and sine sn.  Contraction is off, so every kernel that
+// rotates produces the same bits.
+__device__ __forceinline__ void rope_pair(float x1, float x2, float cs, float sn, float& y1, float& y2) {
+#pragma clang fp contract(off)
+  y1 = x1 * cs - x2 * sn;
+  y2 = x2 * cs + x1 * sn;
+}
+
 // Low / high bf16 of a packed pair as float.
 __device__ __forceinline__ float lo_bf16(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }

@@ -89,6 +89,15 @@ struct AttnArgs {
   int waves;                // wavefronts per work item: 1, 4 or 8 (fp32: 8 runs as 4)
   int wg_cap;               // 0 = one workgroup per work item
   const int32_t* row_seq;   // [T] sequence of each row (-1: padding), or null: no prefill tiles
+  // RoPE and the row's own K/V write fused into the bf16 matrix-core kernel
+  // (rows of distinct sequences only): null = q from q_att, the row's K/V
+  // already in the cache.
+  const float* rope_qkv = nullptr;  // [T][(nq + 2 nkv) d] fp32; slice s at + s * rope_slice_stride
+  long rope_slice_stride = 0;
+  int rope_splits = 1;
+  const float* cosb = nullptr;      // [T][d/2]
+  const float* sinb = nullptr;
+  const int32_t* slot = nullptr;    // [T] cache slot of each row (-1: none)
 };
 int attention_supported(int dtype, int d, int G);
 // Rows are taken in tiles of 32 from row0; a tile of one sequence at

@@ -48,7 +48,7 @@ class ns_sched(C.Structure):
     _fields_ = [("n_nano", C.c_int32), ("nano_rows", C.c_int32 * 4), ("n_qkv", C.c_int32),
                 ("qkv_rows", C.c_int32 * 4), ("overlap", C.c_int32), ("attn_wg_cap", C.c_int32),
                 ("cu_mask_frac", C.c_float), ("prefill_tiles", C.c_int32),
-                ("decode_rows_first", C.c_int32)]
+                ("decode_rows_first", C.c_int32), ("fuse_rope_attention", C.c_int32)]
 
 
 class ns_batch(C.Structure):
@@ -139,7 +139,7 @@ def model_desc(shape) -> ns_model_desc:
 
 def make_sched(nano_rows: Sequence[int] = (), qkv_rows: Sequence[int] = (), overlap: bool = False,
                attn_wg_cap: int = 0, cu_mask_frac: float = 0.0, prefill_tiles: bool = False,
-               decode_rows_first: bool = False) -> ns_sched:
+               decode_rows_first: bool = False, fuse_rope_attention: bool = False) -> ns_sched:
     s = ns_sched()
     s.n_nano = len(nano_rows)
     for i, r in enumerate(nano_rows):
@@ -152,6 +152,7 @@ def make_sched(nano_rows: Sequence[int] = (), qkv_rows: Sequence[int] = (), over
     s.cu_mask_frac = float(cu_mask_frac)
     s.prefill_tiles = int(bool(prefill_tiles))
     s.decode_rows_first = int(bool(decode_rows_first))
+    s.fuse_rope_attention = int(bool(fuse_rope_attention))
     return s
 
 

@@ -195,6 +195,15 @@ int ns_slot_map(const ns_kv* kv, int32_t n_tok, const int32_t* seq, const int32_
  *     O projection + MLP nano-batches run last-first, so the prompt rows'
  *     projections run beside the decode rows' memory-bound attention
  *     ("Nano-batching: manufacturing independence").  Results are
+ *     bit-identical either way.
+ *   fuse_rope_attention: 0 = RoPE and the cache write of each row's own K/V
+ *     run as their own kernel before attention; 1 = (bf16 models) inside the
+ *     attention kernel, one launch fewer per layer (the nanoserve notes'
+ *     changes table counts fused launches as the per-step win).  The rows of
+ *     a step must then belong to distinct sequences (a decode batch): a row
+ *     reads no K/V that another row of the same step writes.  Steps and
+ *     replays of graphs captured with it reject a batch that repeats a
+ *     sequence (NS_EINVAL).  Excludes prefill_tiles.  Results are
  *     bit-identical either way. */
 typedef struct {
   int32_t n_nano;
@@ -206,6 +215,7 @@ typedef struct {
   float cu_mask_frac;
   int32_t prefill_tiles;
   int32_t decode_rows_first;
+  int32_t fuse_rope_attention;
 } ns_sched;
 
 /* One step's rows.  token_ids (host, [n_tok]) for models with a vocabulary,
