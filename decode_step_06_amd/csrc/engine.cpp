@@ -395,7 +395,13 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   // run last-first, so the later rows' projections run beside it.  Attention
   // part j reads only K/V written by parts <= j, all finished before QKV part
   // j's event, so any launch order of the attention parts is valid.
-  const bool fuse = fused_rope(e, sc);
+  // fused only where a work item has several wavefronts to share the RoPE
+  // prologue: with one wavefront per item (>= 2048 items) the prologue
+  // serialises in front of every item's K/V stream (80-layer 70B-shaped step
+  // at 256 rows: 61.6 -> 64.1 ms), so the separate kernel runs there
+  int a_pt = 0, a_np = 0, a_waves = 1;
+  attn_partition(n_tok, nkv, e->maxb * NS_BLOCK_SIZE, &a_pt, &a_np, &a_waves);
+  const bool fuse = fused_rope(e, sc) && a_waves > 1;
   const bool late_first = sc.decode_rows_first != 0 && nano.size() > 1;
   const bool defer0 = sc.decode_rows_first != 0 && qparts.size() > 1;
   int layer = 0;

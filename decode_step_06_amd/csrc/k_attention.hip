@@ -747,10 +747,8 @@ static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
       a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts, scale_log2, a.row_seq
   if constexpr (std::is_same<T, bf16_t>::value) {
     const RopeIn ra{a.rope_qkv, a.rope_slice_stride, a.rope_splits, a.cosb, a.sinb, a.slot};
-    if (a.rope_qkv) {
-      if (a.waves == 1)
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1, true>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS, ra);
-      else if (a.waves == 8)
+    if (a.rope_qkv) {  // the fused prologue runs on 8 or 4 wavefronts per item
+      if (a.waves == 8)
         hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, true>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra);
       else
         hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, true>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra);

@@ -712,6 +712,13 @@ static PartialPlan partial_plan(int M, int N, int K) {
   long best_wg = -1;
   for (int kind = (M > 128 ? TILE_BIG : TILE_BIG128); kind <= TILE_64; ++kind) {
     const long tiles = tile_count(kind, M, N, false);
+    if (kind <= TILE_BIG128) {
+      // one big-tile workgroup per CU: a split count that fills at least 3/4
+      // of one wave beats one that spills a few workgroups into a second
+      // (70B-shaped QKV at 256 rows: 40 tiles x 6 = 240, not x 7 = 280)
+      const int s1 = (int)std::max(1L, std::min((long)max_s, kFillTarget / tiles));
+      if (4 * tiles * s1 >= 3 * kFillTarget) return {kind, s1};
+    }
     const int s = (int)std::max(1L, std::min((long)max_s, (kFillTarget + tiles - 1) / tiles));
     if (tiles * s >= kFillTarget) return {kind, s};
     if (tiles * s > best_wg) {

@@ -203,8 +203,10 @@ int ns_slot_map(const ns_kv* kv, int32_t n_tok, const int32_t* seq, const int32_
  *     a step must then belong to distinct sequences (a decode batch): a row
  *     reads no K/V that another row of the same step writes.  Steps and
  *     replays of graphs captured with it reject a batch that repeats a
- *     sequence (NS_EINVAL).  Excludes prefill_tiles.  Results are
- *     bit-identical either way. */
+ *     sequence (NS_EINVAL).  Excludes prefill_tiles.  Steps whose attention
+ *     runs one wavefront per (row, KV head) item (2048 or more items) keep
+ *     the separate kernel: there the prologue would serialise in front of
+ *     every item.  Results are bit-identical either way. */
 typedef struct {
   int32_t n_nano;
   int32_t nano_rows[4];

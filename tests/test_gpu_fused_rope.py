@@ -3,8 +3,9 @@ attention kernel (ns_sched.fuse_rope_attention), for steps whose rows belong
 to distinct sequences.  It computes the same bits as the separate
 RoPE/cache-write kernel followed by attention: the outputs and the whole KV
 cache after the step are compared bit for bit, in every launch shape of the
-attention kernel (8, 4 and 1 wavefronts per work item, split contexts,
-head_dim 64 and 128), eager and graph-replayed, nano-batched with overlap.
+attention kernel that fuses it (8 and 4 wavefronts per work item, split
+contexts, head_dim 64 and 128; with one wavefront per item the engine keeps
+the separate kernel), eager and graph-replayed, nano-batched with overlap.
 The fused step also matches the oracle, and a batch that repeats a sequence
 is rejected with no side effects."""
 import numpy as np
@@ -28,9 +29,12 @@ CASES = {
     "small-8waves": Workload("f8", SMALL, 6, ctx_range=(1, 200)),
     # <= 2047 items: 4 wavefronts (split-K QKV slices: steps of <= 256 rows)
     "small-4waves": Workload("f4", SMALL_H, 200, ctx_range=(1, 40)),
-    # >= 2048 items: 1 wavefront, with slices and with the unsplit projection
+    # 1024 items of 8 KV heads: 4 wavefronts
+    "kv8-4waves": Workload("f1", KV8, 128, ctx_range=(1, 70)),
+    # >= 2048 items: one wavefront per item, where the engine keeps the
+    # separate kernel (with slices and with the unsplit projection)
     "kv8-1wave": Workload("f1", KV8, 256, ctx_range=(1, 70)),
-    "small-1wave-300rows": Workload("f1b", SMALL_H, 1100, ctx_range=(1, 24)),
+    "small-1wave-1100rows": Workload("f1b", SMALL_H, 1100, ctx_range=(1, 24)),
     # contexts past 8 passes of 8 wavefronts: split into partitions + combine
     "qwen-split": Workload("fs", QWEN1, 3, ctx_range=(4100, 5000)),
     "llama-d128": Workload("fl", LLAMA1, 5, ctx_range=(1, 300)),
@@ -50,10 +54,13 @@ def test_fused_rope_attention_is_bit_exact(name):
         say(f"case {name}: {c.batch.n_rows} rows, contexts {int(c.batch.row_pos.min()) + 1}.."
             f"{int(c.batch.row_pos.max()) + 1}")
         ref = c.step().cpu()
+        n_ref = ns.ns_engine_last_launches(c.h.eng)
         ref_kv = _kv_bytes(c)
         ns.ns_engine_set_sched(c.h.eng, ns.make_sched(fuse_rope_attention=True))
         c.reset_cache()
         got = c.step().cpu()
+        fused = c.batch.n_rows * w.model.n_kv_heads < 2048
+        assert ns.ns_engine_last_launches(c.h.eng) == n_ref - (w.model.n_layers if fused else 0)
         torch.testing.assert_close(got, ref, rtol=0, atol=0)
         assert torch.equal(_kv_bytes(c), ref_kv), "cache after the fused step differs"
         # a captured graph of the fused step replays the same bits
