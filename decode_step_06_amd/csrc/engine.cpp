@@ -510,7 +510,8 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
     else
       ns::launch_rmsnorm(dt, x, e->final_norm, h, n_tok, H, d.rms_eps, st);
     MARK(K_NORM);
-    if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n_tok, d.vocab, H, h, H, e->lm_head, H, out, d.vocab, st))
+    if (ns::launch_gemm(dt, ns::EPI_STORE_F32, n_tok, d.vocab, H, h, H, e->lm_head, wld(d.vocab, H), out, d.vocab,
+                        st, pk))
       NS_FAIL(NS_ESHAPE, "unsupported LM head shape");
     MARK(K_LM_HEAD);
     launches += 2;

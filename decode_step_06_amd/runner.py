@@ -74,7 +74,13 @@ class DeviceWeights:
         layers = [{k: up(pack_kslab_host(v) if (pk and k in PACKED) else v) for k, v in lw.items()}
                   for lw in w["layers"]]
         emb = up(w["embed"])
-        lm = emb if (shape.tied and w["embed"] is not None) else up(w["lm_head"])
+        lm_src = w["embed"] if shape.tied else w["lm_head"]
+        if lm_src is None:
+            lm = None
+        elif pk:  # K-slab-major (a tied model's head is a packed copy of the embedding)
+            lm = up(pack_kslab_host(lm_src))
+        else:
+            lm = emb if shape.tied else up(lm_src)
         return cls(shape, {"layers": layers, "final_norm": up(w["final_norm"]), "embed": emb, "lm_head": lm})
 
     @classmethod
@@ -109,7 +115,14 @@ class DeviceWeights:
         if shape.vocab:
             fn = gain((shape.hidden,))
             emb = mat((shape.vocab, shape.hidden))
-            lm = emb if shape.tied else mat((shape.vocab, shape.hidden))
+            if shape.dtype != "bf16":
+                lm = emb if shape.tied else mat((shape.vocab, shape.hidden))
+            elif shape.tied:  # a packed copy of the embedding
+                lm = torch.empty_like(emb)
+                ns.ns_pack_weight(emb.data_ptr(), lm.data_ptr(), shape.vocab, shape.hidden)
+                torch.cuda.synchronize()
+            else:
+                lm = packed((shape.vocab, shape.hidden))
         return cls(shape, {"layers": layers, "final_norm": fn, "embed": emb, "lm_head": lm})
 
     def logical_layer(self, l: int) -> dict:
@@ -123,6 +136,13 @@ class DeviceWeights:
             else:
                 out[k] = v
         return out
+
+    def logical_lm_head(self) -> torch.Tensor:
+        """The LM head as a row-major [V, H] device tensor."""
+        lm = self.t["lm_head"]
+        if self.shape.dtype == "bf16":
+            return unpack_kslab(lm, self.shape.vocab, self.shape.hidden)
+        return lm
 
     def bytes(self) -> int:
         seen, total = set(), 0

@@ -86,9 +86,11 @@ typedef struct {
  *   wo[l]:   [H, nq d]
  *   wgu[l]:  [2F, H]               rows: gate (F rows) then up (F rows)
  *   wdown[l]:[H, F]
- *   final_norm: [H]; embed: [V, H]; lm_head: [V, H] (may equal embed).
- * Layout: embed, lm_head and every fp32 model's matrices are row-major.  In
- * a bf16 model wqkv, wo, wgu and wdown are K-slab-major instead: element
+ *   final_norm: [H]; embed: [V, H]; lm_head: [V, H].
+ * Layout: embed and every fp32 model's matrices are row-major (an fp32
+ * model's lm_head may equal embed).  In a bf16 model wqkv, wo, wgu, wdown
+ * and lm_head are K-slab-major instead (a tied bf16 model passes a packed
+ * copy of embed as lm_head): element
  * (row r, column k) of a [R, K] matrix sits at ((k / 32) * R + r) * 32 +
  * k % 32, so the 32 columns k0 .. k0+31 of all R rows form one contiguous
  * [R][32] block and each row's piece of it is a whole 64-byte segment (the

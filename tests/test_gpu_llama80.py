@@ -104,7 +104,7 @@ def test_llama70b_80_layers_b256_graph_nano_and_sampled_oracle():
         weights = {"layers": _LayerStream(dw),
                    "final_norm": dw.t["final_norm"].cpu().double().numpy(),
                    "embed": dw.t["embed"].cpu().double().numpy(),
-                   "lm_head": dw.t["lm_head"].cpu().double().numpy()}
+                   "lm_head": dw.logical_lm_head().cpu().double().numpy()}
         say("  oracle (bf16 storage points): streaming 80 layers")
         ref = oracle_sampled(shape, weights, b, rows, keep, kept_k, kept_v, emulate=True)
         say("  oracle (float64 throughout): streaming 80 layers")
