@@ -200,8 +200,9 @@ int ns_slot_map(const ns_kv* kv, int32_t n_tok, const int32_t* seq, const int32_
  *     bit-identical either way.
  *   fuse_rope_attention: 0 = RoPE and the cache write of each row's own K/V
  *     run as their own kernel before attention; 1 = (bf16 models) inside the
- *     attention kernel, one launch fewer per layer (the nanoserve notes'
- *     changes table counts fused launches as the per-step win).  The rows of
+ *     attention kernel, one launch fewer per layer (streams-and-graphs
+ *     page, "Knob 9 -- Fused kernels": fusing removes launches; the nanoserve
+ *     notes' paged-attention kernel took over the ops around it).  The rows of
  *     a step must then belong to distinct sequences (a decode batch): a row
  *     reads no K/V that another row of the same step writes.  Steps and
  *     replays of graphs captured with it reject a batch that repeats a
