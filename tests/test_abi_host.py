@@ -168,3 +168,29 @@ def test_engine_create_rejects_bad_arguments_without_a_gpu():
     bad.n_q_heads, bad.n_kv_heads = 5, 2       # heads do not group evenly
     kvp = ctypes.c_void_p()
     assert ns.lib().ns_kv_create(ctypes.byref(bad), 4, 1, 1, None, ctypes.byref(kvp)) == ns.NS_EINVAL
+
+
+def test_schedule_options_are_validated_without_a_gpu():
+    """ns_sched is checked before anything else of the engine: flags must be
+    0 or 1, and RoPE fused into attention excludes prefill tiles."""
+    desc = ns.model_desc(LLAMA70B)
+    kv = ns.ns_kv_create(desc, 8, 2, 4, None)
+    try:
+        w = ns.ns_weights()
+        out = ctypes.c_void_p()
+        for sched, msg in ((ns.make_sched(fuse_rope_attention=True, prefill_tiles=True), "exclude each other"),
+                           (ns.make_sched(decode_rows_first=True), None),
+                           (ns.make_sched(fuse_rope_attention=True), None)):
+            rc = ns.lib().ns_engine_create(ctypes.byref(desc), ctypes.byref(w), kv, None, 0, None, 0, 16,
+                                           ctypes.byref(sched), ctypes.byref(out))
+            assert rc == ns.NS_EINVAL
+            err = ns.lib().ns_last_error().decode()
+            # a valid schedule gets past the check and fails on the null weights
+            assert (msg in err) if msg else ("null" in err)
+        bad = ns.make_sched()
+        bad.decode_rows_first = 2
+        rc = ns.lib().ns_engine_create(ctypes.byref(desc), ctypes.byref(w), kv, None, 0, None, 0, 16,
+                                       ctypes.byref(bad), ctypes.byref(out))
+        assert rc == ns.NS_EINVAL and "decode_rows_first" in ns.lib().ns_last_error().decode()
+    finally:
+        ns.ns_kv_destroy(kv)
