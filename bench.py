@@ -312,7 +312,16 @@ def dense_batch(stream, steps=10):
                              ("nano_overlap", nano()),
                              ("nano_overlap_decode_first", nano(decode_rows_first=True)),
                              ("nano_overlap_decode_first_cap256", nano(decode_rows_first=True, attn_wg_cap=256)),
-                             ("nano_overlap_decode_first_cap128", nano(decode_rows_first=True, attn_wg_cap=128))):
+                             ("nano_overlap_decode_first_cap128", nano(decode_rows_first=True, attn_wg_cap=128)),
+                             # other split sizes: two halves; the decode rows alone against the
+                             # prompt chunks (512/1536); the pages' 768/1280 at QKV as well
+                             ("nano_overlap_1024_1024", ns.make_sched(nano_rows=(1024, 1024), overlap=True,
+                                                                      prefill_tiles=True)),
+                             ("nano_overlap_512_1536_decode_first",
+                              ns.make_sched(nano_rows=(512, 1536), overlap=True, prefill_tiles=True,
+                                            decode_rows_first=True)),
+                             ("nano_overlap_768_1280_qkv_same",
+                              ns.make_sched(nano_rows=w.nano_splits, overlap=True, prefill_tiles=True))):
             ns.ns_engine_set_sched(h.eng, sched)
             g = ns.ns_graph_capture(h.eng, T, out.data_ptr(), stream)
             try:
