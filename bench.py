@@ -10,7 +10,8 @@ replayed as one captured hipGraph per step: ``value`` is decode tokens/s
 
 Also reported (each kernel timed live with HIP events on the stream it runs
 on, behind a queued busy-wait kernel so host launch gaps do not count):
-  * ``roofline``: the step's dominant kernel against the HBM peak;
+  * ``roofline``: the step's dominant kernel (the gate-up projection) against
+    the HBM peak; ``attention_roofline``: the paged decode attention alike;
   * ``kernels``: per-kernel achieved GB/s or TFLOP/s for the step's kernels;
   * ``dense_batch``: the LLaMA-2-70B-shaped layer at the 2048-token dense
     batch -- decode attention (512 rows x context 1024) against the HBM peak,
@@ -250,6 +251,29 @@ def attention_isolated(h, b, maxb, stream, n=400):
     stream.synchronize()
     t = time_launches(launch, n, stream, reps=3)
     nbytes = int(rf.attention_bytes(s, (b.row_pos + 1).astype(np.int64)))
+    return {"us": t * 1e6, "bytes": nbytes, "gbs": nbytes / t / 1e9, "launches": n * 3 + 20}
+
+
+def gate_up_isolated(h, b, stream, n=400):
+    """The step's gate-up projection (layer 0's K-slab-major weights, a
+    [rows, H] bf16 input, the SwiGLU epilogue: the same kernel and launch
+    shape as in the step) launched n times back to back on `stream`."""
+    s = h.shape
+    T, H, F = b.n_rows, s.hidden, s.ffn
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    A = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    C = torch.empty((T, F), device="cuda", dtype=torch.bfloat16)
+    wgu = h.weights.t["layers"][0]["wgu"]
+
+    def launch(i):
+        ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), wgu.data_ptr(), C.data_ptr(), stream)
+
+    for i in range(20):
+        launch(i)
+    stream.synchronize()
+    t = time_launches(launch, n, stream, reps=3)
+    nbytes = rf.gemm_bytes(T, F, H, 2, "silu")
     return {"us": t * 1e6, "bytes": nbytes, "gbs": nbytes / t / 1e9, "launches": n * 3 + 20}
 
 
@@ -602,6 +626,7 @@ def main():
         greedy = greedy_loop(h, b, stream)
         # last, so that a kernel trace of this run ends with these launches
         att = attention_isolated(h, b, maxb, stream)
+        gu = gate_up_isolated(h, b, stream)
         if not args.no_sweep:
             try:
                 sweep = json.loads(json.dumps(batch_sweep(stream, h.weights), default=_jsonable))
@@ -620,15 +645,32 @@ def main():
     # dominant kernel: decode attention, the class with the largest share of
     # the step's device time; its average launch duration from the isolated
     # back-to-back launches (in-step event intervals also count dispatch gaps)
-    share = kern["attention"]["us_per_step"] / sum(v["us_per_step"] for v in kern.values())
-    # (isolated launches of the paged-attention op; inside the step the same
-    # kernel runs with RoPE and the cache write fused in)
-    roof = {"kernel": "attention (attn_mfma_kernel)", "bound": "hbm", "achieved": round(att["gbs"], 1),
-            "peak": rf.HBM_PEAK_GBS, "unit": "GB/s", "frac": round(att["gbs"] / rf.HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("attention_qwen05b_b32_ctx512"),
-            "bytes_per_launch": att["bytes"], "avg_launch_us": round(att["us"], 3),
-            "isolated_launches": att["launches"], "in_step_event_interval_us": round(kern["attention"]["us_per_launch"], 3),
-            "share_of_step": round(share, 3)}
+    # dominant kernel: the gate-up projection, the single kernel with the
+    # largest share of the step's device time in the kernel trace of this
+    # command (per step: gate-up 24 x 9.8 us, attention 24 x 8.8 us,
+    # RMSNorm 48 x 3.8 us); HBM-bound at 32 rows (17.4 MB of weights per
+    # launch).  Its average launch duration from the isolated back-to-back
+    # launches (in-step event intervals also count dispatch gaps).
+    tot = sum(v["us_per_step"] for v in kern.values())
+    roof = {"kernel": "gate-up projection + SwiGLU (gemv_bf16_kernel)", "bound": "hbm",
+            "achieved": round(gu["gbs"], 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gu["gbs"] / rf.HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("gemm_gate_up_qwen05b_b32"),
+            "bytes_per_launch": gu["bytes"], "avg_launch_us": round(gu["us"], 3),
+            "isolated_launches": gu["launches"],
+            "in_step_event_interval_us": round(kern["gate_up_proj"]["us_per_launch"], 3),
+            "share_of_step": round(kern["gate_up_proj"]["us_per_step"] / tot, 3)}
+    # the paged decode attention the metric names, isolated launches of the
+    # op (inside the step the same kernel runs with RoPE and the cache write
+    # fused in)
+    attn_roof = {"kernel": "paged decode attention (attn_mfma_kernel)", "bound": "hbm",
+                 "achieved": round(att["gbs"], 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(att["gbs"] / rf.HBM_PEAK_GBS, 4),
+                 "traffic": recorded_traffic("attention_qwen05b_b32_ctx512"),
+                 "bytes_per_launch": att["bytes"], "avg_launch_us": round(att["us"], 3),
+                 "isolated_launches": att["launches"],
+                 "in_step_event_interval_us": round(kern["attention"]["us_per_launch"], 3),
+                 "share_of_step": round(kern["attention"]["us_per_step"] / tot, 3)}
     result = {
         "metric": "decode tokens/s @1 GPU; attn HBM GB/s and GEMM MFMA % of peak",
         "value": round(value, 1),
@@ -646,6 +688,7 @@ def main():
                    "kv_block": 16, "mode": "hipGraph replay", "rope_fused_into_attention": True,
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "attention_roofline": attn_roof,
         "calibration_copy_bytes": calib_bytes,
         "step": {"runs_ms": [round(r * 1e3, 4) for r in runs],
                  "runs_disagree_over_15pct": bool(max(runs) > 1.15 * min(runs)),

@@ -1,12 +1,13 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
-    python -m decode_step_06_amd.prof_summary trace TRACE_CSV --title T --cmd C [--kernel K --last N]
+    python -m decode_step_06_amd.prof_summary trace TRACE_CSV --title T --cmd C [--kernel K --last N ...]
     python -m decode_step_06_amd.prof_summary traffic --fetch FETCH_CSV --write WRITE_CSV --kernel K --last N
         --source SRC --calib-bytes B --algorithmic-bytes A --out OUT --cmd C [--cmd C ...]
 
 ``trace`` prints a markdown table of a ``--kernel-trace`` CSV (per kernel:
-dispatches, mean and total duration), and for kernel name K the mean over
-its last N dispatches (the benchmark's isolated back-to-back launches).
+dispatches, mean and total duration), and for each kernel name K given the
+mean over its last N dispatches (the benchmark's isolated back-to-back
+launches).
 
 ``traffic`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the
 same command into HBM bytes per launch of kernel K (mean over its last N
@@ -52,11 +53,12 @@ def trace(args):
         if "ns::" not in k:
             continue
         out.append(f"| `{k}` | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {sum(v) / 1e6:.3f} |")
-    if args.kernel:
-        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows if args.kernel in r["Kernel_Name"]]
-        tail = d[-args.last:] if args.last else d
+    for i, kern in enumerate(args.kernel):
+        last = args.last[i] if i < len(args.last) else 0
+        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows if kern in r["Kernel_Name"]]
+        tail = d[-last:] if last else d
         if tail:
-            out += ["", f"Last {len(tail)} dispatches of `{args.kernel}` (the isolated back-to-back launches): "
+            out += ["", f"Last {len(tail)} dispatches of `{kern}` (the isolated back-to-back launches): "
                         f"mean {sum(tail) / len(tail) / 1e3:.3f} us."]
     print("\n".join(out))
 
@@ -123,8 +125,8 @@ def main(argv=None):
     t.add_argument("csv")
     t.add_argument("--title", required=True)
     t.add_argument("--cmd", required=True)
-    t.add_argument("--kernel")
-    t.add_argument("--last", type=int, default=0)
+    t.add_argument("--kernel", action="append", default=[])
+    t.add_argument("--last", type=int, action="append", default=[])
     t.set_defaults(fn=trace)
     r = sub.add_parser("traffic")
     r.add_argument("--fetch", required=True)
