@@ -29,6 +29,8 @@ CASES = {
     "small-8waves": Workload("f8", SMALL, 6, ctx_range=(1, 200)),
     # <= 2047 items: 4 wavefronts (split-K QKV slices: steps of <= 256 rows)
     "small-4waves": Workload("f4", SMALL_H, 200, ctx_range=(1, 40)),
+    # more than 256 rows: the unsplit QKV projection's fp32 result
+    "small-4waves-300rows": Workload("f4b", SMALL_H, 300, ctx_range=(1, 40)),
     # 1024 items of 8 KV heads: 4 wavefronts
     "kv8-4waves": Workload("f1", KV8, 128, ctx_range=(1, 70)),
     # >= 2048 items: one wavefront per item, where the engine keeps the
