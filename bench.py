@@ -226,8 +226,8 @@ def step_kernels(h, b, stream, reps=5):
 
 
 def attention_isolated(h, b, maxb, stream, n=400):
-    """The step's attention (layer 0's cache, the step's rows and block
-    tables, the engine's launch shape) launched n times back to back on
+    """The step's attention (the layers' caches in turn, the step's rows and
+    block tables, the engine's launch shape) launched n times back to back on
     `stream`: HIP events around the loop give its average launch duration --
     the figure a kernel trace of this run reports for these launches."""
     s = h.shape
@@ -242,8 +242,14 @@ def attention_isolated(h, b, maxb, stream, n=400):
     wsb = ns.ns_op_attention_ws_bytes(h.desc, nd, maxb)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
 
+    # the launches cycle through the layers' caches (as the step does), so
+    # they stream from HBM rather than re-reading one layer's K/V from the
+    # last-level cache
+    layer_bytes = 2 * h.num_blocks * s.n_kv_heads * 16 * s.head_dim * 2
+    bases = [h.kv_mem.data_ptr() + l * layer_bytes for l in range(s.n_layers)]
+
     def launch(i):
-        ns.ns_op_attention(h.desc, nd, q_att.data_ptr(), h.kv_mem.data_ptr(), h.num_blocks, rowb.data_ptr(),
+        ns.ns_op_attention(h.desc, nd, q_att.data_ptr(), bases[i % len(bases)], h.num_blocks, rowb.data_ptr(),
                            pos.data_ptr(), bt.data_ptr(), maxb, o.data_ptr(), ws.data_ptr(), wsb, 0, stream)
 
     for i in range(20):
@@ -255,19 +261,22 @@ def attention_isolated(h, b, maxb, stream, n=400):
 
 
 def gate_up_isolated(h, b, stream, n=400):
-    """The step's gate-up projection (layer 0's K-slab-major weights, a
-    [rows, H] bf16 input, the SwiGLU epilogue: the same kernel and launch
-    shape as in the step) launched n times back to back on `stream`."""
+    """The step's gate-up projection (the layers' K-slab-major weights in
+    turn, a [rows, H] bf16 input, the SwiGLU epilogue: the same kernel and
+    launch shape as in the step) launched n times back to back on `stream`."""
     s = h.shape
     T, H, F = b.n_rows, s.hidden, s.ffn
     g = torch.Generator(device="cuda")
     g.manual_seed(6)
     A = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
     C = torch.empty((T, F), device="cuda", dtype=torch.bfloat16)
-    wgu = h.weights.t["layers"][0]["wgu"]
+    # the launches cycle through the layers' weights (as the step does), so
+    # they stream from HBM rather than from the last-level cache
+    wgu = [lw["wgu"].data_ptr() for lw in h.weights.t["layers"]]
 
     def launch(i):
-        ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), wgu.data_ptr(), C.data_ptr(), stream)
+        ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), wgu[i % len(wgu)], C.data_ptr(),
+                             stream)
 
     for i in range(20):
         launch(i)
