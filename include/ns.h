@@ -179,9 +179,11 @@ int ns_slot_map(const ns_kv* kv, int32_t n_tok, const int32_t* seq, const int32_
  *   attn_wg_cap: 0 = no cap; else the attention kernel runs at most this
  *     many workgroups (a persistent loop), the graph-safe way to bound the
  *     share of the GPU that attention takes.
- *   cu_mask_frac: 0 = none; else the second stream is created restricted to
- *     this fraction of the compute units (hipExtStreamCreateWithCUMask).
- *     Takes effect at engine creation only.
+ *   cu_mask_frac: must be 0 (NS_EINVAL otherwise).  Restricting the
+ *     second stream to a fraction of the compute units
+ *     (hipExtStreamCreateWithCUMask) is switched off: on its first GPU run
+ *     the masked stream's work did not complete, for a reason not yet
+ *     known.  attn_wg_cap bounds the attention's share instead.
  *   prefill_tiles: 0 = every row's attention on the decode kernel; 1 = rows
  *     taken in tiles of 32 from the start of each attention launch, and a
  *     tile of one sequence at 32 consecutive positions (a chunk of a prompt

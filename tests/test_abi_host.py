@@ -172,13 +172,15 @@ def test_engine_create_rejects_bad_arguments_without_a_gpu():
 
 def test_schedule_options_are_validated_without_a_gpu():
     """ns_sched is checked before anything else of the engine: flags must be
-    0 or 1, and RoPE fused into attention excludes prefill tiles."""
+    0 or 1, RoPE fused into attention excludes prefill tiles, and the
+    CU-masked second stream is switched off."""
     desc = ns.model_desc(LLAMA70B)
     kv = ns.ns_kv_create(desc, 8, 2, 4, None)
     try:
         w = ns.ns_weights()
         out = ctypes.c_void_p()
         for sched, msg in ((ns.make_sched(fuse_rope_attention=True, prefill_tiles=True), "exclude each other"),
+                           (ns.make_sched(overlap=True, cu_mask_frac=0.4), "cu_mask_frac is disabled"),
                            (ns.make_sched(decode_rows_first=True), None),
                            (ns.make_sched(fuse_rope_attention=True), None)):
             rc = ns.lib().ns_engine_create(ctypes.byref(desc), ctypes.byref(w), kv, None, 0, None, 0, 16,
