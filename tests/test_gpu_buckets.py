@@ -1,7 +1,9 @@
 """Bucketed graph capture through the C ABI: one graph per batch-size
 bucket, a batch replayed on the smallest bucket that holds it with the rest
 as padding rows.  The real rows equal an eager step of the same padded batch
-bit for bit, and the oracle within the bf16 bound."""
+bit for bit, and the oracle within the bf16 bound; also with RoPE fused into
+attention (padding rows belong to no sequence, so the fused schedule accepts
+them)."""
 import numpy as np
 import pytest
 import torch
@@ -20,7 +22,8 @@ SMALL = ModelShape("small", 2, 256, 8, 2, 64, 512, 1000, True, "bf16")
 BUCKETS = (1, 2, 4, 8, 16, 24)
 
 
-def test_bucketed_replay_pads_to_the_next_bucket():
+@pytest.mark.parametrize("fuse", [False, True], ids=["separate-rope", "rope-fused"])
+def test_bucketed_replay_pads_to_the_next_bucket(fuse):
     shape, S = SMALL, 24
     rng = np.random.default_rng(3)
     ctx = rng.integers(1, 90, size=S)
@@ -37,7 +40,7 @@ def test_bucketed_replay_pads_to_the_next_bucket():
     past_v = [od.round_bf16(prng.standard_normal((n_past, shape.n_kv_heads, shape.head_dim))).astype(np.float32)
               for _ in range(shape.n_layers)]
     dw = DeviceWeights.from_numpy(shape, weights)
-    h = create_engine(shape, dw, nblk, S, maxb, S, None, None)
+    h = create_engine(shape, dw, nblk, S, maxb, S, None, ns.make_sched(fuse_rope_attention=fuse))
     stream = torch.cuda.Stream()
     try:
         alloc_sequences(h, ctx)

@@ -45,7 +45,10 @@ def test_mix_graph_per_batch_size_matches_eager_and_oracle(qwen, B):
     maxb = blocks_for(b.seq_lens)
     say(f"mix B={B}: 24 layers, contexts {int(b.seq_lens.min())}..{int(b.seq_lens.max())}, "
         f"pool {b.num_blocks} blocks (fragmented), sampled rows {rows}")
-    h = create_engine(QWEN05B, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, None)
+    # the benchmark's schedule for these decode batches: RoPE and the cache
+    # write fused into attention
+    h = create_engine(QWEN05B, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order,
+                      ns.make_sched(fuse_rope_attention=True))
     stream = torch.cuda.Stream()
     try:
         alloc_sequences(h, b.seq_lens)
