@@ -82,6 +82,25 @@ def time_launches(fn, n, stream, reps=3):
     return statistics.median(out)
 
 
+def copy_ceiling(stream, nbytes=1 << 30, n=10):
+    """Achievable HBM rate of a plain device copy (torch's copy kernel, 1 GiB
+    read + 1 GiB written per launch) beside the 8 TB/s datasheet figure.  Run
+    after the library's kernels, so that the 256 MiB calibration copy stays
+    the largest copy before them in a profiled run."""
+    src = torch.empty(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    def launch(i):
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+
+    for i in range(3):
+        launch(i)
+    t = time_launches(launch, n, stream)
+    del src, dst
+    torch.cuda.synchronize()
+    return {"bytes_per_copy": 2 * nbytes, "gbs": 2 * nbytes / t / 1e9, "frac_of_peak": 2 * nbytes / t / 1e9 / rf.HBM_PEAK_GBS}
+
+
 # ---------------------------------------------------------------- the timed step
 def setup_step(wname):
     w = WORKLOADS[wname]
@@ -725,6 +744,7 @@ def main():
             result["llama70b_80l_b256"] = json.loads(json.dumps(llama80(stream), default=_jsonable))
         except Exception as e:  # report, do not hide
             result["llama70b_80l_b256"] = {"error": repr(e)}
+    result["hbm_copy_ceiling"] = {k: round(v, 4) for k, v in copy_ceiling(stream).items()}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, weights, b, maxb)
     print(json.dumps(result, default=_jsonable), flush=True)
