@@ -210,8 +210,9 @@ __global__ void __launch_bounds__(256) step_prologue_kernel(const T* __restrict_
 // ---------------------------------------------------------------- greedy sampling
 // Row argmax (lowest index among equal maxima; NaN never wins).  One
 // workgroup of 1024 threads per row; each thread keeps its best (value,
-// index) over a strided quarter of the row, four independent loads at a
-// time, then the pairs meet in wavefront shuffles and LDS.
+// index) over a strided share of the row -- eight 16-byte loads at a time
+// when the row is made of aligned 16-byte chunks, else four 4-byte loads --
+// then the pairs meet in wavefront shuffles and LDS.
 __device__ __forceinline__ bool argmax_better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
@@ -222,6 +223,33 @@ __global__ void __launch_bounds__(1024) argmax_rows_kernel(const float* __restri
   float bv = -INFINITY;
   int bi = INT_MAX;
   int i = threadIdx.x;
+  // The winner is the greatest (value, lower index) pair under
+  // argmax_better, whatever order the entries are visited in.  Rows of whole
+  // 16-byte chunks: eight 16-byte loads in flight per thread.
+  if ((V & 3) == 0 && (((uintptr_t)row) & 15) == 0) {
+    const f32x4_t* row4 = (const f32x4_t*)row;
+    const int V4 = V >> 2;
+    int j = threadIdx.x;
+    for (; j + 7 * 1024 < V4; j += 8 * 1024) {
+      f32x4_t c[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) c[k] = row4[j + k * 1024];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = 4 * (j + k * 1024) + e;
+          if (argmax_better(c[k][e], idx, bv, bi)) bv = c[k][e], bi = idx;
+        }
+    }
+    for (; j < V4; j += 1024) {
+      const f32x4_t c = row4[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (argmax_better(c[e], 4 * j + e, bv, bi)) bv = c[e], bi = 4 * j + e;
+    }
+    i = V;  // nothing left for the scalar loops
+  }
   for (; i + 3 * 1024 < V; i += 4 * 1024) {
     const float v0 = row[i], v1 = row[i + 1024], v2 = row[i + 2048], v3 = row[i + 3072];
     if (argmax_better(v0, i, bv, bi)) bv = v0, bi = i;
