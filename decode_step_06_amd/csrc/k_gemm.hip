@@ -770,9 +770,11 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
       run_big<EPI_PARTIAL, 128>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
     else if (kind == TILE_128)
       run_bf16<128, 128, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
-    // 64-wide K slabs where every split still gets one: half the slab
-    // syncs (0.5B-shaped mix: down projection 18.5 -> 14.6 us at 128 rows,
-    // 20 -> 16 us at 256; steps -4..-7%)
+    // Wide K slabs where every split still gets one: fewer slab syncs
+    // (0.5B-shaped mix, down projection at 128 rows: 32-wide 18.5 us, 64-wide
+    // 14.6 us, 128-wide 12.2 us)
+    else if (K % 128 == 0 && K / 128 >= splits)
+      run_bf16<64, 64, 128, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
     else if (K % 64 == 0 && K / 64 >= splits)
       run_bf16<64, 64, 64, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
     else run_bf16<64, 64, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
@@ -840,7 +842,13 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
     else run_bf16<128, 128, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
   } else {
     constexpr int BN64 = (EPI == EPI_SILU_MUL) ? 128 : 64;
-    if (k64) run_bf16<64, BN64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+    // SwiGLU tiles that fit one wave of workgroups take 128-wide K slabs
+    // (104 KB of LDS, one workgroup per CU): gate-up at 128 rows of the
+    // 0.5B shape 20.8 -> 16.8 us; with more tiles than CUs the second wave
+    // costs more than that saves (256 rows: 21 -> 27 us)
+    if (EPI == EPI_SILU_MUL && K % 128 == 0 && tile_count(TILE_64, M, N, false) <= kFillTarget)
+      run_bf16<64, BN64, 128, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+    else if (k64) run_bf16<64, BN64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
     else run_bf16<64, BN64, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
   }
 }
