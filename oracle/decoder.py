@@ -29,8 +29,15 @@ Storage points (``emulate_bf16``): a bf16 model stores these values as bf16
 points: weights and embedding (already on the grid in the inputs), normalised
 activations, rotated q, the K/V written to the cache, the attention output,
 and the SwiGLU activation.  The residual stream and the logits stay wide.
+
+Precision (``precision``): "f64" (the default) computes every value in
+float64 and is the mode every parity check uses; "f32" is the same code on
+float32 arrays (angles still in float64), for timing the oracle as a CPU
+baseline only.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -59,21 +66,21 @@ def round_bf16(a):
     return out
 
 
-def _store(a, emulate):
-    return round_bf16(a) if emulate else np.asarray(a, dtype=np.float64)
+def _store(a, emulate, ft=np.float64):
+    return (round_bf16(a) if emulate else np.asarray(a, dtype=np.float64)).astype(ft, copy=False)
 
 
 # ---------------------------------------------------------------- operators
-def rmsnorm(x, gain, eps):
+def rmsnorm(x, gain, eps, ft=np.float64):
     """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * gain."""
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=ft)
     ms = np.mean(x * x, axis=-1, keepdims=True)
-    return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=np.float64)
+    return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=ft)
 
 
-def linear(x, w):
+def linear(x, w, ft=np.float64):
     """y = x W^T with W stored row-major as [out, in] (no bias)."""
-    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+    return np.asarray(x, dtype=ft) @ np.asarray(w, dtype=ft).T
 
 
 def rope_angles(pos, head_dim, base):
@@ -87,15 +94,15 @@ def rope_angles(pos, head_dim, base):
     return np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]
 
 
-def apply_rope(x, angles):
+def apply_rope(x, angles, ft=np.float64):
     """Rotate-half RoPE: the pair (j, j + d/2) of each head turns by angle j.
 
     x: [T, heads, d]; angles: [T, d/2].
     """
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=ft)
     half = x.shape[-1] // 2
-    c = np.cos(angles)[:, None, :]
-    s = np.sin(angles)[:, None, :]
+    c = np.cos(angles).astype(ft)[:, None, :]
+    s = np.sin(angles).astype(ft)[:, None, :]
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
@@ -112,13 +119,13 @@ def attention_row(q, keys, values, group):
     """
     nq, d = q.shape
     n = keys.shape[0]
-    o = np.zeros((nq, d))
-    probs = np.zeros((nq, n))
+    o = np.zeros((nq, d), dtype=q.dtype)
+    probs = np.zeros((nq, n), dtype=q.dtype)
     if n == 0:
         return o, probs
     for h in range(nq):
         g = h // group
-        scores = keys[:, g, :] @ q[h] / np.sqrt(d)
+        scores = keys[:, g, :] @ q[h] / math.sqrt(d)
         w = np.exp(scores - scores.max())
         w = w / w.sum()
         probs[h] = w
@@ -134,11 +141,11 @@ class OracleKV:
     touches.
     """
 
-    def __init__(self, n_layers, num_blocks, n_kv, head_dim, block=BLOCK):
+    def __init__(self, n_layers, num_blocks, n_kv, head_dim, block=BLOCK, dtype=np.float64):
         n = num_blocks * block
         self.block = block
-        self.k = [np.full((n, n_kv, head_dim), np.nan) for _ in range(n_layers)]
-        self.v = [np.full((n, n_kv, head_dim), np.nan) for _ in range(n_layers)]
+        self.k = [np.full((n, n_kv, head_dim), np.nan, dtype=dtype) for _ in range(n_layers)]
+        self.v = [np.full((n, n_kv, head_dim), np.nan, dtype=dtype) for _ in range(n_layers)]
 
     def write(self, layer, slots, k, v):
         """Cache write at each row's slot (slot < 0: padding row, nothing written)."""
@@ -161,35 +168,37 @@ class Oracle:
     the input generator (per-layer attn_norm, wqkv, wo, mlp_norm, wgu, wdown;
     final_norm, embed, lm_head)."""
 
-    def __init__(self, model, weights, emulate_bf16=None):
+    def __init__(self, model, weights, emulate_bf16=None, precision="f64"):
         self.m = model
         self.w = weights
         self.emulate = (model.dtype == "bf16") if emulate_bf16 is None else bool(emulate_bf16)
+        assert precision in ("f64", "f32")
+        self.ft = np.float64 if precision == "f64" else np.float32
 
     # -- pieces, each one step of the layer --------------------------------
     def embed(self, tokens):
-        return np.asarray(self.w["embed"], dtype=np.float64)[np.asarray(tokens)]
+        return np.asarray(self.w["embed"])[np.asarray(tokens)].astype(self.ft)
 
     def qkv(self, layer, x, pos):
         """Pre-attention half up to the cache write: norm, QKV projection, RoPE."""
-        m, lw = self.m, self.w["layers"][layer]
+        m, lw, ft = self.m, self.w["layers"][layer], self.ft
         nq, nkv, d = m.n_q_heads, m.n_kv_heads, m.head_dim
-        h = _store(rmsnorm(x, lw["attn_norm"], m.rms_eps), self.emulate)
-        y = linear(h, lw["wqkv"])
+        h = _store(rmsnorm(x, lw["attn_norm"], m.rms_eps, ft), self.emulate, ft)
+        y = linear(h, lw["wqkv"], ft)
         T = x.shape[0]
         q = y[:, : nq * d].reshape(T, nq, d)
         k = y[:, nq * d: (nq + nkv) * d].reshape(T, nkv, d)
         v = y[:, (nq + nkv) * d:].reshape(T, nkv, d)
         ang = rope_angles(pos, d, m.rope_base)
-        q = _store(apply_rope(q, ang), self.emulate)
-        k = _store(apply_rope(k, ang), self.emulate)
-        v = _store(v, self.emulate)
+        q = _store(apply_rope(q, ang, ft), self.emulate, ft)
+        k = _store(apply_rope(k, ang, ft), self.emulate, ft)
+        v = _store(v, self.emulate, ft)
         return q, k, v
 
     def attend(self, layer, cache, tables, q, row_seq, row_pos):
         m = self.m
         T = q.shape[0]
-        o = np.zeros((T, m.n_q_heads, m.head_dim))
+        o = np.zeros((T, m.n_q_heads, m.head_dim), dtype=self.ft)
         for t in range(T):
             s = int(row_seq[t])
             if s < 0:
@@ -197,22 +206,22 @@ class Oracle:
             n = int(row_pos[t]) + 1
             keys, values = cache.gather(layer, tables[s], n)
             o[t], _ = attention_row(q[t], keys, values, m.n_q_heads // m.n_kv_heads)
-        return _store(o.reshape(T, -1), self.emulate)
+        return _store(o.reshape(T, -1), self.emulate, self.ft)
 
     def post_attention(self, layer, x, o):
         """O projection + residual, then the SwiGLU MLP + residual."""
-        m, lw = self.m, self.w["layers"][layer]
-        x = x + linear(o, lw["wo"])
-        h2 = _store(rmsnorm(x, lw["mlp_norm"], m.rms_eps), self.emulate)
-        gu = linear(h2, lw["wgu"])
+        m, lw, ft = self.m, self.w["layers"][layer], self.ft
+        x = x + linear(o, lw["wo"], ft)
+        h2 = _store(rmsnorm(x, lw["mlp_norm"], m.rms_eps, ft), self.emulate, ft)
+        gu = linear(h2, lw["wgu"], ft)
         F = m.ffn
-        act = _store(silu(gu[:, :F]) * gu[:, F:], self.emulate)
-        return x + linear(act, lw["wdown"])
+        act = _store(silu(gu[:, :F]) * gu[:, F:], self.emulate, ft)
+        return x + linear(act, lw["wdown"], ft)
 
     def head(self, x):
-        m = self.m
-        hf = _store(rmsnorm(x, self.w["final_norm"], m.rms_eps), self.emulate)
-        return linear(hf, self.w["lm_head"])
+        m, ft = self.m, self.ft
+        hf = _store(rmsnorm(x, self.w["final_norm"], m.rms_eps, ft), self.emulate, ft)
+        return linear(hf, self.w["lm_head"], ft)
 
     # -- whole step --------------------------------------------------------
     def step(self, cache, tables, row_seq, row_pos, tokens=None, x=None, nano_splits=None):
@@ -231,7 +240,7 @@ class Oracle:
         T = row_seq.shape[0]
         if x is None:
             x = self.embed(tokens)
-        x = np.array(x, dtype=np.float64)
+        x = np.array(x, dtype=self.ft)
         bounds = [0]
         for n in (nano_splits or [T]):
             bounds.append(bounds[-1] + int(n))
@@ -257,6 +266,6 @@ def fill_past(cache, tables, past_seq, past_pos, past_k, past_v):
     """Write the already-cached context (positions before this step) into the
     oracle cache through the block tables."""
     slots = [slot_of(tables[int(s)], int(p), cache.block) for s, p in zip(past_seq, past_pos)]
+    dt = cache.k[0].dtype if cache.k else np.float64
     for layer in range(len(past_k)):
-        cache.write(layer, slots, np.asarray(past_k[layer], dtype=np.float64),
-                    np.asarray(past_v[layer], dtype=np.float64))
+        cache.write(layer, slots, np.asarray(past_k[layer], dtype=dt), np.asarray(past_v[layer], dtype=dt))

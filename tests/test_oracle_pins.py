@@ -338,3 +338,34 @@ def test_padding_row_changes_nothing_and_writes_nothing():
         rows = np.unique(np.where(changed)[0])
         expect = sorted(okv.slot_map(tables, b.row_seq, b.row_pos))
         assert sorted(rows.tolist()) == expect
+
+
+# ---------------------------------------------------------------- float32 timing mode
+def test_float32_mode_agrees_with_float64_to_float32_accuracy():
+    """The fp32 mode (timing only) runs the same code on float32 arrays: on the
+    tiny fp32 layer it agrees with the float64 mode to float32 accuracy, and on
+    a bf16 stack to within a few bf16 roundings that land on the other side."""
+    w = Workload("tiny_b4", TINY, 4, ctx_range=(5, 40), num_blocks=16)
+    weights = gen_weights(TINY, seed=0)
+    b = gen_batch(w)
+    alloc = okv.BlockAllocator(b.num_blocks, b.free_order, b.n_seqs, 4)
+    for s, n in enumerate(b.seq_lens):
+        alloc.alloc(s, int(n))
+    tables = alloc.table_rows()
+    out = {}
+    for prec, dt in (("f64", np.float64), ("f32", np.float32)):
+        cache = od.OracleKV(1, b.num_blocks, TINY.n_kv_heads, TINY.head_dim, dtype=dt)
+        od.fill_past(cache, tables, b.past_seq, b.past_pos, b.past_k, b.past_v)
+        out[prec] = od.Oracle(TINY, weights, precision=prec).step(cache, tables, b.row_seq, b.row_pos, x=b.x)
+    assert out["f32"].dtype == np.float32 and out["f64"].dtype == np.float64
+    rel = np.linalg.norm(out["f32"] - out["f64"]) / np.linalg.norm(out["f64"])
+    assert 1e-9 < rel < 1e-5
+
+    model, weights, b, tables = _small_bf16_case()
+    res = {}
+    for prec, dt in (("f64", np.float64), ("f32", np.float32)):
+        cache = od.OracleKV(model.n_layers, b.num_blocks, model.n_kv_heads, model.head_dim, dtype=dt)
+        od.fill_past(cache, tables, b.past_seq, b.past_pos, b.past_k, b.past_v)
+        res[prec] = od.Oracle(model, weights, precision=prec).step(cache, tables, b.row_seq, b.row_pos, x=b.x)
+    rel = np.linalg.norm(res["f32"] - res["f64"]) / np.linalg.norm(res["f64"])
+    assert res["f32"].dtype == np.float32 and rel < 5e-3
