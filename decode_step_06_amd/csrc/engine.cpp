@@ -862,6 +862,18 @@ int ns_op_gemm_packed(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t 
   return op_gemm(dtype, epi, M, N, K, A, B, C, stream, true);
 }
 
+int ns_op_rmsnorm(int32_t dtype, int32_t n_rows, int32_t hidden, const float* x, const void* gain, float eps, void* out,
+                  void* stream) {
+  if (dtype != NS_F32 && dtype != NS_BF16) NS_FAIL(NS_EINVAL, "bad dtype");
+  if (n_rows < 0 || hidden <= 0) NS_FAIL(NS_EINVAL, "bad sizes");
+  if (!(eps >= 0.f)) NS_FAIL(NS_EINVAL, "eps must be >= 0");
+  if (n_rows > 0 && (!x || !gain || !out)) NS_FAIL(NS_EINVAL, "null argument");
+  ns::launch_rmsnorm(dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32, x, gain, out, n_rows, hidden, eps,
+                     (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return NS_OK;
+}
+
 int ns_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols, void* stream) {
   if (!src || !dst || src == dst) NS_FAIL(NS_EINVAL, "null or equal source and destination");
   if (rows < 1 || cols < 32 || cols % 32 != 0) NS_FAIL(NS_EINVAL, "bad shape [%d, %d]", rows, cols);
@@ -880,10 +892,10 @@ size_t ns_op_attention_ws_bytes(const ns_model_desc* desc, int32_t n_rows, int32
 }
 
 namespace {
-int op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
-                 int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
-                 int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap, void* stream,
-                 bool tiles) {
+// Argument checks shared by the attention ops (nothing enqueued).
+int check_attention_args(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                         int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
+                         int32_t max_blocks_per_seq, void* out, int32_t wg_cap) {
   int rc = ns::check_desc(desc);
   if (rc) return rc;
   if (n_rows <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || wg_cap < 0) NS_FAIL(NS_EINVAL, "bad sizes");
@@ -892,6 +904,18 @@ int op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, c
   const int dt = desc->dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
   if (!ns::attention_supported(dt, desc->head_dim, G))
     NS_FAIL(NS_EINVAL, "no attention kernel for head_dim %d, group %d", desc->head_dim, G);
+  return NS_OK;
+}
+
+int op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                 int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
+                 int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap, void* stream,
+                 bool tiles) {
+  int rc = check_attention_args(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab,
+                                max_blocks_per_seq, out, wg_cap);
+  if (rc) return rc;
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  const int dt = desc->dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
   const size_t need = ns_op_attention_ws_bytes(desc, n_rows, max_blocks_per_seq);
   if (ws_bytes < need || (need > 0 && !ws)) NS_FAIL(NS_ESHAPE, "workspace of %zu bytes < %zu", ws_bytes, need);
   ns::AttnArgs a;

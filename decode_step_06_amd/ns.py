@@ -92,6 +92,7 @@ SIGNATURES = {
     "ns_op_gemm": (C.c_int, [_I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "ns_op_gemm_packed": (C.c_int, [_I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "ns_pack_weight": (C.c_int, [_P, _P, _I, _I, _P]),
+    "ns_op_rmsnorm": (C.c_int, [_I, _I, _I, _P, _P, C.c_float, _P, _P]),
     "ns_op_attention_ws_bytes": (C.c_size_t, [C.POINTER(ns_model_desc), _I, _I]),
     "ns_op_attention": (C.c_int, [C.POINTER(ns_model_desc), _I, _P, _P, _I, _P, _P, _P, _I, _P, _P, C.c_size_t,
                                   _I, _P]),
@@ -330,6 +331,10 @@ def ns_op_gemm_packed(dtype: int, epi: int, M: int, N: int, K: int, A: int, B: i
     _check(lib().ns_op_gemm_packed(dtype, epi, M, N, K, A, B, Cp, _stream_ptr(stream)))
 
 
+def ns_op_rmsnorm(dtype: int, n_rows: int, hidden: int, x: int, gain: int, eps: float, out: int, stream=None) -> None:
+    _check(lib().ns_op_rmsnorm(dtype, n_rows, hidden, x, gain, eps, out, _stream_ptr(stream)))
+
+
 def ns_pack_weight(src: int, dst: int, rows: int, cols: int, stream=None) -> None:
     _check(lib().ns_pack_weight(src, dst, rows, cols, _stream_ptr(stream)))
 
@@ -348,3 +353,4 @@ def ns_op_attention_prefill(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq,
                             out, ws, ws_bytes, wg_cap=0, stream=None) -> None:
     _check(lib().ns_op_attention_prefill(C.byref(desc), n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab,
                                          max_blocks_per_seq, out, ws, ws_bytes, wg_cap, _stream_ptr(stream)))
+

@@ -371,6 +371,15 @@ int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, cons
 int ns_op_gemm_packed(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A,
                       const void* B, void* C, void* stream);
 
+/* RMSNorm of each row (nanoserve notes, changes table: the fused RMSNorm;
+ * the final norm in front of the LM head): out[r] = x[r] / sqrt(mean(x[r]^2)
+ * + eps) * gain, computed in fp32 and stored as dtype.  x: device fp32
+ * [n_rows, hidden]; gain: device [hidden] (dtype); out: device [n_rows,
+ * hidden] (dtype).  The same kernel the step uses for a norm with no split-K
+ * slices to add.  Errors: NS_EINVAL (bad dtype or sizes, eps < 0, null
+ * pointer with n_rows > 0). */
+int ns_op_rmsnorm(int32_t dtype, int32_t n_rows, int32_t hidden, const float* x, const void* gain, float eps,
+                  void* out, void* stream);
 /* Convert a row-major bf16 matrix [rows, cols] (device) into the K-slab-major
  * layout of ns_weights (device, a separate buffer of the same size), on
  * `stream`.  Errors: NS_EINVAL (null or equal pointers, rows < 1, cols not a

@@ -161,3 +161,121 @@ def oracle_sampled(shape, weights, batch: Batch, rows, keep, kept_k, kept_v, emu
     tok = None if batch.tokens is None else batch.tokens[rows]
     x = None if batch.x is None else batch.x[rows]
     return orc.step(cache, tables, rs, batch.row_pos[rows], tokens=tok, x=x)
+
+
+# ---------------------------------------------------------------- teacher-forced per-layer parity
+def one_layer_shape(shape: ModelShape) -> ModelShape:
+    """Layer l of a stack on its own: one layer, no vocabulary (hidden state in
+    and out)."""
+    from dataclasses import replace
+    return replace(shape, name=shape.name + "_1layer", n_layers=1, vocab=0, tied=False)
+
+
+class LayerChain:
+    """Layer l of a stack run alone on the GPU: a one-layer engine without a
+    vocabulary over the stack's weights of layer l and layer l's part of the
+    stack's KV memory (a stack's cache is its layers' regions back to back),
+    with a KV manager that holds the same block tables.  Each call runs one
+    eager step of that engine in the schedule given."""
+
+    def __init__(self, h, b: Batch, sched, stream):
+        import ctypes
+        self._ct = ctypes
+        self.h, self.b, self.sched, self.stream = h, b, sched, stream
+        self.shape1 = one_layer_shape(h.shape)
+        self.desc1 = ns.model_desc(self.shape1)
+        self.kv1 = ns.ns_kv_create(self.desc1, h.num_blocks, h.max_seqs, h.max_blocks, b.free_order)
+        for s, n in enumerate(b.seq_lens):
+            ns.ns_kv_alloc(self.kv1, s, int(n))
+        t1 = ns.ns_kv_block_table(self.kv1, h.max_seqs, h.max_blocks)
+        t0 = ns.ns_kv_block_table(h.kv, h.max_seqs, h.max_blocks)
+        assert np.array_equal(t0, t1), "one-layer KV manager holds other block tables"
+        self.layer_bytes = ns.ns_kv_bytes(self.desc1, h.num_blocks)
+        assert self.layer_bytes * h.shape.n_layers == h.kv_mem.numel()
+        self.ws_bytes = ns.ns_workspace_bytes(self.desc1, h.max_tokens, h.max_blocks)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def run(self, layer: int, x: torch.Tensor) -> torch.Tensor:
+        """Layer `layer` of the stack on the fp32 hidden state x [T, H]."""
+        lw = self.h.weights.t["layers"][layer]
+        names = ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wdown")
+        arrs = {n: (self._ct.c_void_p * 1)(lw[n].data_ptr()) for n in names}
+        w = ns.ns_weights(*[arrs[n] for n in names], None, None, None)
+        eng = ns.ns_engine_create(self.desc1, w, self.kv1, self.h.kv_mem.data_ptr() + layer * self.layer_bytes,
+                                  self.layer_bytes, self.ws.data_ptr(), self.ws_bytes, self.h.max_tokens, self.sched)
+        try:
+            x = x.contiguous()
+            out = torch.full_like(x, float("nan"))
+            ns.ns_decode_step(eng, ns.Batch(self.b.row_seq, self.b.row_pos, None, x), out.data_ptr(), self.stream)
+            self.stream.synchronize()
+        finally:
+            ns.ns_engine_destroy(eng)
+        return out
+
+    def head(self, x: torch.Tensor) -> torch.Tensor:
+        """Final RMSNorm + LM head of the stack on the fp32 hidden state x."""
+        s, t = self.h.shape, self.h.weights.t
+        T = x.shape[0]
+        hf = torch.empty((T, s.hidden), dtype=torch.bfloat16, device="cuda")
+        logits = torch.full((T, s.vocab), float("nan"), device="cuda")
+        ns.ns_op_rmsnorm(ns.NS_BF16, T, s.hidden, x.contiguous().data_ptr(), t["final_norm"].data_ptr(), s.rms_eps,
+                         hf.data_ptr(), self.stream)
+        ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_STORE, T, s.vocab, s.hidden, hf.data_ptr(),
+                             t["lm_head"].data_ptr(), logits.data_ptr(), self.stream)
+        self.stream.synchronize()
+        return logits
+
+    def close(self):
+        if self.kv1:
+            ns.ns_kv_destroy(self.kv1)
+            self.kv1 = None
+
+
+def check_layer(out, ref, x_in, what, ref32=None, max_abs_bound=None):
+    """The bound for bf16 activations on a layer's output hidden state and on
+    its change (the layer's attention and MLP contributions): relative L2 <=
+    5e-3, and max abs <= 2e-2.
+
+    ``ref32``: the oracle's float32-arithmetic run of the same layer (same
+    bf16 storage points) on the same rows.  Two correct fp32 implementations
+    of these storage points differ wherever a value lands on the other side of
+    a bf16 rounding boundary, and such a difference scales with the
+    activation: on hidden states of RMS well above 1 (a LLaMA-70B-shaped
+    layer, RMS about 7.6) the oracle's own float32 run is more than 2e-2 from
+    its float64 run at the worst element.  The max-abs bound is then 1.5 times
+    that measured distance; the relative L2 bound never moves.
+
+    ``max_abs_bound``: a max-abs bound the caller sets instead (a stack's
+    layers checked against one bound pooled over all of them); returns
+    (rel_l2, max_abs, change rel_l2, the oracle's own f32-vs-f64 max abs)."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    x_in = np.asarray(x_in, np.float64)
+    assert np.isfinite(out).all(), f"{what}: non-finite GPU output"
+    r, m = rel_l2(out, ref), max_abs(out, ref)
+    rd = rel_l2(out - x_in, ref - x_in)
+    tr, tm = TOL["bf16"]
+    extra = ""
+    d32 = 0.0
+    if ref32 is not None:
+        d32 = max_abs(ref32, ref)
+        tm = max(tm, 1.5 * d32)
+        extra = f" (oracle f32 vs f64: rel_l2={rel_l2(ref32, ref):.2e} max_abs={d32:.2e})"
+    if max_abs_bound is not None:
+        tm = max_abs_bound
+    say(f"  {what}: rel_l2={r:.2e} max_abs={m:.2e} change rel_l2={rd:.2e}{extra}")
+    assert r <= tr and m <= tm and rd <= tr, f"{what}: rel_l2 {r:.3e} max_abs {m:.3e} change rel_l2 {rd:.3e}"
+    return r, m, rd, d32
+
+
+def oracle_one_layer(shape, lw, tables, num_blocks, past_seq, past_pos, past_k_l, past_v_l, row_seq, row_pos, x,
+                     precision="f64", emulate=None):
+    """The oracle's layer alone (bf16 storage points for a bf16 model) on
+    hidden input x, with that layer's cached context."""
+    s1 = one_layer_shape(shape)
+    ft = np.float64 if precision == "f64" else np.float32
+    cache = od.OracleKV(1, num_blocks, shape.n_kv_heads, shape.head_dim, dtype=ft)
+    od.fill_past(cache, tables, past_seq, past_pos, [past_k_l], [past_v_l])
+    out = od.Oracle(s1, {"layers": [lw]}, emulate_bf16=emulate, precision=precision).step(
+        cache, tables, row_seq, row_pos, x=np.asarray(x, ft))
+    return out.astype(np.float64)

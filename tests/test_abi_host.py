@@ -196,3 +196,11 @@ def test_schedule_options_are_validated_without_a_gpu():
         assert rc == ns.NS_EINVAL and "decode_rows_first" in ns.lib().ns_last_error().decode()
     finally:
         ns.ns_kv_destroy(kv)
+
+
+def test_op_rmsnorm_validates_before_enqueue():
+    L = ns.lib()
+    assert L.ns_op_rmsnorm(7, 4, 8, None, None, 1e-6, None, None) == ns.NS_EINVAL   # bad dtype
+    assert L.ns_op_rmsnorm(ns.NS_BF16, 4, 0, None, None, 1e-6, None, None) == ns.NS_EINVAL  # hidden 0
+    assert L.ns_op_rmsnorm(ns.NS_BF16, 4, 8, None, None, -1.0, None, None) == ns.NS_EINVAL  # eps < 0
+    assert L.ns_op_rmsnorm(ns.NS_BF16, 4, 8, None, None, 1e-6, None, None) == ns.NS_EINVAL  # null pointers

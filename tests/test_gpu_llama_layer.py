@@ -2,7 +2,14 @@
 decode rows at context 1024, then three fresh prefill chunks of 512),
 nano-batched 768/1280 with four QKV nano-ops and attention overlapped on the
 second stream, in the launch configuration the benchmark times.  The oracle
-computes sampled rows one by one."""
+computes 64 sampled rows one by one: 16 decode rows spread over the 512, and
+16 rows of each prompt chunk spread over its positions 0..511 (the first and
+the last included).  Each sampled row's output hidden state and its change
+must be within relative L2 <= 5e-3 of the oracle, and within max abs <= 2e-2,
+or 1.5 times the distance between the oracle's own float32-arithmetic and
+float64 runs on the same rows where that is larger: at this layer's output
+RMS (about 7.6) two correct fp32 implementations of the bf16 storage points
+are about 0.14 apart at the worst element."""
 import numpy as np
 import pytest
 import torch
@@ -10,15 +17,43 @@ import torch
 from decode_step_06_amd import ns
 from decode_step_06_amd.configs import WORKLOADS
 from decode_step_06_amd.inputs import gen_batch, gen_weights
-from gpu_helpers import Case, assert_close, say
+from gpu_helpers import Case, check_layer, say
 from oracle import decoder as od
 from oracle import kvcache as okv
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE_ROWS = [0, 1, 255, 511,                 # decode rows (context 1024)
-               512, 513, 812, 1023,            # first prefill chunk: positions 0, 1, 300, 511
-               1024 + 17, 1536 + 511]          # later chunks
+_SPREAD = np.linspace(0, 511, 16).round().astype(int)
+SAMPLE_ROWS = np.concatenate([_SPREAD] + [512 * (c + 1) + _SPREAD for c in range(3)])
+
+
+def _oracle_rows(shape, weights, b, tables, rows, precision):
+    """The oracle's layer output for `rows`: every row's K/V enter the cache
+    (prompt rows read their chunk's earlier rows), then each sampled row's
+    attention over its context and the rest of the layer."""
+    orc = od.Oracle(shape, weights, precision=precision)
+    ft = orc.ft
+    x = b.x.astype(ft)
+    q, k, v = orc.qkv(0, x, b.row_pos)
+    slots = okv.slot_map(tables, b.row_seq, b.row_pos)
+    # cached context of the decode rows plus this step's K/V, by slot
+    kcache, vcache = {}, {}
+    psl = okv.slot_map(tables, b.past_seq, b.past_pos)
+    for i, s in enumerate(psl):
+        kcache[s] = b.past_k[0][i]
+        vcache[s] = b.past_v[0][i]
+    for i, s in enumerate(slots):
+        kcache[s] = k[i]
+        vcache[s] = v[i]
+    o = np.zeros((len(rows), shape.n_q_heads, shape.head_dim), dtype=ft)
+    for j, t in enumerate(rows):
+        s, p = int(b.row_seq[t]), int(b.row_pos[t])
+        sl = [okv.slot_of(tables[s], i) for i in range(p + 1)]
+        keys = np.stack([kcache[z] for z in sl]).astype(ft)
+        vals = np.stack([vcache[z] for z in sl]).astype(ft)
+        o[j], _ = od.attention_row(q[t], keys, vals, shape.group)
+    o = od.round_bf16(o.reshape(len(rows), -1)).astype(ft)
+    return orc.post_attention(0, x[rows], o).astype(np.float64)
 
 
 @pytest.mark.parametrize("prefill_tiles", [True, False], ids=["prefill-tiles", "decode-kernel-only"])
@@ -36,24 +71,14 @@ def test_llama70b_layer_dense_batch_sampled_rows(prefill_tiles):
         got = c.step().cpu().numpy()
         assert np.isfinite(got).all()
         say("  oracle for sampled rows")
-        orc = od.Oracle(shape, weights)
         alloc = okv.BlockAllocator(b.num_blocks, b.free_order, b.n_seqs, c.maxb)
         for s, n in enumerate(b.seq_lens):
             alloc.alloc(s, int(n))
         tables = alloc.table_rows()
         np.testing.assert_array_equal(c.tables(), np.array(tables, dtype=np.int32))
-        x = b.x.astype(np.float64)
-        q, k, v = orc.qkv(0, x, b.row_pos)          # every row's K/V enters the cache
-        slots = okv.slot_map(tables, b.row_seq, b.row_pos)
-        # cached context of the decode rows plus this step's K/V, by slot
-        kcache, vcache = {}, {}
-        psl = okv.slot_map(tables, b.past_seq, b.past_pos)
-        for i, s in enumerate(psl):
-            kcache[s] = b.past_k[0][i]
-            vcache[s] = b.past_v[0][i]
-        for i, s in enumerate(slots):
-            kcache[s] = k[i]
-            vcache[s] = v[i]
+        rows = np.array(SAMPLE_ROWS)
+        ref = _oracle_rows(shape, weights, b, tables, rows, "f64")
+        ref32 = _oracle_rows(shape, weights, b, tables, rows, "f32")
         if prefill_tiles:
             # decode rows' attention queued last, prompt nano-batch's projections
             # first: the same work in another order, bit-exact
@@ -61,16 +86,7 @@ def test_llama70b_layer_dense_batch_sampled_rows(prefill_tiles):
                                                           overlap=True, prefill_tiles=True, decode_rows_first=True))
             c.reset_cache()
             np.testing.assert_array_equal(c.step().cpu().numpy(), got)
-        rows = np.array(SAMPLE_ROWS)
-        o = np.zeros((len(rows), shape.n_q_heads, shape.head_dim))
-        for j, t in enumerate(rows):
-            s, p = int(b.row_seq[t]), int(b.row_pos[t])
-            sl = [okv.slot_of(tables[s], i) for i in range(p + 1)]
-            keys = np.stack([kcache[z] for z in sl]).astype(np.float64)
-            vals = np.stack([vcache[z] for z in sl]).astype(np.float64)
-            o[j], _ = od.attention_row(q[t], keys, vals, shape.group)
-        o = od.round_bf16(o.reshape(len(rows), -1))
-        ref = orc.post_attention(0, x[rows], o)
-        assert_close(got[rows], ref, "bf16", "llama70b layer, sampled rows")
+        assert len(set(rows.tolist())) == 64
+        check_layer(got[rows], ref, b.x[rows], "llama70b layer, 64 sampled rows", ref32=ref32)
     finally:
         c.close()
