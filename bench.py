@@ -46,7 +46,8 @@ from decode_step_06_amd.inputs import gen_batch, gen_weights  # noqa: E402
 from decode_step_06_amd.runner import (DeviceWeights, alloc_sequences, blocks_for, create_engine,  # noqa: E402
                                        fill_past, fill_past_random_on_device)
 
-WORKLOAD = "qwen05b_b32_ctx512"
+HEADLINE = "llama70b_80l_b256"
+SMALL = "qwen05b_b32_ctx512"
 
 
 def decode_sched(**kw):
@@ -546,12 +547,73 @@ def bucket_capture(stream, dw, steps=50):
     return res
 
 
-# ---------------------------------------------------------------- 80-layer 70B
-def llama80(stream, steps=10, warm_seconds=2.0):
-    """LLaMA-2-70B-shaped 80-layer step, 256 sequences at contexts uniform in
-    512..1536, weights and cache drawn on the device; the graph replayed with
-    the two-way nano-batch overlap and without it."""
-    w = WORKLOADS["llama70b_80l_b256"]
+# ---------------------------------------------------------------- GPU clock
+def gfx_clock_reader():
+    """A function returning the shader clock (MHz) of the GPU torch uses, read
+    from the amd-smi metrics on the host, or None when it cannot be read."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        hdl = handles[0]
+        if len(handles) > 1:
+            bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+            for x in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(x)
+                if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                    hdl = x
+    except Exception:
+        return None
+
+    def read():
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(hdl)
+        except Exception:
+            return None
+        cur = m.get("current_gfxclks")
+        if isinstance(cur, (list, tuple)):
+            vals = [v for v in cur if isinstance(v, (int, float)) and 0 < v < 10000]
+            if vals:
+                return float(np.mean(vals))
+        for k in ("average_gfxclk_frequency", "current_gfxclk"):
+            v = m.get(k)
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                return float(v)
+        return None
+    return read
+
+
+def sample_clock(enqueue, stream, seconds=0.8):
+    """Shader clock while the GPU runs the work `enqueue()` queues (a second
+    or more of graph replays): sampled on the host every 50 ms."""
+    read = gfx_clock_reader()
+    if read is None:
+        return None
+    enqueue()
+    time.sleep(0.2)
+    vals = []
+    t_end = time.time() + seconds
+    while time.time() < t_end:
+        v = read()
+        if v is not None:
+            vals.append(v)
+        time.sleep(0.05)
+    stream.synchronize()
+    if not vals:
+        return None
+    return {"mhz_median": float(np.median(vals)), "mhz_min": float(min(vals)), "mhz_max": float(max(vals)),
+            "samples": len(vals), "source": "amd-smi gpu metrics (shader clock), during graph replays"}
+
+
+# ---------------------------------------------------------------- the headline: 80-layer 70B step
+def llama80(args, stream):
+    """LLaMA-2-70B-shaped 80-layer decode step, 256 sequences at contexts
+    uniform in 512..1536, weights (138 GB) and cache (88 GB) drawn on the
+    device: the whole step replayed as one hipGraph (the unsplit schedule),
+    with and without the two-way nano-batch overlap; the paged attention and
+    the gate-up projection launched alone over the layers' caches and
+    weights for their rooflines."""
+    w = WORKLOADS[HEADLINE]
     s = w.model
     torch.cuda.empty_cache()
     b = gen_batch(w, with_past=False, pool_slack=1.02)
@@ -559,48 +621,155 @@ def llama80(stream, steps=10, warm_seconds=2.0):
     log("[bench] llama70b 80 layers: drawing weights and cache on the device")
     t0 = time.time()
     dw = DeviceWeights.random_on_device(s, seed=w.seeds["weights"])
-    h = create_engine(s, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, None, nan_poison=False)
+    h = create_engine(s, dw, b.num_blocks, b.n_seqs, maxb, b.n_rows, b.free_order, decode_sched(), nan_poison=False)
     res = {"weights_gb": dw.bytes() / 1e9, "kv_pool_gb": h.kv_mem.numel() / 1e9}
     try:
         alloc_sequences(h, b.seq_lens)
         fill_past_random_on_device(h, b.past_seq, b.past_pos, seed=w.seeds["kv"])
+        torch.cuda.synchronize()
         res["setup_s"] = time.time() - t0
         log("[bench] llama70b 80 layers: timing graph replays")
-        t_nano = _graph_rate(h, b, stream, steps, warm_seconds, decode_sched(nano_rows=w.nano_splits, overlap=True))
-        t_ser = _graph_rate(h, b, stream, steps, 0.5, decode_sched())
-        row = _step_row(h, b, t_nano, stream)
-        row["ms_per_step_unsplit"] = t_ser * 1e3
-        row["tokens_per_s_unsplit"] = b.n_rows / t_ser
-        row["nano_split"] = list(w.nano_splits)
-        res.update(row)
+        res["runs"], res["eager"], res["launches"] = run_step_bench(h, b, args.steps, args.warmup, args.warm_seconds,
+                                                                    stream)
+        out = torch.empty((b.n_rows, s.vocab), device="cuda")
+        nb = ns.Batch(b.row_seq, b.row_pos, b.tokens)
+        g = ns.ns_graph_capture(h.eng, b.n_rows, out.data_ptr(), stream)
+        try:
+            res["clock"] = sample_clock(lambda: [ns.ns_graph_replay(g, nb, stream) for _ in range(25)], stream)
+        finally:
+            ns.ns_graph_destroy(g)
+        res["kernels"] = step_kernels(h, b, stream, reps=2)
+        res["nano_ms"] = _graph_rate(h, b, stream, max(5, args.steps // 2), 1.0,
+                                     decode_sched(nano_rows=w.nano_splits, overlap=True)) * 1e3
+        ns.ns_engine_set_sched(h.eng, decode_sched())
+        # last, so that a kernel trace of this run ends with these launches
+        res["att"] = attention_isolated(h, b, maxb, stream, n=100)
+        res["gu"] = gate_up_isolated(h, b, stream, n=100)
     finally:
         h.destroy()
         del dw
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-    return res
+    return w, b, res
+
+
+# ---------------------------------------------------------------- the small model's decode steps
+def small_step(stream, wname, steps, warm_seconds, detail):
+    """The Qwen2.5-0.5B-shaped 24-layer step at one batch (graph replay);
+    with `detail`, also per-kernel times, the two-way nano split, the
+    separate RoPE kernel, greedy decoding and the rooflines of the gate-up
+    GEMV and the attention (isolated launches)."""
+    w, weights, b, h, maxb = setup_step(wname)
+    res = {}
+    try:
+        runs, eager, launches = run_step_bench(h, b, steps, 5, warm_seconds, stream)
+        step_s = runs[-1]
+        sb = rf.step_bytes(w.model, (b.row_pos + 1).tolist())
+        res = {"tokens_per_s": b.n_rows / step_s, "ms_per_step": step_s * 1e3,
+               "runs_ms": [r * 1e3 for r in runs], "runs_disagree_over_15pct": bool(max(runs) > 1.15 * min(runs)),
+               "eager_ms": eager * 1e3, "fixed_cost_ms": (eager - step_s) * 1e3, "kernels_per_step": launches,
+               "algorithmic_bytes": sb, "hbm_floor_ms": rf.floor_seconds(sb) * 1e3,
+               "step_hbm_frac": sb / step_s / 1e9 / rf.HBM_PEAK_GBS}
+        if detail:
+            kern = step_kernels(h, b, stream)
+            res["kernels"] = kern
+            if w.nano_splits:
+                res["nano_overlap_ms"] = _graph_rate(h, b, stream, steps, 1.0,
+                                                     decode_sched(nano_rows=w.nano_splits, overlap=True)) * 1e3
+                res["nano_split"] = list(w.nano_splits)
+            res["separate_rope_kernel_ms"] = _graph_rate(h, b, stream, steps, 1.0, ns.make_sched()) * 1e3
+            ns.ns_engine_set_sched(h.eng, decode_sched())
+            res["greedy_decoding"] = greedy_loop(h, b, stream)
+            att = attention_isolated(h, b, maxb, stream)
+            gu = gate_up_isolated(h, b, stream)
+            tot = sum(v["us_per_step"] for v in kern.values())
+            res["gate_up_roofline"] = {
+                "kernel": "gate-up projection + SwiGLU (gemv_bf16_kernel)", "bound": "hbm",
+                "achieved": gu["gbs"], "peak": rf.HBM_PEAK_GBS, "unit": "GB/s", "frac": gu["gbs"] / rf.HBM_PEAK_GBS,
+                "traffic": recorded_traffic("gemm_gate_up_qwen05b_b32"), "bytes_per_launch": gu["bytes"],
+                "avg_launch_us": gu["us"], "isolated_launches": gu["launches"],
+                "share_of_step": kern["gate_up_proj"]["us_per_step"] / tot}
+            res["attention_roofline"] = {
+                "kernel": "paged decode attention (attn_mfma_kernel)", "bound": "hbm", "achieved": att["gbs"],
+                "peak": rf.HBM_PEAK_GBS, "unit": "GB/s", "frac": att["gbs"] / rf.HBM_PEAK_GBS,
+                "traffic": recorded_traffic("attention_qwen05b_b32_ctx512"), "bytes_per_launch": att["bytes"],
+                "avg_launch_us": att["us"], "isolated_launches": att["launches"],
+                "share_of_step": kern["attention"]["us_per_step"] / tot}
+    finally:
+        h.destroy()
+        torch.cuda.synchronize()
+    return res, h.weights
 
 
 # ---------------------------------------------------------------- CPU oracle
-def cpu_baseline(w, weights, b, maxb, n_steps=3):
+def oracle_step_seconds(shape, b, maxb, gen):
+    """Wall time of the oracle in its float32 mode for one decode step of a
+    workload: one layer over all of the batch's rows (its attention over each
+    row's cached context through the block tables), times the layer count,
+    plus the final norm and LM head.  The oracle gets inputs of its own, of
+    the workload's shapes and distributions, drawn with torch's generator
+    `gen` on the device and copied to the host (nothing read back from the
+    library).  Returns (seconds, seconds of the one layer, seconds of the
+    head)."""
+    from dataclasses import replace
+
+    from decode_step_06_amd.inputs import GAIN_STD, WEIGHT_STD, weight_names
     from oracle import decoder as od
     from oracle import kvcache as okv
-    log("[bench] cpu_baseline: timing the oracle")
+
+    def draw(shp, std=1.0, mean=0.0):
+        t = torch.randn(shp, generator=gen, device="cuda") * std + mean
+        return t.to(torch.bfloat16).float().cpu().numpy()
+
+    lw = {n: draw(sh, GAIN_STD, 1.0) if n.endswith("norm") else draw(sh, WEIGHT_STD) for n, sh in weight_names(shape)}
     alloc = okv.BlockAllocator(b.num_blocks, b.free_order, b.n_seqs, maxb)
-    for s, n in enumerate(b.seq_lens):
-        alloc.alloc(s, int(n))
+    for q, n in enumerate(b.seq_lens):
+        alloc.alloc(q, int(n))
     tables = alloc.table_rows()
-    cache = od.OracleKV(w.model.n_layers, b.num_blocks, w.model.n_kv_heads, w.model.head_dim)
-    od.fill_past(cache, tables, b.past_seq, b.past_pos, b.past_k, b.past_v)
-    orc = od.Oracle(w.model, weights)
+    cache = od.OracleKV(1, b.num_blocks, shape.n_kv_heads, shape.head_dim, dtype=np.float32)
+    P = len(b.past_seq)
+    od.fill_past(cache, tables, b.past_seq, b.past_pos, [draw((P, shape.n_kv_heads, shape.head_dim))],
+                 [draw((P, shape.n_kv_heads, shape.head_dim))])
+    x = draw((b.n_rows, shape.hidden))
+    one = od.Oracle(replace(shape, n_layers=1, vocab=0, tied=False), {"layers": [lw]}, precision="f32")
     t0 = time.perf_counter()
-    for _ in range(n_steps):
-        orc.step(cache, tables, b.row_seq, b.row_pos, tokens=b.tokens)
-    dt = time.perf_counter() - t0
+    y = one.step(cache, tables, b.row_seq, b.row_pos, x=x)
+    t_layer = time.perf_counter() - t0
+    t_head = 0.0
+    if shape.vocab:
+        head = od.Oracle(shape, {"final_norm": draw((shape.hidden,), GAIN_STD, 1.0),
+                                 "lm_head": draw((shape.vocab, shape.hidden), WEIGHT_STD)}, precision="f32")
+        t0 = time.perf_counter()
+        head.head(y)
+        t_head = time.perf_counter() - t0
+    return t_layer * shape.n_layers + t_head, t_layer, t_head
+
+
+def cpu_baseline(full=False):
+    """The oracle (float32 mode) timed on this host's cores: the headline's
+    80-layer step from one of its layers (256 rows) and its LM head, and the
+    0.5B-shaped step at batch 32; with `full`, also the continuous-batching
+    mix at each batch size and the 2048-row 70B-shaped layer."""
+    log("[bench] cpu_baseline: timing the oracle (float32)")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
     cores = len(os.sched_getaffinity(0))
-    return {"value": b.n_rows * n_steps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_steps} full steps of {w.name} (24 layers, batch {b.n_rows}, float64 numpy), "
-                      f"{dt:.1f} s", "threads_env": os.environ.get("OMP_NUM_THREADS")}
+    w = WORKLOADS[HEADLINE]
+    b = gen_batch(w, with_past=False, pool_slack=1.02)
+    t, tl, th = oracle_step_seconds(w.model, b, blocks_for(b.seq_lens), gen)
+    out = {"value": b.n_rows / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"one of the 80 layers of {HEADLINE} over all {b.n_rows} rows ({tl:.1f} s) plus the final norm "
+                     f"and LM head ({th:.1f} s), float32 numpy; the step time is 80 x the layer + the head",
+           "threads_env": os.environ.get("OMP_NUM_THREADS")}
+    other = [SMALL] + ([f"qwen05b_mix_b{B}" for B in SWEEP] + ["llama70b_layer_t2048"] if full else [])
+    extra = {}
+    for name in other:
+        wo = WORKLOADS[name]
+        bo = gen_batch(wo, with_past=False)
+        t, tl, th = oracle_step_seconds(wo.model, bo, blocks_for(bo.seq_lens), gen)
+        extra[name] = {"tokens_per_s": bo.n_rows / t, "step_s": t, "layer_s": tl, "head_s": th}
+    out["other_workloads"] = extra
+    return out
 
 
 def _jsonable(o):
@@ -608,19 +777,42 @@ def _jsonable(o):
         return int(o)
     if isinstance(o, (np.floating,)):
         return float(o)
+    if isinstance(o, float):
+        return o
     raise TypeError(type(o))
+
+
+def _rounded(o, nd=4):
+    if isinstance(o, dict):
+        return {k: _rounded(v, nd) for k, v in o.items()}
+    if isinstance(o, (list, tuple)):
+        return [_rounded(v, nd) for v in o]
+    if isinstance(o, (float, np.floating)):
+        return float(f"{float(o):.{nd + 2}g}")
+    if isinstance(o, np.integer):
+        return int(o)
+    return o
+
+
+def _leg(fn, *a, **kw):
+    try:
+        return json.loads(json.dumps(fn(*a, **kw), default=_jsonable))
+    except Exception as e:  # report, do not hide
+        log(f"[bench] {fn.__name__} failed: {e!r}")
+        return {"error": repr(e)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--warm-seconds", type=float, default=3.0)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-full", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--no-llama80", action="store_true")
+    ap.add_argument("--no-small", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step is built and measured on a single MI355X "
@@ -637,71 +829,41 @@ def main():
     calib_dst.copy_(calib_src)
     torch.cuda.synchronize()
     del calib_src, calib_dst
-    w, weights, b, h, maxb = setup_step(WORKLOAD)
-    sweep = buckets = None
-    try:
-        runs, eager, launches = run_step_bench(h, b, args.steps, args.warmup, args.warm_seconds, stream)
-        kern = step_kernels(h, b, stream)
-        # the same step as two nano-batches on two streams (the workload's
-        # split), graph-replayed: both chains of latency-bound kernels overlap
-        nano_ms = None
-        if w.nano_splits:
-            nano_ms = _graph_rate(h, b, stream, args.steps, 1.0,
-                                  decode_sched(nano_rows=w.nano_splits, overlap=True)) * 1e3
-        # the same step with RoPE and the cache write as their own kernel
-        separate_ms = _graph_rate(h, b, stream, args.steps, 1.0, ns.make_sched()) * 1e3
-        ns.ns_engine_set_sched(h.eng, decode_sched())
-        greedy = greedy_loop(h, b, stream)
-        # last, so that a kernel trace of this run ends with these launches
-        att = attention_isolated(h, b, maxb, stream)
-        gu = gate_up_isolated(h, b, stream)
-        if not args.no_sweep:
-            try:
-                sweep = json.loads(json.dumps(batch_sweep(stream, h.weights), default=_jsonable))
-            except Exception as e:  # report, do not hide
-                sweep = {"error": repr(e)}
-            try:
-                buckets = json.loads(json.dumps(bucket_capture(stream, h.weights), default=_jsonable))
-            except Exception as e:  # report, do not hide
-                buckets = {"error": repr(e)}
-    finally:
-        h.destroy()
+
+    w, b, r = llama80(args, stream)
+    s = w.model
+    runs = r["runs"]
     step_s = runs[-1]
-    value = b.n_rows / step_s
     ctx = (b.row_pos + 1).tolist()
-    sb = rf.step_bytes(w.model, ctx)
-    # dominant kernel: decode attention, the class with the largest share of
-    # the step's device time; its average launch duration from the isolated
-    # back-to-back launches (in-step event intervals also count dispatch gaps)
-    # dominant kernel: the gate-up projection, the single kernel with the
-    # largest share of the step's device time in the kernel trace of this
-    # command (per step: gate-up 24 x 9.8 us, attention 24 x 8.8 us,
-    # RMSNorm 48 x 3.8 us); HBM-bound at 32 rows (17.4 MB of weights per
-    # launch).  Its average launch duration from the isolated back-to-back
-    # launches (in-step event intervals also count dispatch gaps).
+    sb = rf.step_bytes(s, ctx)
+    kern = r["kernels"]
     tot = sum(v["us_per_step"] for v in kern.values())
-    roof = {"kernel": "gate-up projection + SwiGLU (gemv_bf16_kernel)", "bound": "hbm",
-            "achieved": round(gu["gbs"], 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gu["gbs"] / rf.HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("gemm_gate_up_qwen05b_b32"),
-            "bytes_per_launch": gu["bytes"], "avg_launch_us": round(gu["us"], 3),
-            "isolated_launches": gu["launches"],
-            "in_step_event_interval_us": round(kern["gate_up_proj"]["us_per_launch"], 3),
-            "share_of_step": round(kern["gate_up_proj"]["us_per_step"] / tot, 3)}
-    # the paged decode attention the metric names, isolated launches of the
-    # op (inside the step the same kernel runs with RoPE and the cache write
-    # fused in)
-    attn_roof = {"kernel": "paged decode attention (attn_mfma_kernel)", "bound": "hbm",
-                 "achieved": round(att["gbs"], 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
-                 "frac": round(att["gbs"] / rf.HBM_PEAK_GBS, 4),
-                 "traffic": recorded_traffic("attention_qwen05b_b32_ctx512"),
-                 "bytes_per_launch": att["bytes"], "avg_launch_us": round(att["us"], 3),
-                 "isolated_launches": att["launches"],
-                 "in_step_event_interval_us": round(kern["attention"]["us_per_launch"], 3),
-                 "share_of_step": round(kern["attention"]["us_per_step"] / tot, 3)}
+    att, gu = r["att"], r["gu"]
+    # dominant kernel: the paged decode attention (the split kernel and its
+    # combine: each row's context in two parts), the class with the largest
+    # share of the step's device time in the kernel trace of this command;
+    # HBM-bound.  Its average launch duration from back-to-back launches over
+    # the layers' caches (events on the launching stream).
+    roof = {"kernel": "paged decode attention (attn_mfma_kernel + attn_combine_kernel)", "bound": "hbm",
+            "achieved": round(att["gbs"], 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(att["gbs"] / rf.HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("attention_llama70b_80l_b256"),
+            "bytes_per_launch": att["bytes"], "avg_launch_us": round(att["us"], 3),
+            "isolated_launches": att["launches"],
+            "in_step_event_interval_us": round(kern["attention"]["us_per_launch"], 3),
+            "share_of_step": round(kern["attention"]["us_per_step"] / tot, 3)}
+    T, H, F = b.n_rows, s.hidden, s.ffn
+    gfl = rf.gemm_flops(T, F, H, True)
+    gemm_roof = {"kernel": "gate-up projection + SwiGLU at 256 rows (gemm_big_kernel)", "bound": "mfma",
+                 "achieved": round(gfl / (gu["us"] * 1e-6) / 1e12, 1), "peak": rf.BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(gfl / (gu["us"] * 1e-6) / 1e12 / rf.BF16_PEAK_TFLOPS, 4),
+                 "hbm_gbs": round(gu["gbs"], 1), "hbm_frac": round(gu["gbs"] / rf.HBM_PEAK_GBS, 4),
+                 "flops_per_launch": gfl, "bytes_per_launch": gu["bytes"], "avg_launch_us": round(gu["us"], 3),
+                 "isolated_launches": gu["launches"],
+                 "share_of_step": round(kern["gate_up_proj"]["us_per_step"] / tot, 3)}
     result = {
         "metric": "decode tokens/s @1 GPU; attn HBM GB/s and GEMM MFMA % of peak",
-        "value": round(value, 1),
+        "value": round(b.n_rows / step_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -711,42 +873,42 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded random-init weights and cached context)",
-        "config": {"workload": w.name, "batch": b.n_rows, "context": int(w.decode_ctx), "layers": w.model.n_layers,
-                   "kv_block": 16, "mode": "hipGraph replay", "rope_fused_into_attention": True,
-                   "parallelism": "single GPU"},
+        "data": "synthetic (seeded random-init weights and cached context, drawn on the device)",
+        "config": {"workload": w.name, "batch": b.n_rows, "context": "uniform 512..1536", "layers": s.n_layers,
+                   "hidden": s.hidden, "heads": f"{s.n_q_heads}q/{s.n_kv_heads}kv", "vocab": s.vocab,
+                   "kv_block": 16, "mode": "hipGraph replay of the whole step", "parallelism": "single GPU"},
         "roofline": roof,
-        "attention_roofline": attn_roof,
+        "gemm_roofline": gemm_roof,
         "calibration_copy_bytes": calib_bytes,
-        "step": {"runs_ms": [round(r * 1e3, 4) for r in runs],
-                 "runs_disagree_over_15pct": bool(max(runs) > 1.15 * min(runs)),
-                 "eager_ms": round(eager * 1e3, 4), "fixed_cost_ms": round((eager - step_s) * 1e3, 4),
-                 "kernels_per_step": launches, "algorithmic_bytes": sb,
-                 "nano_overlap_ms": nano_ms, "nano_split": list(w.nano_splits),
-                 "separate_rope_kernel_ms": round(separate_ms, 4),
-                 "hbm_floor_ms": round(rf.floor_seconds(sb) * 1e3, 4),
-                 "step_hbm_frac": round(sb / step_s / 1e9 / rf.HBM_PEAK_GBS, 4)},
-        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for k, v in kern.items()},
-        "greedy_decoding": {k: round(v, 4) for k, v in greedy.items()},
+        "step": _rounded({"runs_ms": [x * 1e3 for x in runs], "runs_disagree_over_15pct": max(runs) > 1.15 * min(runs),
+                          "eager_ms": r["eager"] * 1e3, "fixed_cost_ms": (r["eager"] - step_s) * 1e3,
+                          "kernels_per_step": r["launches"], "algorithmic_bytes": sb,
+                          "hbm_floor_ms": rf.floor_seconds(sb) * 1e3,
+                          "step_hbm_frac": sb / step_s / 1e9 / rf.HBM_PEAK_GBS,
+                          "nano_overlap_ms": r["nano_ms"], "nano_split": list(w.nano_splits),
+                          "warm_seconds": args.warm_seconds, "weights_gb": r["weights_gb"],
+                          "kv_pool_gb": r["kv_pool_gb"], "setup_s": r["setup_s"]}),
+        "clock": _rounded(r["clock"]),
+        "kernels": _rounded(kern),
     }
+    del r
+    if not args.no_small:
+        def small(detail, wname):
+            res, dw = small_step(stream, wname, 200, 8.0 if detail else 3.0, detail)
+            return res, dw
+        sm, dw = small(True, SMALL)
+        result[SMALL] = _rounded(json.loads(json.dumps(sm, default=_jsonable)))
+        result["qwen05b_b1_ctx512"] = _rounded(_leg(lambda: small(False, "qwen05b_b1_ctx512")[0]))
+        if not args.no_sweep:
+            result["batch_sweep"] = _rounded(_leg(batch_sweep, stream, dw))
+            result["bucketed_capture"] = _rounded(_leg(bucket_capture, stream, dw))
+        del dw
+        torch.cuda.empty_cache()
     if not args.no_dense:
-        try:
-            result["dense_batch"] = json.loads(json.dumps(dense_batch(stream), default=_jsonable))
-        except Exception as e:  # report, do not hide
-            result["dense_batch"] = {"error": repr(e)}
-    if sweep is not None:
-        result["batch_sweep"] = sweep
-    if buckets is not None:
-        result["bucketed_capture"] = buckets
-    if not args.no_llama80:
-        try:
-            result["llama70b_80l_b256"] = json.loads(json.dumps(llama80(stream), default=_jsonable))
-        except Exception as e:  # report, do not hide
-            result["llama70b_80l_b256"] = {"error": repr(e)}
-    result["hbm_copy_ceiling"] = {k: round(v, 4) for k, v in copy_ceiling(stream).items()}
+        result["dense_batch"] = _rounded(_leg(dense_batch, stream))
+    result["torch_copy_rate"] = _rounded(copy_ceiling(stream))
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, weights, b, maxb)
+        result["cpu_baseline"] = _rounded(cpu_baseline(args.cpu_baseline_full))
     print(json.dumps(result, default=_jsonable), flush=True)
 
 
