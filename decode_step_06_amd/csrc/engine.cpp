@@ -17,6 +17,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -953,6 +954,53 @@ int ns_op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att
                     void* stream) {
   return op_attention(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab, max_blocks_per_seq, out, ws,
                       ws_bytes, wg_cap, stream, false);
+}
+
+// ---------------------------------------------------------------- attention without allocation
+// ns_op_attention_static keeps its split-context partials in `scratch`, a
+// file-scope device array: every GPU the library runs on holds its own copy
+// from module load until the process ends.  In host code the array's name
+// is only a stand-in, so the device address of the current GPU's copy is
+// looked up once per device (hipGetSymbolAddress, with that device
+// current) and that address is what the kernels receive.
+namespace {
+constexpr size_t kStaticScratchBytes = NS_ATTENTION_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) NS_FAIL(NS_EINVAL, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) NS_FAIL(NS_EHIP, "hipGetSymbolAddress gave a null address for the static scratch");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return NS_OK;
+}
+}  // namespace
+
+int ns_op_attention_static(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                           int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos, const int32_t* btab,
+                           int32_t max_blocks_per_seq, void* out, int32_t wg_cap, void* stream) {
+  int rc = check_attention_args(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab,
+                                max_blocks_per_seq, out, wg_cap);
+  if (rc) return rc;
+  const size_t need = ns_op_attention_ws_bytes(desc, n_rows, max_blocks_per_seq);
+  if (need > kStaticScratchBytes)
+    NS_FAIL(NS_ESHAPE, "split-context partials of %zu bytes exceed the static scratch of %zu bytes (%d rows, %d blocks "
+                       "per sequence); use ns_op_attention with a workspace",
+            need, kStaticScratchBytes, n_rows, max_blocks_per_seq);
+  void* ws = nullptr;
+  if (need > 0 && (rc = static_scratch(&ws))) return rc;
+  return op_attention(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab, max_blocks_per_seq, out, ws,
+                      need, wg_cap, stream, false);
 }
 
 int ns_op_attention_prefill(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,

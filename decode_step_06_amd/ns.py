@@ -98,6 +98,7 @@ SIGNATURES = {
                                   _I, _P]),
     "ns_op_attention_prefill": (C.c_int, [C.POINTER(ns_model_desc), _I, _P, _P, _I, _P, _P, _P, _I, _P, _P,
                                           C.c_size_t, _I, _P]),
+    "ns_op_attention_static": (C.c_int, [C.POINTER(ns_model_desc), _I, _P, _P, _I, _P, _P, _P, _I, _P, _I, _P]),
 }
 
 _LIB: Optional[C.CDLL] = None
@@ -354,3 +355,11 @@ def ns_op_attention_prefill(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq,
     _check(lib().ns_op_attention_prefill(C.byref(desc), n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab,
                                          max_blocks_per_seq, out, ws, ws_bytes, wg_cap, _stream_ptr(stream)))
 
+
+NS_ATTENTION_STATIC_SCRATCH_BYTES = 17 << 20  # include/ns.h
+
+
+def ns_op_attention_static(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab, max_blocks_per_seq,
+                           out, wg_cap=0, stream=None) -> None:
+    _check(lib().ns_op_attention_static(C.byref(desc), n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab,
+                                        max_blocks_per_seq, out, wg_cap, _stream_ptr(stream)))

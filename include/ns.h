@@ -411,6 +411,25 @@ int ns_op_attention_prefill(const ns_model_desc* desc, int32_t n_rows, const voi
                     int32_t max_blocks_per_seq, void* out, void* ws, size_t ws_bytes, int32_t wg_cap,
                     void* stream);
 
+/* Paged GQA decode attention that allocates nothing, for callers that
+ * cannot call hipMalloc or take a workspace: code under graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Arguments, layout and
+ * results as ns_op_attention, without ws / ws_bytes: the split-context
+ * partials live in a static device array of NS_ATTENTION_STATIC_SCRATCH_BYTES
+ * (17 MiB) that the library holds on every GPU it runs on until the process
+ * ends (looked up once per device on the first call there).  Contexts are
+ * split only while the split work items stay within 4096, so the partials
+ * of any supported shape (G * d <= 1024) take at most 16.25 MiB.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap on one GPU (two
+ * streams, or two host threads) race and give wrong results; the partials
+ * are written before they are read within each call, so nothing needs
+ * clearing.  Errors: those of ns_op_attention, and NS_ESHAPE when the
+ * partials (ns_op_attention_ws_bytes) exceed the static array. */
+#define NS_ATTENTION_STATIC_SCRATCH_BYTES ((size_t)17 << 20)
+int ns_op_attention_static(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
+                           int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos,
+                           const int32_t* btab, int32_t max_blocks_per_seq, void* out, int32_t wg_cap,
+                           void* stream);
 #ifdef __cplusplus
 }
 #endif
