@@ -159,6 +159,7 @@ struct ns_engine {
   hipStream_t s2 = nullptr;
   hipEvent_t ev_qkv[kMaxParts] = {};
   hipEvent_t ev_att[kMaxParts] = {};
+  hipEvent_t ev_join = nullptr;  // joins the second stream back into a capture that failed half-way
   int32_t* staging[2] = {nullptr, nullptr};
   hipEvent_t staging_ev[2] = {};
   bool staging_used[2] = {false, false};
@@ -629,6 +630,10 @@ int ns_engine_create(const ns_model_desc* desc, const ns_weights* w, ns_kv* kv, 
       return fail(NS_EHIP);
     }
   }
+  if (hipEventCreateWithFlags(&e->ev_join, hipEventDisableTiming) != hipSuccess) {
+    ns::set_error("hipEventCreate failed");
+    return fail(NS_EHIP);
+  }
   for (int k = 0; k < 2; ++k) {
     if (hipHostMalloc((void**)&e->staging[k], plan.meta_ints * sizeof(int32_t), hipHostMallocDefault) !=
             hipSuccess ||
@@ -652,6 +657,7 @@ void ns_engine_destroy(ns_engine* e) {
     if (e->ev_qkv[i]) hipEventDestroy(e->ev_qkv[i]);
     if (e->ev_att[i]) hipEventDestroy(e->ev_att[i]);
   }
+  if (e->ev_join) hipEventDestroy(e->ev_join);
   for (hipEvent_t ev : e->prof_ev) hipEventDestroy(ev);
   if (e->prof_start) hipEventDestroy(e->prof_start);
   for (int k = 0; k < 2; ++k) {
@@ -702,6 +708,12 @@ int ns_graph_capture(ns_engine* e, int32_t bucket, void* out, void* stream, ns_g
     NS_FAIL(NS_EHIP, "hipStreamBeginCapture: %s", hipGetErrorString(he));
   }
   int rc = enqueue_step(e, e->sched, bucket, out, st, true);
+  if (rc != NS_OK && e->sched.overlap) {
+    // a step that failed after forking to the second stream: join that
+    // stream back into the capture so that the capture can end
+    hipEventRecord(e->ev_join, e->s2);
+    hipStreamWaitEvent(st, e->ev_join, 0);
+  }
   he = hipStreamEndCapture(st, &g->graph);
   if (rc != NS_OK || he != hipSuccess) {
     if (g->graph) hipGraphDestroy(g->graph);
