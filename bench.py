@@ -396,6 +396,11 @@ def dense_batch(stream, steps=10):
             ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), lw["wgu"].data_ptr(),
                                  Cb.data_ptr(), stream=stream)
             stream.synchronize()
+        # the shader clock under this GEMM's sustained load (the MFMA peak
+        # scales with it)
+        res["clock_during_gate_up_gemm"] = sample_clock(
+            lambda: [ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), lw["wgu"].data_ptr(),
+                                          Cb.data_ptr(), stream=stream) for _ in range(800)], stream)
         gem = {}
         for name, epi, N, K, Bw, C in (("qkv_proj", ns.NS_EPI_STORE, s.qkv_dim, H, lw["wqkv"], C32),
                                        ("o_proj", ns.NS_EPI_RESID, H, DQ, lw["wo"], C32),
@@ -813,7 +818,15 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-small", action="store_true")
+    ap.add_argument("--legs", default="headline,small,sweep,dense,cpu",
+                    help="comma list of legs to run (profiling runs take one); without 'headline' the line "
+                         "carries only the legs run and no value")
     args = ap.parse_args()
+    legs = set(args.legs.split(","))
+    args.no_small = args.no_small or "small" not in legs
+    args.no_sweep = args.no_sweep or "sweep" not in legs
+    args.no_dense = args.no_dense or "dense" not in legs
+    args.no_cpu_baseline = args.no_cpu_baseline or "cpu" not in legs
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step is built and measured on a single MI355X "
               "(no sharding, no collectives); --gpus must be 1.", file=sys.stderr)
@@ -830,6 +843,13 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    if "headline" not in legs:
+        result = {"metric": "decode tokens/s @1 GPU; attn HBM GB/s and GEMM MFMA % of peak", "value": None,
+                  "legs": sorted(legs)}
+        if not args.no_dense:
+            result["dense_batch"] = _rounded(_leg(dense_batch, stream))
+        print(json.dumps(result, default=_jsonable), flush=True)
+        return
     w, b, r = llama80(args, stream)
     s = w.model
     runs = r["runs"]

@@ -50,18 +50,21 @@ int elem_size(int32_t dtype) { return dtype == NS_BF16 ? 2 : 4; }
 // partition).  A wavefront's 64-token pass costs about 1 us of memory
 // latency and the combine launch of a split context about 6 us, so:
 // 8 wavefronts per item while items are few (<= 256, at most 2048
-// wavefronts: more passes in flight per row), 4 up to 2047 items, 1 once
-// the items alone fill the chip; the context is split (in halves, repeatedly) only while a wavefront would take
-// more than 8 passes and the split items stay within 4096 wavefronts.  The
-// shape depends only on the whole batch's row count and the capacity, so
-// nano-batched and unsplit steps, eager and captured, compute identically.
-// (Fitted to timings of the matrix-core kernel on MI355X: batch 1..512,
-// contexts 128..2048, head_dim 64 with 7 query heads per KV head and 128
-// with 8.)
+// wavefronts: more passes in flight per row), 4 up to 4095 items, 1 once
+// the items alone fill the chip twice over; the context is split (in
+// halves, repeatedly) only while a wavefront would take more than 8 passes
+// and the split items stay within 4096 wavefronts.  The shape depends only
+// on the whole batch's row count and the capacity, so nano-batched and
+// unsplit steps, eager and captured, compute identically.  (Fitted to
+// timings of the matrix-core kernel on MI355X: batch 1..512, contexts
+// 128..2048, head_dim 64 with 7 query heads per KV head and 128 with 8; at
+// 256 rows of 8 KV heads with contexts 512..1536, 4 wavefronts on whole
+// contexts took 200 us against 226 us for 1 wavefront on contexts split in
+// two, whose short rows leave their second part empty.)
 void attn_partition(int n_rows, int nkv, int cap_tokens, int* part_tokens, int* n_parts, int* waves) {
   const int chunks = std::max(1, (cap_tokens + 63) / 64);
   const long items = std::max(1L, (long)n_rows * nkv);
-  const int w = items >= 2048 ? 1 : (items <= 256 ? 8 : 4);
+  const int w = items >= 4096 ? 1 : (items <= 256 ? 8 : 4);
   int parts = 1;
   auto passes = [&](int p) { return ((chunks + p - 1) / p + w - 1) / w; };
   while (parts < chunks && passes(parts) > 8 && items * parts * 2 * w <= 4096) parts *= 2;
@@ -403,13 +406,15 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   // run last-first, so the later rows' projections run beside it.  Attention
   // part j reads only K/V written by parts <= j, all finished before QKV part
   // j's event, so any launch order of the attention parts is valid.
-  // fused only where a work item has several wavefronts to share the RoPE
-  // prologue: with one wavefront per item (>= 2048 items) the prologue
-  // serialises in front of every item's K/V stream (80-layer 70B-shaped step
-  // at 256 rows: 61.6 -> 64.1 ms), so the separate kernel runs there
+  // fused only below 2048 work items (rows x KV heads), where the launches
+  // are latency-bound and a work item's wavefronts share the RoPE prologue;
+  // at 2048 items and more the prologue serialises in front of every item's
+  // K/V stream while the separate kernel runs wide (80-layer 70B-shaped step
+  // at 256 rows: 55.8 ms separate, 58.7 ms fused), so the separate kernel
+  // runs there
   int a_pt = 0, a_np = 0, a_waves = 1;
   attn_partition(n_tok, nkv, e->maxb * NS_BLOCK_SIZE, &a_pt, &a_np, &a_waves);
-  const bool fuse = fused_rope(e, sc) && a_waves > 1;
+  const bool fuse = fused_rope(e, sc) && a_waves > 1 && (long)n_tok * nkv < 2048;
   const bool late_first = sc.decode_rows_first != 0 && nano.size() > 1;
   const bool defer0 = sc.decode_rows_first != 0 && qparts.size() > 1;
   int layer = 0;

@@ -77,11 +77,13 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
 // of the previous projection (slice order), written back, then the norm.
 // 16-byte chunks, CH per thread held in registers between the two passes;
 // all of a chunk's slice loads are in flight together (a chain of
-// dependent loads would cost one memory latency per slice).
-template <typename T, int CH>
-__global__ void __launch_bounds__(256) rmsnorm_reduce_kernel(float* __restrict__ x, const float* __restrict__ P,
-                                                             long slice_stride, int splits, const T* __restrict__ g,
-                                                             T* __restrict__ h, int H, float eps) {
+// dependent loads would cost one memory latency per slice).  NT threads per
+// row: 256 up to 2048 elements, 1024 above (a thread's chunks are rounds of
+// dependent loads, so wide rows take more threads rather than more rounds).
+template <typename T, int CH, int NT>
+__global__ void __launch_bounds__(NT) rmsnorm_reduce_kernel(float* __restrict__ x, const float* __restrict__ P,
+                                                            long slice_stride, int splits, const T* __restrict__ g,
+                                                            T* __restrict__ h, int H, float eps) {
   const int t = blockIdx.x, H4 = H >> 2;
   float* xr = x + (long)t * H;
   const float* pr = P + (long)t * H;
@@ -89,7 +91,7 @@ __global__ void __launch_bounds__(256) rmsnorm_reduce_kernel(float* __restrict__
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int i4 = threadIdx.x + c * 256;
+    const int i4 = threadIdx.x + c * NT;
     if (i4 < H4) {
       const f32x4_t add = slice_sum4(pr + 4 * i4, slice_stride, splits);
       f32x4_t xv = *(const f32x4_t*)(xr + 4 * i4);
@@ -99,15 +101,19 @@ __global__ void __launch_bounds__(256) rmsnorm_reduce_kernel(float* __restrict__
       ss += xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3];
     }
   }
-  __shared__ float red[4];
+  constexpr int NW = NT / 64;
+  __shared__ float red[NW];
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) tot += red[i];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
   T* hr = h + (long)t * H;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int i4 = threadIdx.x + c * 256;
+    const int i4 = threadIdx.x + c * NT;
     if (i4 < H4) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) Elem<T>::store(hr, 4 * i4 + e, v[c][e] * r * Elem<T>::load(g, 4 * i4 + e));
@@ -306,8 +312,8 @@ __device__ __forceinline__ long v_index(long blk, int g, int tok, int j, int nkv
 // arrives as split-K slices, every slice's load of a chunk in flight at once.
 // Then each thread produces whole 16-byte chunks: E consecutive elements j of
 // one head and, for q and k, their rotation partners j + d/2.
-template <typename T>
-__global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ qkv, long slice_stride, int splits,
+template <typename T, int NT>
+__global__ void __launch_bounds__(NT) rope_kv_kernel(const float* __restrict__ qkv, long slice_stride, int splits,
                                                       const float* __restrict__ cosb,
                                                       const float* __restrict__ sinb, const int32_t* __restrict__ slot,
                                                       T* __restrict__ q_att, T* __restrict__ kc, T* __restrict__ vc,
@@ -318,7 +324,7 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ 
   const int half = d >> 1, G = nq / nkv, nch = d / E, hch = half / E;
   const int width = (nq + 2 * nkv) * d;
   const float* row = qkv + (long)t * width;
-  for (int i4 = threadIdx.x; i4 < (width >> 2); i4 += 256)
+  for (int i4 = threadIdx.x; i4 < (width >> 2); i4 += NT)
     *(f32x4_t*)(rowbuf + 4 * i4) = slice_sum4(row + 4 * i4, slice_stride, splits);
   __syncthreads();
   const float* cr = cosb + (long)t * half;
@@ -327,7 +333,7 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(const float* __restrict__ 
   const long blk = s >= 0 ? (long)(s / NS_BLOCK) : 0;
   const int tok = s >= 0 ? s % NS_BLOCK : 0;
   const int n_q = nq * hch, n_k = s >= 0 ? nkv * hch : 0, n_v = s >= 0 ? nkv * nch : 0;
-  for (int it = threadIdx.x; it < n_q + n_k + n_v; it += 256) {
+  for (int it = threadIdx.x; it < n_q + n_k + n_v; it += NT) {
     if (it < n_q + n_k) {
       // rotate chunk c (elements j0..j0+E) of head hd with its partners
       const bool is_q = it < n_q;
@@ -456,34 +462,45 @@ void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, 
                     const float* sinb, const int32_t* slot, void* q_att, void* kc, void* vc, int T, int nq, int nkv,
                     int d, hipStream_t st) {
   if (T <= 0) return;
+  // rows wider than 2048 floats take 1024 threads: each thread's 16-byte
+  // chunks are rounds of dependent slice loads
   const size_t lds = (size_t)(nq + 2 * nkv) * d * sizeof(float);
-  if (dtype == NS_DT_BF16)
-    hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb, sinb,
-                       slot, (bf16_t*)q_att, (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
-  else
-    hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb, sinb,
-                       slot, (float*)q_att, (float*)kc, (float*)vc, nq, nkv, d);
+  const bool wide = (nq + 2 * nkv) * d > 2048;
+  if (dtype == NS_DT_BF16) {
+    if (wide)
+      hipLaunchKernelGGL((rope_kv_kernel<bf16_t, 1024>), dim3(T), dim3(1024), lds, st, qkv, slice_stride, splits, cosb,
+                         sinb, slot, (bf16_t*)q_att, (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
+    else
+      hipLaunchKernelGGL((rope_kv_kernel<bf16_t, 256>), dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb,
+                         sinb, slot, (bf16_t*)q_att, (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
+  } else {
+    hipLaunchKernelGGL((rope_kv_kernel<float, 256>), dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb,
+                       sinb, slot, (float*)q_att, (float*)kc, (float*)vc, nq, nkv, d);
+  }
 }
 
 template <typename T>
 static void run_rmsnorm_reduce(float* x, const float* P, long slice_stride, int splits, const T* g, T* h, int T_,
                                int H, float eps, hipStream_t st) {
   const int ch = (H / 4 + 255) / 256;
-  if (H % 4 != 0 || ch > 8)
+  if (H % 4 != 0 || ch > 32)
     hipLaunchKernelGGL(rmsnorm_reduce_any_kernel<T>, dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
                        H, eps);
   else if (ch == 1)
-    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 1>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
-                       H, eps);
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 1, 256>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g,
+                       h, H, eps);
   else if (ch == 2)
-    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 2>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
-                       H, eps);
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 2, 256>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g,
+                       h, H, eps);
   else if (ch <= 4)
-    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 4>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
-                       H, eps);
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 1, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
+                       g, h, H, eps);
+  else if (ch <= 8)
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 2, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
+                       g, h, H, eps);
   else
-    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 8>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
-                       H, eps);
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 8, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
+                       g, h, H, eps);
 }
 
 void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_stride, int splits, const void* g,

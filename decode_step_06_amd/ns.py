@@ -356,7 +356,7 @@ def ns_op_attention_prefill(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq,
                                          max_blocks_per_seq, out, ws, ws_bytes, wg_cap, _stream_ptr(stream)))
 
 
-NS_ATTENTION_STATIC_SCRATCH_BYTES = 17 << 20  # include/ns.h
+NS_ATTENTION_STATIC_SCRATCH_BYTES = 5 << 20  # include/ns.h
 
 
 def ns_op_attention_static(desc, n_rows, q_att, kv_layer, num_blocks, row_bseq, row_pos, btab, max_blocks_per_seq,

@@ -9,6 +9,17 @@ dispatches, mean and total duration), and for each kernel name K given the
 mean over its last N dispatches (the benchmark's isolated back-to-back
 launches).
 
+``trace`` also splits those last N dispatches by grid size (one line per
+grid), which separates launches of one kernel on different shapes.
+
+``counters`` prints, for the last N dispatches of kernel K in one or more
+``--pmc`` runs, the mean of every counter per dispatch, and what follows from
+them: with the kernel's mean duration (``--duration-us``, from the trace),
+GRBM_GUI_ACTIVE / duration is the clock the GPU ran at; with
+SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512 FLOPs), the FLOP rate the matrix
+cores issued; SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x compute units
+is the fraction of the time the matrix cores were busy.
+
 ``traffic`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the
 same command into HBM bytes per launch of kernel K (mean over its last N
 dispatches).  Each counter is scaled by what it reads for the command's
@@ -55,12 +66,50 @@ def trace(args):
         out.append(f"| `{k}` | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {sum(v) / 1e6:.3f} |")
     for i, kern in enumerate(args.kernel):
         last = args.last[i] if i < len(args.last) else 0
-        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows if kern in r["Kernel_Name"]]
-        tail = d[-last:] if last else d
-        if tail:
-            out += ["", f"Last {len(tail)} dispatches of `{kern}` (the isolated back-to-back launches): "
-                        f"mean {sum(tail) / len(tail) / 1e3:.3f} us."]
+        sel = [r for r in rows if kern in r["Kernel_Name"]]
+        sel = sel[-last:] if last else sel
+        if not sel:
+            continue
+        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel]
+        out += ["", f"Last {len(d)} dispatches of `{kern}` (the isolated back-to-back launches): "
+                    f"mean {sum(d) / len(d) / 1e3:.3f} us."]
+        grids = collections.OrderedDict()
+        for r, dd in zip(sel, d):
+            grids.setdefault(r.get("Grid_Size_X", "?"), []).append(dd)
+        if len(grids) > 1:
+            for g, v in grids.items():
+                out.append(f"- grid {g}: {len(v)} dispatches, mean {sum(v) / len(v) / 1e3:.3f} us")
     print("\n".join(out))
+
+
+def counters(args):
+    per = collections.OrderedDict()
+    for path in args.csv:
+        rows = _rows(path)
+        names = sorted({r["Counter_Name"] for r in rows})
+        for name in names:
+            vals = [v for d, (n, v) in sorted(_counter(rows, name).items()) if args.kernel in n][-args.last:]
+            if vals:
+                per[name] = sum(vals) / len(vals)
+    if not per:
+        sys.exit(f"no dispatches of {args.kernel}")
+    lines = [f"# Counters of {args.kernel}: mean per dispatch over its last {args.last} dispatches",
+             *[f"# command: {c}" for c in args.cmd]]
+    lines += [f"{k}: {v:.1f}" for k, v in per.items()]
+    if args.duration_us:
+        lines.append(f"duration_us (kernel trace): {args.duration_us:.3f}")
+        if "GRBM_GUI_ACTIVE" in per:
+            lines.append(f"clock_mhz (GRBM_GUI_ACTIVE / duration): {per['GRBM_GUI_ACTIVE'] / args.duration_us:.0f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in per:
+            tf = per["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (args.duration_us * 1e-6) / 1e12
+            lines.append(f"mfma_bf16_tflops_issued (MOPS x 512 / duration): {tf:.1f}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in per and "GRBM_GUI_ACTIVE" in per:
+        frac = per["SQ_VALU_MFMA_BUSY_CYCLES"] / (per["GRBM_GUI_ACTIVE"] * args.cus)
+        lines.append(f"mfma_busy_fraction (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {args.cus} CUs)): {frac:.3f}")
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _counter(rows, name):
@@ -128,6 +177,15 @@ def main(argv=None):
     t.add_argument("--kernel", action="append", default=[])
     t.add_argument("--last", type=int, action="append", default=[])
     t.set_defaults(fn=trace)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--last", type=int, required=True)
+    c.add_argument("--duration-us", type=float, default=0.0)
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--out", default="")
+    c.add_argument("--cmd", action="append", default=[])
+    c.set_defaults(fn=counters)
     r = sub.add_parser("traffic")
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)

@@ -416,16 +416,17 @@ int ns_op_attention_prefill(const ns_model_desc* desc, int32_t n_rows, const voi
  * serving loops, harnesses that forbid allocation.  Arguments, layout and
  * results as ns_op_attention, without ws / ws_bytes: the split-context
  * partials live in a static device array of NS_ATTENTION_STATIC_SCRATCH_BYTES
- * (17 MiB) that the library holds on every GPU it runs on until the process
+ * (5 MiB) that the library holds on every GPU it runs on until the process
  * ends (looked up once per device on the first call there).  Contexts are
- * split only while the split work items stay within 4096, so the partials
- * of any supported shape (G * d <= 1024) take at most 16.25 MiB.  Every call on
+ * split only while the split work items' wavefronts stay within 4096, at 4
+ * or 8 wavefronts per item, so at most 1024 split items and partials of at
+ * most 4 MiB + 64 KiB for any supported shape (G * d <= 1024).  Every call on
  * one GPU shares that GPU's array, so calls that overlap on one GPU (two
  * streams, or two host threads) race and give wrong results; the partials
  * are written before they are read within each call, so nothing needs
  * clearing.  Errors: those of ns_op_attention, and NS_ESHAPE when the
  * partials (ns_op_attention_ws_bytes) exceed the static array. */
-#define NS_ATTENTION_STATIC_SCRATCH_BYTES ((size_t)17 << 20)
+#define NS_ATTENTION_STATIC_SCRATCH_BYTES ((size_t)5 << 20)
 int ns_op_attention_static(const ns_model_desc* desc, int32_t n_rows, const void* q_att, const void* kv_layer,
                            int32_t num_blocks, const int32_t* row_bseq, const int32_t* row_pos,
                            const int32_t* btab, int32_t max_blocks_per_seq, void* out, int32_t wg_cap,

@@ -4,8 +4,8 @@ to distinct sequences.  It computes the same bits as the separate
 RoPE/cache-write kernel followed by attention: the outputs and the whole KV
 cache after the step are compared bit for bit, in every launch shape of the
 attention kernel that fuses it (8 and 4 wavefronts per work item, split
-contexts, head_dim 64 and 128; with one wavefront per item the engine keeps
-the separate kernel), eager and graph-replayed, nano-batched with overlap.
+contexts, head_dim 64 and 128; from 2048 work items on the engine keeps the
+separate kernel), eager and graph-replayed, nano-batched with overlap.
 The fused step also matches the oracle, and a batch that repeats a sequence
 is rejected with no side effects."""
 import numpy as np
@@ -33,10 +33,13 @@ CASES = {
     "small-4waves-300rows": Workload("f4b", SMALL_H, 300, ctx_range=(1, 40)),
     # 1024 items of 8 KV heads: 4 wavefronts
     "kv8-4waves": Workload("f1", KV8, 128, ctx_range=(1, 70)),
-    # >= 2048 items: one wavefront per item, where the engine keeps the
-    # separate kernel (with slices and with the unsplit projection)
-    "kv8-1wave": Workload("f1", KV8, 256, ctx_range=(1, 70)),
-    "small-1wave-1100rows": Workload("f1b", SMALL_H, 1100, ctx_range=(1, 24)),
+    # 2048..4095 items: 4 wavefronts, where the engine keeps the separate
+    # kernel (with slices)
+    "kv8-4waves-2048items": Workload("f1", KV8, 256, ctx_range=(1, 70)),
+    # >= 4096 items: one wavefront per item, separate kernel (with slices and
+    # with the unsplit projection)
+    "kv8-1wave": Workload("f1c", KV8, 512, ctx_range=(1, 40)),
+    "small-1wave-2100rows": Workload("f1b", SMALL_H, 2100, ctx_range=(1, 24)),
     # contexts past 8 passes of 8 wavefronts: split into partitions + combine
     "qwen-split": Workload("fs", QWEN1, 3, ctx_range=(4100, 5000)),
     "llama-d128": Workload("fl", LLAMA1, 5, ctx_range=(1, 300)),

@@ -231,11 +231,12 @@ def test_attention_workgroup_cap_is_bit_exact():
 
 
 # Launch shapes the engine picks from the batch: 8 wavefronts per work item
-# for few items, 4 for a few hundred, 1 once items fill the chip, and a split
-# context with the combine launch for a long context at a small batch.
-@pytest.mark.parametrize("shape_i,n_rows,ctx_hi", [(0, 300, 300), (0, 1100, 80), (0, 1, 9000), (1, 1, 4100)],
-                         ids=["qwen-300rows-4waves", "qwen-1100rows-1wave", "qwen-ctx9000-split",
-                              "llama-ctx4100-split"])
+# for few items, 4 up to 4095 items, 1 from 4096, and a split context with
+# the combine launch for a long context at a small batch.
+@pytest.mark.parametrize("shape_i,n_rows,ctx_hi", [(0, 300, 300), (0, 1100, 80), (0, 2100, 60), (0, 1, 9000),
+                                                   (1, 1, 4100)],
+                         ids=["qwen-300rows-4waves", "qwen-1100rows-4waves", "qwen-2100rows-1wave",
+                              "qwen-ctx9000-split", "llama-ctx4100-split"])
 def test_attention_launch_shapes_match_oracle(shape_i, n_rows, ctx_hi):
     shape = ATTN_SHAPES[shape_i]
     rng = np.random.default_rng(11 + n_rows)

@@ -55,3 +55,36 @@ def test_traffic_calibration(tmp_path):
     assert int(vals["traffic_bytes_per_launch"]) == 100 * 1024 * 2 + 8 * 1024
     assert vals["source_sha256"] == hashlib.sha256(b"kernel source\n").hexdigest()
     assert abs(float(vals["traffic_over_algorithmic"]) - (100 * 1024 * 2 + 8 * 1024) / 409600) < 1e-3
+
+
+def test_trace_splits_last_dispatches_by_grid(tmp_path, capsys):
+    p = tmp_path / "trace.csv"
+    rows = [["void ns::gemm_big_kernel<0>(int)", 0, 4000, 512],
+            ["void ns::gemm_big_kernel<0>(int)", 5000, 7000, 256],
+            ["void ns::gemm_big_kernel<0>(int)", 8000, 10000, 256],
+            ["void ns::gemm_big_kernel<0>(int)", 11000, 17000, 512]]
+    _write(p, ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"], rows)
+    ps.main(["trace", str(p), "--title", "T", "--cmd", "C", "--kernel", "gemm_big_kernel<0>", "--last", "3"])
+    out = capsys.readouterr().out
+    assert "- grid 256: 2 dispatches, mean 2.000 us" in out
+    assert "- grid 512: 1 dispatches, mean 6.000 us" in out
+
+
+def test_counters_clock_mfma_rate_and_busy(tmp_path):
+    p = tmp_path / "c.csv"
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = [[1, "ns::gemm_big_kernel<2>", "GRBM_GUI_ACTIVE", 1000.0],
+            [1, "ns::gemm_big_kernel<2>", "SQ_VALU_MFMA_BUSY_CYCLES", 128000.0],
+            [1, "ns::gemm_big_kernel<2>", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2000.0],
+            [2, "ns::gemm_big_kernel<2>", "GRBM_GUI_ACTIVE", 3000.0],
+            [2, "ns::gemm_big_kernel<2>", "SQ_VALU_MFMA_BUSY_CYCLES", 384000.0],
+            [2, "ns::gemm_big_kernel<2>", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 6000.0]]
+    _write(p, hdr, rows)
+    out = tmp_path / "o.txt"
+    ps.main(["counters", str(p), "--kernel", "gemm_big_kernel<2>", "--last", "2", "--duration-us", "2.0",
+             "--out", str(out)])
+    vals = dict(line.split(": ", 1) for line in out.read_text().splitlines() if ": " in line and not line.startswith("#"))
+    assert float(vals["GRBM_GUI_ACTIVE"]) == 2000.0
+    assert float(vals["clock_mhz (GRBM_GUI_ACTIVE / duration)"]) == 1000.0
+    assert abs(float(vals["mfma_bf16_tflops_issued (MOPS x 512 / duration)"]) - 4000 * 512 / 2e-6 / 1e12) < 0.05
+    assert float(vals["mfma_busy_fraction (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs))"]) == 0.5

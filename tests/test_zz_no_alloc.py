@@ -58,8 +58,8 @@ def _run(c, static):
 
 
 def test_static_scratch_attention_matches_workspace_attention_twice():
-    big = _case(256, 512, 1536, 1)     # 2048 work items, contexts in two parts
-    small = _case(4, 5000, 8192, 2)    # 32 work items, contexts in two parts
+    big = _case(64, 4000, 8192, 1)     # 512 work items of 4 wavefronts, contexts in two parts
+    small = _case(4, 5000, 8192, 2)    # 32 work items of 8 wavefronts, contexts in two parts
     for c in (big, small):
         need = ns.ns_op_attention_ws_bytes(c["desc"], c["n"], c["maxb"])
         assert 0 < need <= ns.NS_ATTENTION_STATIC_SCRATCH_BYTES
