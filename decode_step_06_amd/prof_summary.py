@@ -14,17 +14,21 @@ grid), which separates launches of one kernel on different shapes.
 
 ``counters`` prints, for the last N dispatches of kernel K in one or more
 ``--pmc`` runs, the mean of every counter per dispatch, and what follows from
-them: with the kernel's mean duration (``--duration-us``, from the trace),
-GRBM_GUI_ACTIVE / duration is the clock the GPU ran at; with
-SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512 FLOPs), the FLOP rate the matrix
-cores issued; SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x compute units
-is the fraction of the time the matrix cores were busy.
+them, with the dispatches' mean duration (from their timestamps in the same
+run, or ``--duration-us``): GRBM_GUI_ACTIVE is summed over the XCDs, so
+GRBM_GUI_ACTIVE / XCDs / duration is the clock the GPU ran at;
+SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 FLOPs, so MOPS x 512 /
+duration is the FLOP rate the matrix cores issued; SQ_VALU_MFMA_BUSY_CYCLES
+is summed over the SIMDs, so over (GRBM_GUI_ACTIVE / XCDs) x SIMDs it is the
+fraction of the time the matrix cores were busy.  The issued FLOP rate over
+the peak at the measured clock (1024 bf16 FLOP per cycle per SIMD for the
+32x32x16 form) checks the busy fraction.
 
 ``traffic`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the
 same command into HBM bytes per launch of kernel K (mean over its last N
 dispatches).  Each counter is scaled by what it reads for the command's
-plain 256 MiB device copy (the largest-fetch dispatch before the library's
-first kernel; B bytes read and B written): the counters' KiB are
+plain 256 MiB device copy (the first dispatch whose fetch is at least an
+eighth of B; B bytes read and B written): the counters' KiB are
 converted to bytes and calibrated so that the copy reads and writes exactly
 B.  The output file records the kernel's source file and its SHA-256, so a
 later change of the kernel invalidates the figure.
@@ -79,11 +83,14 @@ def trace(args):
         if len(grids) > 1:
             for g, v in grids.items():
                 out.append(f"- grid {g}: {len(v)} dispatches, mean {sum(v) / len(v) / 1e3:.3f} us")
+        if len(d) <= 32:
+            out.append("- in dispatch order (us): " + ", ".join(f"{x / 1e3:.1f}" for x in d))
     print("\n".join(out))
 
 
 def counters(args):
     per = collections.OrderedDict()
+    dur = {}
     for path in args.csv:
         rows = _rows(path)
         names = sorted({r["Counter_Name"] for r in rows})
@@ -91,21 +98,36 @@ def counters(args):
             vals = [v for d, (n, v) in sorted(_counter(rows, name).items()) if args.kernel in n][-args.last:]
             if vals:
                 per[name] = sum(vals) / len(vals)
+        for r in rows:  # each dispatch's own duration in the counter run, when recorded
+            if args.kernel in r["Kernel_Name"] and r.get("Start_Timestamp"):
+                dur[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     if not per:
         sys.exit(f"no dispatches of {args.kernel}")
     lines = [f"# Counters of {args.kernel}: mean per dispatch over its last {args.last} dispatches",
              *[f"# command: {c}" for c in args.cmd]]
     lines += [f"{k}: {v:.1f}" for k, v in per.items()]
-    if args.duration_us:
+    if not args.duration_us and dur:
+        tail = [v for _, v in sorted(dur.items())][-args.last:]
+        args.duration_us = sum(tail) / len(tail) / 1e3
+        lines.append(f"duration_us (the same dispatches in this counter run): {args.duration_us:.3f}")
+    elif args.duration_us:
         lines.append(f"duration_us (kernel trace): {args.duration_us:.3f}")
-        if "GRBM_GUI_ACTIVE" in per:
-            lines.append(f"clock_mhz (GRBM_GUI_ACTIVE / duration): {per['GRBM_GUI_ACTIVE'] / args.duration_us:.0f}")
-        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in per:
-            tf = per["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (args.duration_us * 1e-6) / 1e12
-            lines.append(f"mfma_bf16_tflops_issued (MOPS x 512 / duration): {tf:.1f}")
-    if "SQ_VALU_MFMA_BUSY_CYCLES" in per and "GRBM_GUI_ACTIVE" in per:
-        frac = per["SQ_VALU_MFMA_BUSY_CYCLES"] / (per["GRBM_GUI_ACTIVE"] * args.cus)
-        lines.append(f"mfma_busy_fraction (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {args.cus} CUs)): {frac:.3f}")
+    cycles = per["GRBM_GUI_ACTIVE"] / args.xcds if "GRBM_GUI_ACTIVE" in per else None
+    mhz = None
+    if args.duration_us and cycles is not None:
+        mhz = cycles / args.duration_us
+        lines.append(f"clock_mhz (GRBM_GUI_ACTIVE / {args.xcds} XCDs / duration): {mhz:.0f}")
+    if args.duration_us and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in per:
+        tf = per["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (args.duration_us * 1e-6) / 1e12
+        lines.append(f"mfma_bf16_tflops_issued (MOPS x 512 / duration): {tf:.1f}")
+        if mhz:
+            peak = 1024.0 * args.simds * mhz * 1e6 / 1e12
+            lines.append(f"mfma_bf16_peak_tflops_at_this_clock (1024 x {args.simds} SIMDs x clock): {peak:.1f}")
+            lines.append(f"issued_over_peak_at_this_clock: {tf / peak:.3f}")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in per and cycles:
+        frac = per["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * args.simds)
+        lines.append(f"mfma_busy_fraction (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xcds} x {args.simds} "
+                     f"SIMDs)): {frac:.3f}")
     if args.out:
         with open(args.out, "w") as f:
             f.write("\n".join(lines) + "\n")
@@ -127,10 +149,13 @@ def _counter(rows, name):
 def traffic(args):
     fetch = _counter(_rows(args.fetch), "FETCH_SIZE")
     write = _counter(_rows(args.write), "WRITE_SIZE")
-    # the copy runs first: the largest-fetch dispatch before the library's
-    # first kernel
-    first_ns = min((d for d, (n, v) in fetch.items() if "ns::" in n), default=max(fetch) + 1)
-    calib = max((d for d, (n, v) in fetch.items() if d < first_ns), key=lambda d: fetch[d][1])
+    # the copy is the first dispatch that reads a substantial part of its
+    # bytes (the fill before it reads nothing; kernels drawing inputs come
+    # after it)
+    big = [d for d, (n, v) in sorted(fetch.items()) if v * 1024.0 >= args.calib_bytes / 8]
+    if not big:
+        sys.exit("calibration copy not found")
+    calib = big[0]
     f_calib_kib = fetch[calib][1]
     w_calib_kib = write.get(calib, (None, 0.0))[1]
     if f_calib_kib <= 0 or w_calib_kib <= 0:
@@ -182,7 +207,8 @@ def main(argv=None):
     c.add_argument("--kernel", required=True)
     c.add_argument("--last", type=int, required=True)
     c.add_argument("--duration-us", type=float, default=0.0)
-    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--simds", type=int, default=1024)
     c.add_argument("--out", default="")
     c.add_argument("--cmd", action="append", default=[])
     c.set_defaults(fn=counters)

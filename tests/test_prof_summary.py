@@ -72,19 +72,22 @@ def test_trace_splits_last_dispatches_by_grid(tmp_path, capsys):
 
 def test_counters_clock_mfma_rate_and_busy(tmp_path):
     p = tmp_path / "c.csv"
-    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
-    rows = [[1, "ns::gemm_big_kernel<2>", "GRBM_GUI_ACTIVE", 1000.0],
-            [1, "ns::gemm_big_kernel<2>", "SQ_VALU_MFMA_BUSY_CYCLES", 128000.0],
-            [1, "ns::gemm_big_kernel<2>", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2000.0],
-            [2, "ns::gemm_big_kernel<2>", "GRBM_GUI_ACTIVE", 3000.0],
-            [2, "ns::gemm_big_kernel<2>", "SQ_VALU_MFMA_BUSY_CYCLES", 384000.0],
-            [2, "ns::gemm_big_kernel<2>", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 6000.0]]
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    # GRBM_GUI_ACTIVE summed over 8 XCDs: 8 x 2000 cycles in 2 us -> 1000 MHz;
+    # SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs: half of the 2000 cycles busy
+    rows = []
+    for d, (t0, t1) in enumerate([(0, 2000), (5000, 7000)], 1):
+        rows += [[d, "ns::gemm_big_kernel<2>", "GRBM_GUI_ACTIVE", 16000.0, t0, t1],
+                 [d, "ns::gemm_big_kernel<2>", "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1000.0, t0, t1],
+                 [d, "ns::gemm_big_kernel<2>", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2.048e6, t0, t1]]
     _write(p, hdr, rows)
     out = tmp_path / "o.txt"
-    ps.main(["counters", str(p), "--kernel", "gemm_big_kernel<2>", "--last", "2", "--duration-us", "2.0",
-             "--out", str(out)])
-    vals = dict(line.split(": ", 1) for line in out.read_text().splitlines() if ": " in line and not line.startswith("#"))
-    assert float(vals["GRBM_GUI_ACTIVE"]) == 2000.0
-    assert float(vals["clock_mhz (GRBM_GUI_ACTIVE / duration)"]) == 1000.0
-    assert abs(float(vals["mfma_bf16_tflops_issued (MOPS x 512 / duration)"]) - 4000 * 512 / 2e-6 / 1e12) < 0.05
-    assert float(vals["mfma_busy_fraction (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs))"]) == 0.5
+    ps.main(["counters", str(p), "--kernel", "gemm_big_kernel<2>", "--last", "2", "--out", str(out)])
+    vals = {k.split(" (")[0]: v for k, v in
+            (line.split(": ", 1) for line in out.read_text().splitlines() if ": " in line and not line.startswith("#"))}
+    assert float(vals["duration_us"]) == 2.0
+    assert float(vals["clock_mhz"]) == 1000.0
+    # 2.048e6 x 512 FLOP in 2 us = 524.3 TFLOP/s; the peak at 1 GHz is 1024 x 1024 x 1e9 = 1048.6 TFLOP/s
+    assert abs(float(vals["mfma_bf16_tflops_issued"]) - 524.3) < 0.1
+    assert float(vals["issued_over_peak_at_this_clock"]) == 0.5
+    assert float(vals["mfma_busy_fraction"]) == 0.5
