@@ -324,6 +324,68 @@ def recorded_traffic(name):
     return int(float(kv["traffic_bytes_per_launch"]))
 
 
+# ---------------------------------------------------------------- co-run interference P(R)
+CORUN_CAPS = tuple(range(16, 257, 16))   # attention workgroup caps: 1/16 .. all of the 256 CUs
+
+
+def corun_launches(t_gemm_us, t_attn_us, n_gemm):
+    """Attention launches that keep the second stream busy about as long as
+    n_gemm projection launches keep the first (at least one)."""
+    if t_gemm_us <= 0 or t_attn_us <= 0 or n_gemm < 1:
+        raise ValueError("solo times and the launch count must be positive")
+    return max(1, int(round(n_gemm * t_gemm_us / t_attn_us)))
+
+
+def corun_profile(gemm, attn, gemm_flops, attn_bytes, caps=CORUN_CAPS, n_gemm=4):
+    """NanoFlow's interference profile P(R) on one GPU ("The part that is
+    harder than it looks": the share R of the GPU given to the memory-bound
+    op, and each op's throughput when the two co-run).  `gemm(stream)` and
+    `attn(stream, cap)` enqueue one launch of the projection and of the paged
+    attention (capped at `cap` workgroups, a persistent grid: the share R =
+    cap / 256 CUs).  For each cap: the attention alone, then both together on
+    two streams released by one event (the attention launched as often as
+    keeps its stream busy as long as the projection's), each stream timed
+    from the release to its last launch with HIP events.  P_gemm and P_attn
+    are the co-run throughputs over the solo ones (uncapped); their sum over
+    1 is what overlapping gains over running the two one after the other."""
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def solo(fn, stream, n):
+        for _ in range(2):
+            fn(stream)
+        stream.synchronize()
+        return time_launches(lambda i: fn(stream), n, stream) * 1e6
+
+    t_g = solo(gemm, sa, n_gemm)
+    t_a0 = solo(lambda st: attn(st, 0), sb, 8)
+    rows = []
+    for cap in caps:
+        t_a = solo(lambda st: attn(st, cap), sb, 8)
+        n_a = corun_launches(t_g, t_a, n_gemm)
+        busy(sa)
+        e0 = torch.cuda.Event(enable_timing=True)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(sa)
+        sb.wait_event(e0)
+        for _ in range(n_gemm):
+            gemm(sa)
+        ea.record(sa)
+        for _ in range(n_a):
+            attn(sb, cap)
+        eb.record(sb)
+        sa.synchronize()
+        sb.synchronize()
+        tg_co = e0.elapsed_time(ea) * 1e3 / n_gemm
+        ta_co = e0.elapsed_time(eb) * 1e3 / n_a
+        p_g, p_a = t_g / tg_co, t_a0 / ta_co
+        rows.append({"cap": cap, "share": cap / 256.0, "attn_solo_us": t_a, "attn_corun_us": ta_co,
+                     "gemm_corun_us": tg_co, "p_gemm": p_g, "p_attn": p_a, "p_sum": p_g + p_a})
+    best = max(rows, key=lambda r: r["p_sum"])
+    return {"gemm_solo_us": t_g, "gemm_tflops_solo": gemm_flops / t_g / 1e6, "attn_solo_us": t_a0,
+            "attn_gbs_solo": attn_bytes / t_a0 / 1e3, "curve": rows, "best_cap": best["cap"],
+            "best_p_sum": best["p_sum"]}
+
+
 # ---------------------------------------------------------------- the dense-batch layer
 def dense_batch(stream, steps=10):
     """LLaMA-2-70B-shaped layer at the 2048-token dense batch (device-drawn
@@ -355,6 +417,29 @@ def dense_batch(stream, steps=10):
             return ns.make_sched(nano_rows=w.nano_splits, qkv_rows=(512,) * w.qkv_splits, overlap=overlap,
                                  prefill_tiles=True, **kw)
 
+        # the interference profile P(R): the gate-up projection at 2048 rows
+        # against the decode attention of the 512 decode rows (context 1024)
+        # capped at R workgroups, on two streams
+        nd = w.n_decode
+        rowb = torch.arange(nd, dtype=torch.int32, device="cuda")
+        pos = torch.from_numpy(b.row_pos[:nd].astype(np.int32)).cuda()
+        bt = torch.from_numpy(ns.ns_kv_block_table(h.kv, b.n_seqs, maxb)[:nd].copy()).cuda()
+        q_att = torch.randn((nd, s.n_kv_heads, s.head_dim // 8, s.group, 8), device="cuda").to(torch.bfloat16)
+        o = torch.empty((nd, DQ), device="cuda", dtype=torch.bfloat16)
+        wsb = ns.ns_op_attention_ws_bytes(h.desc, nd, maxb)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        ab = rf.attention_bytes(s, [w.decode_ctx] * nd)
+        Cb2 = torch.empty_like(Cb)
+
+        def attn_op(st, cap):
+            ns.ns_op_attention(h.desc, nd, q_att.data_ptr(), h.kv_mem.data_ptr(), h.num_blocks, rowb.data_ptr(),
+                               pos.data_ptr(), bt.data_ptr(), maxb, o.data_ptr(), ws.data_ptr(), wsb, cap, st)
+
+        def gu_op(st):
+            ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), lw["wgu"].data_ptr(),
+                                 Cb2.data_ptr(), st)
+
+        res["corun"] = corun_profile(gu_op, attn_op, rf.gemm_flops(T, F, H, True), ab)
         # nano-batched variants: the split alone on one stream (the cost of
         # smaller projection launches); overlapped in row order; decode rows'
         # attention queued last with the prompt nano-batch's projections
@@ -374,7 +459,11 @@ def dense_batch(stream, steps=10):
                               ns.make_sched(nano_rows=(512, 1536), overlap=True, prefill_tiles=True,
                                             decode_rows_first=True)),
                              ("nano_overlap_768_1280_qkv_same",
-                              ns.make_sched(nano_rows=w.nano_splits, overlap=True, prefill_tiles=True))):
+                              ns.make_sched(nano_rows=w.nano_splits, overlap=True, prefill_tiles=True)),
+                             # the split with the attention capped at the P(R) profile's best share
+                             ("nano_overlap_1024_1024_cap_best",
+                              ns.make_sched(nano_rows=(1024, 1024), overlap=True, prefill_tiles=True,
+                                            attn_wg_cap=res["corun"]["best_cap"]))):
             ns.ns_engine_set_sched(h.eng, sched)
             g = ns.ns_graph_capture(h.eng, T, out.data_ptr(), stream)
             try:
@@ -387,6 +476,9 @@ def dense_batch(stream, steps=10):
             res[f"layer_step_ms_{label}"] = t * 1e3
         best = min((k for k in res if k.startswith("layer_step_ms_nano_overlap")), key=lambda k: res[k])
         res["layer_best_nano_schedule"] = best[len("layer_step_ms_"):]
+        # the schedule search's choice over every variant timed (serial included)
+        chosen = min((k for k in res if k.startswith("layer_step_ms_")), key=lambda k: res[k])
+        res["chosen_schedule"] = chosen[len("layer_step_ms_"):]
         res["layer_tokens_per_s_nano"] = T / (res[best] * 1e-3)
         res["layer_tokens_per_s_serial"] = T / (res["layer_step_ms_serial"] * 1e-3)
         # sustained GEMM work before the isolated timings: the clock ramps up
@@ -419,14 +511,6 @@ def dense_batch(stream, steps=10):
         res["gemm_tflops"] = tot_fl / tot_t / 1e12
         res["gemm_mfma_frac"] = res["gemm_tflops"] / rf.BF16_PEAK_TFLOPS
         # decode attention: the 512 decode rows at context 1024
-        nd = w.n_decode
-        rowb = torch.arange(nd, dtype=torch.int32, device="cuda")
-        pos = torch.from_numpy(b.row_pos[:nd].astype(np.int32)).cuda()
-        bt = torch.from_numpy(ns.ns_kv_block_table(h.kv, b.n_seqs, maxb)[:nd].copy()).cuda()
-        q_att = torch.randn((nd, s.n_kv_heads, s.head_dim // 8, s.group, 8), device="cuda").to(torch.bfloat16)
-        o = torch.empty((nd, DQ), device="cuda", dtype=torch.bfloat16)
-        wsb = ns.ns_op_attention_ws_bytes(h.desc, nd, maxb)
-        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
         t = time_launches(lambda i: ns.ns_op_attention(h.desc, nd, q_att.data_ptr(), h.kv_mem.data_ptr(),
                                                        h.num_blocks, rowb.data_ptr(), pos.data_ptr(), bt.data_ptr(),
                                                        maxb, o.data_ptr(), ws.data_ptr(), wsb, 0, stream), 5, stream)
@@ -647,6 +731,7 @@ def llama80(args, stream):
         res["nano_ms"] = _graph_rate(h, b, stream, max(5, args.steps // 2), 1.0,
                                      decode_sched(nano_rows=w.nano_splits, overlap=True)) * 1e3
         ns.ns_engine_set_sched(h.eng, decode_sched())
+        res["corun"] = llama80_corun(h, b, maxb)
         # last, so that a kernel trace of this run ends with these launches
         res["att"] = attention_isolated(h, b, maxb, stream, n=100)
         res["gu"] = gate_up_isolated(h, b, stream, n=100)
@@ -656,6 +741,37 @@ def llama80(args, stream):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     return w, b, res
+
+
+def llama80_corun(h, b, maxb):
+    """P(R) at the 80-layer step's shapes: the gate-up projection at 256 rows
+    (layer 0's weights, 940 MB, streamed from HBM every launch) against the
+    step's paged attention over layer 0's cache (1.1 GB)."""
+    s = h.shape
+    T, H, F = b.n_rows, s.hidden, s.ffn
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8)
+    A = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    C = torch.empty((T, F), device="cuda", dtype=torch.bfloat16)
+    wgu = h.weights.t["layers"][0]["wgu"]
+    rowb = torch.from_numpy(b.row_seq.astype(np.int32)).cuda()
+    pos = torch.from_numpy(b.row_pos.astype(np.int32)).cuda()
+    bt = torch.from_numpy(ns.ns_kv_block_table(h.kv, b.n_seqs, maxb).copy()).cuda()
+    q_att = torch.randn((T, s.n_kv_heads, s.head_dim // 8, s.group, 8), generator=g,
+                        device="cuda").to(torch.bfloat16)
+    o = torch.empty((T, s.n_q_heads * s.head_dim), device="cuda", dtype=torch.bfloat16)
+    wsb = ns.ns_op_attention_ws_bytes(h.desc, T, maxb)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+    def attn_op(st, cap):
+        ns.ns_op_attention(h.desc, T, q_att.data_ptr(), h.kv_mem.data_ptr(), h.num_blocks, rowb.data_ptr(),
+                           pos.data_ptr(), bt.data_ptr(), maxb, o.data_ptr(), ws.data_ptr(), wsb, cap, st)
+
+    def gu_op(st):
+        ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), wgu.data_ptr(), C.data_ptr(), st)
+
+    return corun_profile(gu_op, attn_op, rf.gemm_flops(T, F, H, True),
+                         rf.attention_bytes(s, (b.row_pos + 1).tolist()))
 
 
 # ---------------------------------------------------------------- the small model's decode steps
@@ -906,9 +1022,11 @@ def main():
                           "hbm_floor_ms": rf.floor_seconds(sb) * 1e3,
                           "step_hbm_frac": sb / step_s / 1e9 / rf.HBM_PEAK_GBS,
                           "nano_overlap_ms": r["nano_ms"], "nano_split": list(w.nano_splits),
+                          "chosen_schedule": "unsplit" if step_s * 1e3 <= r["nano_ms"] else "nano_overlap",
                           "warm_seconds": args.warm_seconds, "weights_gb": r["weights_gb"],
                           "kv_pool_gb": r["kv_pool_gb"], "setup_s": r["setup_s"]}),
         "clock": _rounded(r["clock"]),
+        "corun_interference": _rounded(r["corun"]),
         "kernels": _rounded(kern),
     }
     del r
