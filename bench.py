@@ -964,6 +964,8 @@ def main():
                   "legs": sorted(legs)}
         if not args.no_dense:
             result["dense_batch"] = _rounded(_leg(dense_batch, stream))
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = _rounded(cpu_baseline(args.cpu_baseline_full))
         print(json.dumps(result, default=_jsonable), flush=True)
         return
     w, b, r = llama80(args, stream)

@@ -75,7 +75,7 @@ void attn_partition(int n_rows, int nkv, int cap_tokens, int* part_tokens, int* 
 }
 
 struct Plan {
-  size_t x, h, qkv, q_att, o, act, cosb, sinb, meta, part_acc, part_ml, part_qkv, part_res, total;
+  size_t x, h, qkv, q_att, o, act, cosb, sinb, meta, part_acc, part_ml, part_qkv, part_res, bad_tok, total;
   int tdec;  // rows of the split-K slice buffers (steps of at most 256 rows)
   size_t meta_ints;  // int32 entries of the metadata block
 };
@@ -115,6 +115,7 @@ Plan make_plan(const ns_model_desc* d, int T, int maxb) {
   const bool dec = d->dtype == NS_BF16;
   p.part_qkv = take(dec ? (size_t)kMaxSlices * p.tdec * qkv_w * 4 : 0);
   p.part_res = take(dec ? (size_t)kMaxSlices * p.tdec * d->hidden * 4 : 0);
+  p.bad_tok = take(sizeof(int32_t));  // running count of out-of-range device-fed token ids
   p.total = off;
   return p;
 }
@@ -168,6 +169,13 @@ struct ns_engine {
   bool staging_used[2] = {false, false};
   int staging_next = 0;
   int last_launches = 0;
+  // out-of-range device-fed token ids: the device count, copied to pinned
+  // host memory after each step fed from device memory, and the count the
+  // host has reported so far
+  int32_t* bad_tok_host = nullptr;
+  hipEvent_t bad_tok_ev = nullptr;
+  bool bad_tok_copied = false;
+  int32_t bad_tok_reported = 0;
   // profiling: an event after every launch of an eager serial step
   bool prof = false;
   hipEvent_t prof_start = nullptr;
@@ -191,6 +199,7 @@ struct ns_engine {
   int32_t* m_pos() const { return meta() + 2 * max_tokens; }
   int32_t* m_slot() const { return meta() + 3 * max_tokens; }
   int32_t* m_btab() const { return meta() + 4 * max_tokens; }
+  int32_t* bad_tok() const { return (int32_t*)(ws + plan.bad_tok); }
   float* part_qkv() const { return (float*)(ws + plan.part_qkv); }
   float* part_res() const { return (float*)(ws + plan.part_res); }
   char* k_layer(int l) const { return kv_dev + (size_t)l * kv_layer; }
@@ -373,7 +382,8 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
 
   // embedding (or the hidden input already in x), RoPE table, layer 0's norm
   ns::launch_step_prologue(dt, d.vocab > 0 ? e->embed : nullptr, e->m_tok(), e->x(), e->m_pos(), e->cosb(),
-                           e->sinb(), e->attn_norm[0], e->h(), n_tok, H, d.vocab, hd, d.rope_base, d.rms_eps, st);
+                           e->sinb(), e->attn_norm[0], e->h(), n_tok, H, d.vocab, hd, d.rope_base, d.rms_eps,
+                           e->bad_tok(), st);
   ++launches;
   MARK(K_EMBED);
 
@@ -554,6 +564,30 @@ int make_second_stream(ns_engine* e, float frac) {
   return NS_OK;
 }
 
+// A device-fed step's out-of-range token ids: reported by a later call once
+// the count copied after that step has arrived (no waiting).
+int check_bad_tokens(ns_engine* e) {
+  if (!e->bad_tok_copied || hipEventQuery(e->bad_tok_ev) != hipSuccess) return NS_OK;
+  const int32_t n = *e->bad_tok_host;
+  if (n > e->bad_tok_reported) {
+    const int32_t fresh = n - e->bad_tok_reported;
+    e->bad_tok_reported = n;
+    NS_FAIL(NS_EINVAL, "%d device-fed token id(s) of an earlier step lay outside [0, %d); those rows gathered the "
+                       "nearest valid embedding row",
+            fresh, e->d.vocab);
+  }
+  return NS_OK;
+}
+
+// After a step that took its token ids from device memory: copy the count.
+int copy_bad_tokens(ns_engine* e, const ns_batch* b, hipStream_t st) {
+  if (e->d.vocab == 0 || !b->token_ids_dev) return NS_OK;
+  HIP_TRY(hipMemcpyAsync(e->bad_tok_host, e->bad_tok(), sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipEventRecord(e->bad_tok_ev, st));
+  e->bad_tok_copied = true;
+  return NS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -635,10 +669,17 @@ int ns_engine_create(const ns_model_desc* desc, const ns_weights* w, ns_kv* kv, 
       return fail(NS_EHIP);
     }
   }
-  if (hipEventCreateWithFlags(&e->ev_join, hipEventDisableTiming) != hipSuccess) {
+  if (hipEventCreateWithFlags(&e->ev_join, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&e->bad_tok_ev, hipEventDisableTiming) != hipSuccess) {
     ns::set_error("hipEventCreate failed");
     return fail(NS_EHIP);
   }
+  if (hipHostMalloc((void**)&e->bad_tok_host, sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+      hipMemset(e->bad_tok(), 0, sizeof(int32_t)) != hipSuccess) {
+    ns::set_error("token-id counter set-up failed");
+    return fail(NS_EHIP);
+  }
+  *e->bad_tok_host = 0;
   for (int k = 0; k < 2; ++k) {
     if (hipHostMalloc((void**)&e->staging[k], plan.meta_ints * sizeof(int32_t), hipHostMallocDefault) !=
             hipSuccess ||
@@ -663,6 +704,11 @@ void ns_engine_destroy(ns_engine* e) {
     if (e->ev_att[i]) hipEventDestroy(e->ev_att[i]);
   }
   if (e->ev_join) hipEventDestroy(e->ev_join);
+  if (e->bad_tok_ev) {
+    hipEventSynchronize(e->bad_tok_ev);
+    hipEventDestroy(e->bad_tok_ev);
+  }
+  if (e->bad_tok_host) hipHostFree(e->bad_tok_host);
   for (hipEvent_t ev : e->prof_ev) hipEventDestroy(ev);
   if (e->prof_start) hipEventDestroy(e->prof_start);
   for (int k = 0; k < 2; ++k) {
@@ -689,11 +735,13 @@ int ns_decode_step(ns_engine* e, const ns_batch* b, void* out, void* stream) {
   if (!e || !out) NS_FAIL(NS_EINVAL, "null engine or output");
   int rc = check_batch(e, b, e->max_tokens, fused_rope(e, e->sched));
   if (rc) return rc;
+  if ((rc = check_bad_tokens(e))) return rc;
   hipStream_t st = (hipStream_t)stream;
   if ((rc = upload_meta(e, b, b->n_tok, st))) return rc;
   if (e->d.vocab == 0)
     HIP_TRY(hipMemcpyAsync(e->x(), b->hidden_in, (size_t)b->n_tok * e->d.hidden * 4, hipMemcpyDeviceToDevice, st));
-  return enqueue_step(e, e->sched, b->n_tok, out, st, false);
+  if ((rc = enqueue_step(e, e->sched, b->n_tok, out, st, false))) return rc;
+  return copy_bad_tokens(e, b, st);
 }
 
 int ns_graph_capture(ns_engine* e, int32_t bucket, void* out, void* stream, ns_graph** gout) {
@@ -741,12 +789,13 @@ int ns_graph_replay(ns_graph* g, const ns_batch* b, void* stream) {
   ns_engine* e = g->e;
   int rc = check_batch(e, b, g->bucket, g->fused_rope);
   if (rc) return rc;
+  if ((rc = check_bad_tokens(e))) return rc;
   hipStream_t st = (hipStream_t)stream;
   if ((rc = upload_meta(e, b, g->bucket, st))) return rc;
   if (e->d.vocab == 0)
     HIP_TRY(hipMemcpyAsync(e->x(), b->hidden_in, (size_t)b->n_tok * e->d.hidden * 4, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipGraphLaunch(g->exec, st));
-  return NS_OK;
+  return copy_bad_tokens(e, b, st);
 }
 
 int ns_graph_set_capture(ns_engine* e, const int32_t* buckets, int32_t n, void* out, void* stream,

@@ -171,19 +171,24 @@ __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restric
 // projections: the embedding gather (models with a vocabulary; otherwise x
 // already holds the hidden input), this row's RoPE cos/sin (the table every
 // layer reads, built once per step) and layer 0's RMSNorm.  Three launches
-// become one.
+// become one.  A token id outside [0, V) (possible only for ids fed from
+// device memory) gathers the nearest valid row and adds 1 to *bad_tok.
 template <typename T>
 __global__ void __launch_bounds__(256) step_prologue_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
                                                             float* __restrict__ x, const int32_t* __restrict__ pos,
                                                             float* __restrict__ cosb, float* __restrict__ sinb,
                                                             const T* __restrict__ g0, T* __restrict__ h, int H, int V,
-                                                            int half, double log2_base, float eps) {
+                                                            int half, double log2_base, float eps,
+                                                            int32_t* __restrict__ bad_tok) {
   const int t = blockIdx.x;
   float* xr = x + (long)t * H;
   float ss = 0.f;
   if (E) {
     int id = tok[t];
-    id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+    if (id < 0 || id >= V) {
+      if (threadIdx.x == 0 && bad_tok) atomicAdd(bad_tok, 1);
+      id = id < 0 ? 0 : V - 1;
+    }
     const T* src = E + (long)id * H;
     for (int i = threadIdx.x; i < H; i += 256) {
       const float v = Elem<T>::load(src, i);
@@ -439,15 +444,15 @@ void launch_rope_table(const int32_t* pos, float* cosb, float* sinb, int T, int 
 
 void launch_step_prologue(int dtype, const void* E, const int32_t* tok, float* x, const int32_t* pos, float* cosb,
                           float* sinb, const void* g0, void* h, int T, int H, int V, int d, float base, float eps,
-                          hipStream_t st) {
+                          int32_t* bad_tok, hipStream_t st) {
   if (T <= 0) return;
   const double lb = log2((double)base);
   if (dtype == NS_DT_BF16)
     hipLaunchKernelGGL(step_prologue_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)E, tok, x, pos, cosb,
-                       sinb, (const bf16_t*)g0, (bf16_t*)h, H, V, d / 2, lb, eps);
+                       sinb, (const bf16_t*)g0, (bf16_t*)h, H, V, d / 2, lb, eps, bad_tok);
   else
     hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)E, tok, x, pos, cosb,
-                       sinb, (const float*)g0, (float*)h, H, V, d / 2, lb, eps);
+                       sinb, (const float*)g0, (float*)h, H, V, d / 2, lb, eps, bad_tok);
 }
 
 void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st) {

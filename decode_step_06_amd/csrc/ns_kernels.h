@@ -55,10 +55,12 @@ void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_strid
 void launch_reduce_rows(const float* x, const float* P, long slice_stride, int splits, float* out, int T, int H,
                         hipStream_t st);
 // Embedding (E non-null) or hidden input already in x, RoPE cos/sin table,
-// and layer 0's RMSNorm, one workgroup per row.
+// and layer 0's RMSNorm, one workgroup per row.  Rows whose token id lies
+// outside [0, V) gather the nearest valid row and add 1 to *bad_tok (may be
+// null).
 void launch_step_prologue(int dtype, const void* E, const int32_t* tok, float* x, const int32_t* pos, float* cosb,
                           float* sinb, const void* g0, void* h, int T, int H, int V, int d, float base, float eps,
-                          hipStream_t st);
+                          int32_t* bad_tok, hipStream_t st);
 // qkv holds `splits` fp32 slices (slice_stride apart) that are summed first.
 void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, const float* cosb,
                     const float* sinb, const int32_t* slot, void* q_att, void* kc, void* vc, int T, int nq, int nkv,

@@ -238,8 +238,12 @@ typedef struct {
  * step with no host round trip, and the host can form step i+1's rows while
  * step i still runs (NanoFlow review, "Runtime details that keep the
  * pipeline fed").  The ids are copied on the step's stream after the
- * metadata; the host cannot check them, so an id outside [0, vocab) gathers
- * the nearest valid embedding row. */
+ * metadata; the host cannot check them before the step runs: an id outside
+ * [0, vocab) gathers the nearest valid embedding row and is counted on the
+ * device.  The count is copied back after each such step, and a later
+ * ns_decode_step / ns_graph_replay on this engine (the first one that finds
+ * that copy complete, without waiting for it) returns NS_EINVAL, with no
+ * other effect, saying how many ids were out of range. */
 typedef struct {
   int32_t n_tok;
   const int32_t* token_ids;

@@ -105,3 +105,46 @@ def test_device_token_feedback_matches_host_driven_decoding():
     finally:
         h.destroy()
         torch.cuda.synchronize()
+
+
+def test_out_of_range_device_token_is_reported_by_a_later_call():
+    """A token id fed from device memory outside [0, vocab): the step gathers
+    the nearest valid embedding row (the same logits as that id), counts the
+    row on the device, and a later call reports it (NS_EINVAL, no other
+    effect); after that report, calls succeed again."""
+    shape = SMALL
+    B = 3
+    weights = gen_weights(shape, seed=0)
+    dw = DeviceWeights.from_numpy(shape, weights)
+    ctx = np.array([9, 20, 33])
+    maxb = blocks_for(ctx)
+    nblk = int(sum(-(-int(n) // 16) for n in ctx)) + 2
+    h = create_engine(shape, dw, nblk, B, maxb, B, None, None)
+    stream = torch.cuda.Stream()
+    try:
+        alloc_sequences(h, ctx)
+        past_seq = np.concatenate([np.full(c - 1, s, np.int32) for s, c in enumerate(ctx)])
+        past_pos = np.concatenate([np.arange(c - 1, dtype=np.int32) for c in ctx])
+        fill_past_random_on_device(h, past_seq, past_pos, seed=4)
+        seq = np.arange(B, dtype=np.int32)
+        pos = ctx - 1
+        valid = np.array([5, shape.vocab - 1, 0], np.int32)
+        ref = torch.full((B, shape.vocab), float("nan"), device="cuda")
+        ns.ns_decode_step(h.eng, ns.Batch(seq, pos, valid), ref.data_ptr(), stream)
+        stream.synchronize()
+        bad = torch.tensor([5, shape.vocab + 17, -3], dtype=torch.int32, device="cuda")
+        out = torch.full_like(ref, float("nan"))
+        ns.ns_decode_step(h.eng, ns.Batch(seq, pos, tokens_dev=bad), out.data_ptr(), stream)
+        stream.synchronize()
+        # clamped to the nearest valid id: the same step as the valid ids
+        assert torch.equal(out, ref)
+        with pytest.raises(ns.NSError) as err:
+            ns.ns_decode_step(h.eng, ns.Batch(seq, pos, valid), out.data_ptr(), stream)
+        assert err.value.code == ns.NS_EINVAL and "2 device-fed token id" in str(err.value)
+        say(f"  reported: {err.value}")
+        ns.ns_decode_step(h.eng, ns.Batch(seq, pos, valid), out.data_ptr(), stream)
+        stream.synchronize()
+        assert torch.equal(out, ref)
+    finally:
+        h.destroy()
+        torch.cuda.synchronize()
