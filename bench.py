@@ -923,6 +923,25 @@ def _leg(fn, *a, **kw):
         return {"error": repr(e)}
 
 
+def _small_legs(args, stream, result):
+    """The 0.5B-shaped step (32 rows, then 1 row), and the batch sweep and
+    bucketed capture over its weights."""
+    if args.no_small:
+        return
+
+    def small(detail, wname):
+        res, dw = small_step(stream, wname, 200, 8.0 if detail else 3.0, detail)
+        return res, dw
+    sm, dw = small(True, SMALL)
+    result[SMALL] = _rounded(json.loads(json.dumps(sm, default=_jsonable)))
+    result["qwen05b_b1_ctx512"] = _rounded(_leg(lambda: small(False, "qwen05b_b1_ctx512")[0]))
+    if not args.no_sweep:
+        result["batch_sweep"] = _rounded(_leg(batch_sweep, stream, dw))
+        result["bucketed_capture"] = _rounded(_leg(bucket_capture, stream, dw))
+    del dw
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -962,6 +981,7 @@ def main():
     if "headline" not in legs:
         result = {"metric": "decode tokens/s @1 GPU; attn HBM GB/s and GEMM MFMA % of peak", "value": None,
                   "legs": sorted(legs)}
+        _small_legs(args, stream, result)
         if not args.no_dense:
             result["dense_batch"] = _rounded(_leg(dense_batch, stream))
         if not args.no_cpu_baseline:
@@ -1032,18 +1052,7 @@ def main():
         "kernels": _rounded(kern),
     }
     del r
-    if not args.no_small:
-        def small(detail, wname):
-            res, dw = small_step(stream, wname, 200, 8.0 if detail else 3.0, detail)
-            return res, dw
-        sm, dw = small(True, SMALL)
-        result[SMALL] = _rounded(json.loads(json.dumps(sm, default=_jsonable)))
-        result["qwen05b_b1_ctx512"] = _rounded(_leg(lambda: small(False, "qwen05b_b1_ctx512")[0]))
-        if not args.no_sweep:
-            result["batch_sweep"] = _rounded(_leg(batch_sweep, stream, dw))
-            result["bucketed_capture"] = _rounded(_leg(bucket_capture, stream, dw))
-        del dw
-        torch.cuda.empty_cache()
+    _small_legs(args, stream, result)
     if not args.no_dense:
         result["dense_batch"] = _rounded(_leg(dense_batch, stream))
     result["torch_copy_rate"] = _rounded(copy_ceiling(stream))
