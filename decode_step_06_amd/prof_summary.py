@@ -128,6 +128,20 @@ def counters(args):
         frac = per["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * args.simds)
         lines.append(f"mfma_busy_fraction (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xcds} x {args.simds} "
                      f"SIMDs)): {frac:.3f}")
+    # wave-time shares: the SQ wave counters all count in 4-cycle units
+    if per.get("SQ_WAVE_CYCLES"):
+        for name, what in (("SQ_WAIT_INST_ANY", "waiting to issue an instruction"),
+                           ("SQ_WAIT_ANY", "waiting on a counter or barrier"),
+                           ("SQ_WAIT_INST_LDS", "waiting to issue an LDS instruction"),
+                           ("SQ_ACTIVE_INST_ANY", "issuing instructions")):
+            if name in per:
+                lines.append(f"share_of_wave_time {what} ({name} / SQ_WAVE_CYCLES): "
+                             f"{per[name] / per['SQ_WAVE_CYCLES']:.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in per and per.get("SQ_LDS_IDX_ACTIVE"):
+        busy = per["SQ_LDS_IDX_ACTIVE"] - per["SQ_LDS_BANK_CONFLICT"]
+        if busy > 0:
+            lines.append(f"lds_bank_conflict_rate (SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - "
+                         f"SQ_LDS_BANK_CONFLICT)): {per['SQ_LDS_BANK_CONFLICT'] / busy:.3f}")
     if args.out:
         with open(args.out, "w") as f:
             f.write("\n".join(lines) + "\n")

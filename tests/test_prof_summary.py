@@ -91,3 +91,24 @@ def test_counters_clock_mfma_rate_and_busy(tmp_path):
     assert abs(float(vals["mfma_bf16_tflops_issued"]) - 524.3) < 0.1
     assert float(vals["issued_over_peak_at_this_clock"]) == 0.5
     assert float(vals["mfma_busy_fraction"]) == 0.5
+
+
+def test_counters_wave_time_shares_and_bank_conflicts(tmp_path):
+    p = tmp_path / "c.csv"
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for d in (1, 2):
+        rows += [[d, "ns::gemm_big_kernel<2>", "SQ_WAVE_CYCLES", 1000.0, 0, 10],
+                 [d, "ns::gemm_big_kernel<2>", "SQ_WAIT_INST_ANY", 550.0, 0, 10],
+                 [d, "ns::gemm_big_kernel<2>", "SQ_WAIT_ANY", 65.0, 0, 10],
+                 [d, "ns::gemm_big_kernel<2>", "SQ_LDS_IDX_ACTIVE", 300.0, 0, 10],
+                 [d, "ns::gemm_big_kernel<2>", "SQ_LDS_BANK_CONFLICT", 100.0, 0, 10]]
+    _write(p, hdr, rows)
+    out = tmp_path / "o.txt"
+    ps.main(["counters", str(p), "--kernel", "gemm_big_kernel<2>", "--last", "2", "--out", str(out)])
+    text = out.read_text()
+    assert "waiting to issue an instruction (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES): 0.550" in text
+    assert "waiting on a counter or barrier (SQ_WAIT_ANY / SQ_WAVE_CYCLES): 0.065" in text
+    assert "SQ_WAIT_INST_LDS" not in text
+    # 100 conflict cycles over 200 conflict-free active cycles
+    assert "SQ_LDS_BANK_CONFLICT)): 0.500" in text
