@@ -40,6 +40,7 @@ namespace {
 constexpr int kMaxParts = 4;
 constexpr int kSplitRows = 256;  // steps of at most this many rows use the split-K projections
 constexpr int kMaxSlices = 8;
+constexpr long kOrderItems = 1024;  // attention work items from which rows go longest first
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int elem_size(int32_t dtype) { return dtype == NS_BF16 ? 2 : 4; }
@@ -98,7 +99,7 @@ Plan make_plan(const ns_model_desc* d, int T, int maxb) {
   p.act = take((size_t)T * d->ffn * es);
   p.cosb = take((size_t)T * d->head_dim / 2 * 4);
   p.sinb = take((size_t)T * d->head_dim / 2 * 4);
-  p.meta_ints = 4 * (size_t)T + (size_t)T * maxb;
+  p.meta_ints = 5 * (size_t)T + (size_t)T * maxb;
   p.meta = take(p.meta_ints * 4);
   long items = 0;
   for (int n = 1; n <= T; ++n) {
@@ -198,7 +199,8 @@ struct ns_engine {
   int32_t* m_seq() const { return meta() + max_tokens; }
   int32_t* m_pos() const { return meta() + 2 * max_tokens; }
   int32_t* m_slot() const { return meta() + 3 * max_tokens; }
-  int32_t* m_btab() const { return meta() + 4 * max_tokens; }
+  int32_t* m_order() const { return meta() + 4 * max_tokens; }
+  int32_t* m_btab() const { return meta() + 5 * max_tokens; }
   int32_t* bad_tok() const { return (int32_t*)(ws + plan.bad_tok); }
   float* part_qkv() const { return (float*)(ws + plan.part_qkv); }
   float* part_res() const { return (float*)(ws + plan.part_res); }
@@ -210,6 +212,7 @@ struct ns_graph {
   ns_engine* e = nullptr;
   int bucket = 0;
   bool fused_rope = false;  // captured with RoPE fused into attention: one row per sequence
+  ns_sched sched{};         // the schedule captured (its attention parts order the rows at replay)
   void* out = nullptr;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
@@ -274,9 +277,16 @@ int check_batch(const ns_engine* e, const ns_batch* b, int max_rows, bool one_ro
   return NS_OK;
 }
 
-// Pack the step metadata for `rows` rows (rows >= n_tok are padding) into
-// pinned staging and copy it to the device with one transfer.
-int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
+// The row ranges of a step's attention launches: the QKV parts when the QKV
+// projection is split, else the nano-batches.
+std::vector<std::pair<int, int>> attn_row_parts(const ns_sched& sc, int n_tok) {
+  return sc.n_qkv > 1 ? row_parts(n_tok, sc.n_qkv, sc.qkv_rows) : row_parts(n_tok, sc.n_nano, sc.nano_rows);
+}
+
+// Pack the step metadata for `rows` rows (rows >= n_tok are padding) of a
+// step run under schedule sc into pinned staging and copy it to the device
+// with one transfer.
+int upload_meta(ns_engine* e, const ns_batch* b, int rows, const ns_sched& sc, hipStream_t st) {
   const int k = e->staging_next;
   e->staging_next ^= 1;
   if (e->staging_used[k]) HIP_TRY(hipEventSynchronize(e->staging_ev[k]));
@@ -286,7 +296,8 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
   int32_t* rowb = m + T;  // sequence of each row (-1: padding)
   int32_t* pos = m + 2 * T;
   int32_t* slot = m + 3 * T;
-  int32_t* btab = m + 4 * T;
+  int32_t* order = m + 4 * T;  // attention's row order within each of its parts
+  int32_t* btab = m + 5 * T;
   // one block-table row per step row (attention then reads its blocks
   // without first looking up the row's sequence)
   for (int i = 0; i < rows; ++i) {
@@ -307,7 +318,16 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, hipStream_t st) {
     const int32_t p = b->pos[i];
     slot[i] = tab[p / NS_BLOCK_SIZE] * NS_BLOCK_SIZE + p % NS_BLOCK_SIZE;
   }
-  const size_t head = 4 * (size_t)T * sizeof(int32_t);
+  // longest context first within each attention part (padding rows last);
+  // ties in row order
+  for (const auto& pr : attn_row_parts(sc, rows)) {
+    for (int i = pr.first; i < pr.second; ++i) order[i] = i;
+    std::stable_sort(order + pr.first, order + pr.second, [&](int32_t a, int32_t c) {
+      const int32_t ka = rowb[a] < 0 ? -1 : pos[a], kc = rowb[c] < 0 ? -1 : pos[c];
+      return ka > kc;
+    });
+  }
+  const size_t head = 5 * (size_t)T * sizeof(int32_t);
   const size_t bytes = head + (size_t)rows * e->maxb * sizeof(int32_t);
   HIP_TRY(hipMemcpyAsync(e->meta(), m, bytes, hipMemcpyHostToDevice, st));
   HIP_TRY(hipEventRecord(e->staging_ev[k], st));
@@ -340,6 +360,12 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
                  &a->n_parts, &a->waves);
   a->wg_cap = e->sched.attn_wg_cap;
   a->row_seq = e->sched.prefill_tiles ? e->m_seq() : nullptr;
+  // Longest rows first once the work items outnumber what the chip holds at
+  // once (the dispatch then hands the short ones to the CUs that free up
+  // first: 256 rows of the 70B shape with contexts 512..1536, 202 -> 192 us
+  // in isolation).  Below that every item starts at once and the order
+  // would only add a dependent load in front of each.
+  if ((long)(r1 - r0) * a->nkv * a->n_parts >= kOrderItems) a->row_order = e->m_order();
 }
 
 // The kernel sequence of one step over n_tok rows (metadata already on the
@@ -356,7 +382,7 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   const size_t es = e->es;
   const bool overlap = sc.overlap != 0;
   auto nano = row_parts(n_tok, sc.n_nano, sc.nano_rows);
-  auto qparts = sc.n_qkv > 1 ? row_parts(n_tok, sc.n_qkv, sc.qkv_rows) : nano;
+  auto qparts = attn_row_parts(sc, n_tok);
   int launches = 0;
   hipStream_t sa = overlap ? e->s2 : st;
   const bool prof = e->prof && !capturing && !overlap;
@@ -737,7 +763,7 @@ int ns_decode_step(ns_engine* e, const ns_batch* b, void* out, void* stream) {
   if (rc) return rc;
   if ((rc = check_bad_tokens(e))) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if ((rc = upload_meta(e, b, b->n_tok, st))) return rc;
+  if ((rc = upload_meta(e, b, b->n_tok, e->sched, st))) return rc;
   if (e->d.vocab == 0)
     HIP_TRY(hipMemcpyAsync(e->x(), b->hidden_in, (size_t)b->n_tok * e->d.hidden * 4, hipMemcpyDeviceToDevice, st));
   if ((rc = enqueue_step(e, e->sched, b->n_tok, out, st, false))) return rc;
@@ -755,6 +781,7 @@ int ns_graph_capture(ns_engine* e, int32_t bucket, void* out, void* stream, ns_g
   g->bucket = bucket;
   g->out = out;
   g->fused_rope = fused_rope(e, e->sched);
+  g->sched = e->sched;
   hipError_t he = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
   if (he != hipSuccess) {
     delete g;
@@ -791,7 +818,7 @@ int ns_graph_replay(ns_graph* g, const ns_batch* b, void* stream) {
   if (rc) return rc;
   if ((rc = check_bad_tokens(e))) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if ((rc = upload_meta(e, b, g->bucket, st))) return rc;
+  if ((rc = upload_meta(e, b, g->bucket, g->sched, st))) return rc;
   if (e->d.vocab == 0)
     HIP_TRY(hipMemcpyAsync(e->x(), b->hidden_in, (size_t)b->n_tok * e->d.hidden * 4, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipGraphLaunch(g->exec, st));

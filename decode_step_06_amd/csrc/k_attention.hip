@@ -565,7 +565,7 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
     const int32_t* __restrict__ row_bseq, const int32_t* __restrict__ row_pos, const int32_t* __restrict__ btab,
     bf16_t* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml, int maxb, int row0,
     int n_rows, int nq, int nkv, int P, int n_parts, float scale_log2, const int32_t* __restrict__ skip_seq,
-    RopeIn ra) {
+    RopeIn ra, const int32_t* __restrict__ row_order) {
   static_assert(G <= 16 && D % 32 == 0, "heads must fit the 16 MFMA columns, d whole k-steps");
   constexpr int NCH = D / 8;  // 16-byte chunks per head row
   constexpr int KS = D / 32, DT = D / 16;
@@ -578,7 +578,9 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
     const int part = w % n_parts;
     const int rest = w / n_parts;
     const int g = rest % nkv;
-    const int t = row0 + rest / nkv;
+    // rows in the order given (longest context first: the long items start
+    // early and the dispatch tail is short ones), else in index order
+    const int t = row_order ? row_order[row0 + rest / nkv] : row0 + rest / nkv;
     if (skip_seq) {  // rows of prefill tiles belong to the prefill kernel
       const int t0 = row0 + ((t - row0) & ~31);
       if (t0 + 32 <= row0 + n_rows && prefill_tile(skip_seq, row_pos, t0, lane)) continue;
@@ -749,16 +751,21 @@ static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
     const RopeIn ra{a.rope_qkv, a.rope_slice_stride, a.rope_splits, a.cosb, a.sinb, a.slot};
     if (a.rope_qkv) {  // the fused prologue runs on 8 or 4 wavefronts per item
       if (a.waves == 8)
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, true>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra);
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, true>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra,
+                           a.row_order);
       else
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, true>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra);
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, true>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra,
+                           a.row_order);
     } else {
       if (a.waves == 1)
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1, false>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS, ra);
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1, false>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS, ra,
+                           a.row_order);
       else if (a.waves == 8)
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, false>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra);
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, false>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra,
+                           a.row_order);
       else
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, false>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra);
+        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, false>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra,
+                           a.row_order);
     }
   } else {
     if (a.waves == 1)

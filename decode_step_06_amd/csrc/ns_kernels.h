@@ -100,6 +100,10 @@ struct AttnArgs {
   const float* cosb = nullptr;      // [T][d/2]
   const float* sinb = nullptr;
   const int32_t* slot = nullptr;    // [T] cache slot of each row (-1: none)
+  // bf16 matrix-core kernel: the order of its rows, row_order[row0 .. row0 +
+  // n_rows) a permutation of those row indices (null: index order).  Rows are
+  // independent, so the order changes no result.
+  const int32_t* row_order = nullptr;
 };
 int attention_supported(int dtype, int d, int G);
 // Rows are taken in tiles of 32 from row0; a tile of one sequence at
