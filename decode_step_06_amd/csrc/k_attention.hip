@@ -344,7 +344,9 @@ struct MfmaPass {
 };
 
 // Issue every K and V load of the pass (tokens past the context end are
-// masked by the math).
+// masked by the math).  Each cached K/V byte is read once per step, so the
+// loads are non-temporal: measured on MI355X, random 4 KB reads stream at
+// 6.8-6.9 TB/s with the hint and 6.1-6.2 TB/s without.
 // Block ids of the pass's 4 blocks, wave-uniform scalars (never an indexed
 // array: a lane-dependent pick between two entries of one made the compiler
 // keep the array in LDS, a store and a load between the block ids and every
@@ -381,7 +383,7 @@ __device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restr
       const int slot = 8 * ((hc >> 2) & 1) + 4 * u + (hc & 3);
 #pragma unroll
       for (int j = 0; j < D / 32; ++j)
-        r.k[s][u][j] = *(const bf16x8_t*)(kb + ((long)(4 * j + grp) * 16 + slot) * 8);
+        r.k[s][u][j] = __builtin_nontemporal_load((const bf16x8_t*)(kb + ((long)(4 * j + grp) * 16 + slot) * 8));
     }
   }
   // PV step s, d tile dt, A row hc: V^T row 16 dt + hc, tokens
@@ -391,7 +393,8 @@ __device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restr
     const int b = (grp >> 1) ? (s ? b3 : b1) : (s ? b2 : b0);
     const bf16_t* vb = vc + ((long)b * nkv + g) * HEAD_BLK + 8 * (grp & 1);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) r.v[dt][s] = *(const u32x4_t*)(vb + (long)(16 * dt + hc) * 16);
+    for (int dt = 0; dt < D / 16; ++dt)
+      r.v[dt][s] = __builtin_nontemporal_load((const u32x4_t*)(vb + (long)(16 * dt + hc) * 16));
   }
 }
 

@@ -249,7 +249,9 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
 
 constexpr unsigned BUF_RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit dwords, no swizzle
 
-template <int EPI, typename OutT, int BM = 256>
+// BNT: the B operand streams with non-temporal loads (set when one row tile
+// covers all M rows, so that each B slab is read by one workgroup only).
+template <int EPI, typename OutT, int BM = 256, int BNT = 0>
 __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
                                                        const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
                                                        void* __restrict__ Cv, int ldc, int splits, long slice_stride,
@@ -327,11 +329,16 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
     // packed B: slab ks is a contiguous [rows][32] block
     const unsigned soff_b = bpk ? (unsigned)ks * (unsigned)ldb * (BK * 2) : soff;
     char* base = lds + (kt % NSTAGE) * STAGE;
+    // load slots j < AG / 4 carry A rows, the rest B rows (wave < 4)
+    static_assert(AG % 4 == 0, "A load slots");
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       const int g = wave + 4 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < AG ? ra : rb, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j],
-                                               g < AG ? soff : soff_b, 0, 0);
+      if (j < AG / 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j], soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j], soff_b, 0,
+                                                 BNT ? 2 : 0);  // cache policy: 2 = nt
     }
   };
   // v_mfma_f32_32x32x16_bf16 operands: lane l holds row (or column) l % 32
@@ -491,7 +498,9 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
 // rows) for all rows; its NW wavefronts split K into contiguous ranges.  Each
 // lane loads its fragment of the weight rows straight from global memory into
 // MFMA registers, U k-steps at a time, so every wavefront keeps U x 16 x NB
-// rows x 64 bytes in flight with no LDS staging.  The wavefront partials meet
+// rows x 64 bytes in flight with no LDS staging.  Each weight byte is read
+// once per launch: non-temporal loads (the activations, re-read by every
+// workgroup, stay ordinary).  The wavefront partials meet
 // in LDS and are summed in wavefront order (deterministic), then wavefront 0
 // applies the fused epilogue.  The K partition depends only on K and NW, so a
 // row's result does not depend on how many rows share the launch.
@@ -552,7 +561,8 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
 #pragma unroll
     for (int u = 0; u < R; ++u) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bv[u][j] = *(const bf16x8_t*)(brow[j] + (s + u) * bstep);
+      for (int j = 0; j < NB; ++j)
+        bv[u][j] = __builtin_nontemporal_load((const bf16x8_t*)(brow[j] + (s + u) * bstep));
 #pragma unroll
       for (int i = 0; i < MF; ++i) av[u][i] = *(const bf16x8_t*)(arow[i] + (s + u) * 32);
     }
@@ -664,8 +674,12 @@ static void run_big(int M, int N, int K, const void* A, int lda, const void* B, 
                     hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
-  hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0, st,
-                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+  if (M <= BM)  // one row tile: each weight slab is read once
+    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 1>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0,
+                       st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 0>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0,
+                       st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
 }
 
 template <int MF, int NF, int NW, int EPI>
