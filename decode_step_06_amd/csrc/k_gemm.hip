@@ -47,7 +47,9 @@ struct GemmCfg {
 
 }  // namespace
 
-template <int BM, int BN, int BK, int WM, int WN, int EPI, typename OutT>
+// BNT: B loads are non-temporal (one row tile covers all M rows, so each B
+// element is read by one workgroup).
+template <int BM, int BN, int BK, int WM, int WN, int EPI, typename OutT, int BNT = 0>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                                  const bf16_t* __restrict__ B, int ldb, int M, int N,
                                                                  int K, void* __restrict__ Cv, int ldc, int splits,
@@ -97,8 +99,9 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
       const int c = tid + i * C::NT;
       if (c < C::B_CH) {
         const int r = c / (BK / 8), k = k0 + (c % (BK / 8)) * 8;
-        rb[i] = bpk ? *(const u32x4_t*)(B + ((long)(k >> 5) * ldb + b_row(r)) * 32 + (k & 31))
-                    : *(const u32x4_t*)(B + (long)b_row(r) * ldb + k);
+        const u32x4_t* src = bpk ? (const u32x4_t*)(B + ((long)(k >> 5) * ldb + b_row(r)) * 32 + (k & 31))
+                                 : (const u32x4_t*)(B + (long)b_row(r) * ldb + k);
+        rb[i] = BNT ? __builtin_nontemporal_load(src) : *src;
       }
     }
   };
@@ -664,9 +667,14 @@ static void run_bf16(int M, int N, int K, const void* A, int lda, const void* B,
                      hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? BN / 2 : BN;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t>), dim3((unsigned)tiles, (unsigned)splits),
-                     dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc,
-                     splits, slice_stride, bpk);
+  if (M <= BM)  // one row tile: each weight element is read once
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t, 1>), dim3((unsigned)tiles,
+                       (unsigned)splits), dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M,
+                       N, K, Cv, ldc, splits, slice_stride, bpk);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t, 0>), dim3((unsigned)tiles,
+                       (unsigned)splits), dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M,
+                       N, K, Cv, ldc, splits, slice_stride, bpk);
 }
 
 template <int EPI, int BM = 256>

@@ -95,7 +95,7 @@ template <int S>
 __device__ __forceinline__ f32x4_t slice_sum4_n(const float* p, long slice_stride) {
   f32x4_t v[S];
 #pragma unroll
-  for (int s = 0; s < S; ++s) v[s] = *(const f32x4_t*)(p + s * slice_stride);
+  for (int s = 0; s < S; ++s) v[s] = __builtin_nontemporal_load((const f32x4_t*)(p + s * slice_stride));
   f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < S; ++s) a += v[s];
