@@ -245,15 +245,22 @@ def step_kernels(h, b, stream, reps=5):
     return res
 
 
+ORDER_ITEMS = 1024  # work items from which the engine takes attention rows longest context first
+
+
 def attention_isolated(h, b, maxb, stream, n=400):
     """The step's attention (the layers' caches in turn, the step's rows and
-    block tables, the engine's launch shape) launched n times back to back on
-    `stream`: HIP events around the loop give its average launch duration --
-    the figure a kernel trace of this run reports for these launches."""
+    block tables, the engine's launch shape and row order) launched n times
+    back to back on `stream`: HIP events around the loop give its average
+    launch duration -- the figure a kernel trace of this run reports for these
+    launches."""
     s = h.shape
     nd = b.n_rows
-    rowb = torch.from_numpy(b.row_seq.astype(np.int32)).cuda()
-    pos = torch.from_numpy(b.row_pos.astype(np.int32)).cuda()
+    order = np.arange(nd)
+    if nd * s.n_kv_heads >= ORDER_ITEMS:  # as the engine orders them (the op takes rows as given)
+        order = np.argsort(-(b.row_pos.astype(np.int64)), kind="stable")
+    rowb = torch.from_numpy(b.row_seq[order].astype(np.int32)).cuda()
+    pos = torch.from_numpy(b.row_pos[order].astype(np.int32)).cuda()
     bt = torch.from_numpy(ns.ns_kv_block_table(h.kv, b.n_seqs, maxb).copy()).cuda()
     g = torch.Generator(device="cuda")
     g.manual_seed(5)
@@ -924,8 +931,8 @@ def _leg(fn, *a, **kw):
 
 
 def _small_legs(args, stream, result):
-    """The 0.5B-shaped step (32 rows, then 1 row), and the batch sweep and
-    bucketed capture over its weights."""
+    """The 0.5B-shaped step at 32 rows (then at 1 row with the 'b1' leg), and
+    the batch sweep and bucketed capture over its weights."""
     if args.no_small:
         return
 
@@ -934,7 +941,8 @@ def _small_legs(args, stream, result):
         return res, dw
     sm, dw = small(True, SMALL)
     result[SMALL] = _rounded(json.loads(json.dumps(sm, default=_jsonable)))
-    result["qwen05b_b1_ctx512"] = _rounded(_leg(lambda: small(False, "qwen05b_b1_ctx512")[0]))
+    if not args.no_b1:
+        result["qwen05b_b1_ctx512"] = _rounded(_leg(lambda: small(False, "qwen05b_b1_ctx512")[0]))
     if not args.no_sweep:
         result["batch_sweep"] = _rounded(_leg(batch_sweep, stream, dw))
         result["bucketed_capture"] = _rounded(_leg(bucket_capture, stream, dw))
@@ -953,12 +961,13 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-small", action="store_true")
-    ap.add_argument("--legs", default="headline,small,sweep,dense,cpu",
+    ap.add_argument("--legs", default="headline,small,b1,sweep,dense,cpu",
                     help="comma list of legs to run (profiling runs take one); without 'headline' the line "
                          "carries only the legs run and no value")
     args = ap.parse_args()
     legs = set(args.legs.split(","))
     args.no_small = args.no_small or "small" not in legs
+    args.no_b1 = "b1" not in legs
     args.no_sweep = args.no_sweep or "sweep" not in legs
     args.no_dense = args.no_dense or "dense" not in legs
     args.no_cpu_baseline = args.no_cpu_baseline or "cpu" not in legs
