@@ -41,6 +41,14 @@ constexpr int kMaxParts = 4;
 constexpr int kSplitRows = 256;  // steps of at most this many rows use the split-K projections
 constexpr int kMaxSlices = 8;
 constexpr long kOrderItems = 1024;  // attention work items from which rows go longest first
+// One layer's K/V region from which the attention streams the cache with
+// non-temporal loads (an upper bound on what one launch reads).  Measured on
+// MI355X, one box, both ways: the 70B shape (1.04 GiB per layer) gains with
+// the hint (attention at 256 rows 192.5 -> 180.2 us, the 80-layer step 56.9 ->
+// 56.5 ms); the 0.5B shape (at most 146 MB per layer) loses at every batch
+// (B = 32 step 0.924 -> 0.975 ms, the mix at B = 1 0.816 -> 0.955 ms,
+// B = 256 2.363 -> 2.443 ms).
+constexpr size_t kKvStreamBytes = 512ul << 20;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int elem_size(int32_t dtype) { return dtype == NS_BF16 ? 2 : 4; }
@@ -360,6 +368,7 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
                  &a->n_parts, &a->waves);
   a->wg_cap = e->sched.attn_wg_cap;
   a->row_seq = e->sched.prefill_tiles ? e->m_seq() : nullptr;
+  a->kv_nt = e->kv_layer >= kKvStreamBytes;
   // Longest rows first once the work items outnumber what the chip holds at
   // once (the dispatch then hands the short ones to the CUs that free up
   // first: 256 rows of the 70B shape with contexts 512..1536, 202 -> 192 us
@@ -1017,6 +1026,7 @@ int op_attention(const ns_model_desc* desc, int32_t n_rows, const void* q_att, c
   a.q_att = q_att;
   a.kc = kv_layer;
   a.vc = (const char*)kv_layer + ns::kv_layer_bytes(desc, num_blocks) / 2;
+  a.kv_nt = ns::kv_layer_bytes(desc, num_blocks) >= kKvStreamBytes;
   a.row_bseq = row_bseq;
   a.row_pos = row_pos;
   a.btab = btab;

@@ -343,10 +343,17 @@ struct MfmaPass {
   u32x4_t v[D / 16][2];
 };
 
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 // Issue every K and V load of the pass (tokens past the context end are
-// masked by the math).  Each cached K/V byte is read once per step, so the
-// loads are non-temporal: measured on MI355X, random 4 KB reads stream at
-// 6.8-6.9 TB/s with the hint and 6.1-6.2 TB/s without.
+// masked by the math).  NT: non-temporal loads, for launches that stream
+// hundreds of MB (each K/V byte is read once per step; measured on MI355X,
+// random 4 KB reads stream at 6.8-6.9 TB/s with the hint and 6.1-6.2 TB/s
+// without).  Smaller launches, latency-bound, run faster with ordinary loads.
 // Block ids of the pass's 4 blocks, wave-uniform scalars (never an indexed
 // array: a lane-dependent pick between two entries of one made the compiler
 // keep the array in LDS, a store and a load between the block ids and every
@@ -365,7 +372,7 @@ __device__ __forceinline__ Blk4 pass_blocks(const int32_t* __restrict__ bt, int 
   return r;
 }
 
-template <int D>
+template <int D, bool NT>
 __device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restrict__ kc,
                                            const bf16_t* __restrict__ vc, const Blk4& blk, int g, int nkv, int hc,
                                            int grp) {
@@ -383,7 +390,7 @@ __device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restr
       const int slot = 8 * ((hc >> 2) & 1) + 4 * u + (hc & 3);
 #pragma unroll
       for (int j = 0; j < D / 32; ++j)
-        r.k[s][u][j] = __builtin_nontemporal_load((const bf16x8_t*)(kb + ((long)(4 * j + grp) * 16 + slot) * 8));
+        r.k[s][u][j] = ld<NT>((const bf16x8_t*)(kb + ((long)(4 * j + grp) * 16 + slot) * 8));
     }
   }
   // PV step s, d tile dt, A row hc: V^T row 16 dt + hc, tokens
@@ -394,7 +401,7 @@ __device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restr
     const bf16_t* vb = vc + ((long)b * nkv + g) * HEAD_BLK + 8 * (grp & 1);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      r.v[dt][s] = __builtin_nontemporal_load((const u32x4_t*)(vb + (long)(16 * dt + hc) * 16));
+      r.v[dt][s] = ld<NT>((const u32x4_t*)(vb + (long)(16 * dt + hc) * 16));
   }
 }
 
@@ -562,7 +569,7 @@ __device__ __forceinline__ void patch_own_token(MfmaPass<D>& r, int o, int hc, i
 // Lane l of a wavefront: head column hc = l % 16 (heads >= G are zero
 // padding whose results are dropped), lane group grp = l / 16.  Arguments as
 // attn_decode_kernel.
-template <int D, int G, int NWAVE, bool ROPE>
+template <int D, int G, int NWAVE, bool ROPE, bool KNT>
 __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
     const bf16_t* __restrict__ qatt, const bf16_t* kc, const bf16_t* vc,
     const int32_t* __restrict__ row_bseq, const int32_t* __restrict__ row_pos, const int32_t* __restrict__ btab,
@@ -655,7 +662,7 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
     cur.b[3] = cf + 48 < end ? f3 : f0;
     for (int c0 = cf; c0 < end; c0 += 64 * NWAVE) {
       MfmaPass<D> pr;
-      mfma_issue<D>(pr, kc, vc, cur, g, nkv, hc, grp);
+      mfma_issue<D, KNT>(pr, kc, vc, cur, g, nkv, hc, grp);
       // the next pass's block ids load while this pass's K/V are in flight
       const int cn = c0 + 64 * NWAVE;
       if (cn < end) cur = pass_blocks(bt, cn, end);
@@ -737,6 +744,31 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
   }
 }
 
+// The bf16 matrix-core kernel in its launch shape: 8 or 4 wavefronts per
+// item with the fused RoPE prologue, else 1, 4 or 8.
+template <int D, int G, bool KNT>
+static void launch_mfma(const AttnArgs& a, long grid, float scale_log2, hipStream_t st) {
+  const RopeIn ra{a.rope_qkv, a.rope_slice_stride, a.rope_splits, a.cosb, a.sinb, a.slot};
+#define NS_MFMA_ARGS                                                                                           \
+  (const bf16_t*)a.q_att, (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.row_bseq, a.row_pos, a.btab,             \
+      (bf16_t*)a.out, a.part_acc, a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts,  \
+      scale_log2, a.row_seq, ra, a.row_order
+  const dim3 g((unsigned)grid);
+  if (a.rope_qkv) {  // the fused prologue runs on 8 or 4 wavefronts per item
+    if (a.waves == 8)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, true, KNT>), g, dim3(512), 0, st, NS_MFMA_ARGS);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, true, KNT>), g, dim3(256), 0, st, NS_MFMA_ARGS);
+  } else if (a.waves == 1) {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1, false, KNT>), g, dim3(64), 0, st, NS_MFMA_ARGS);
+  } else if (a.waves == 8) {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, false, KNT>), g, dim3(512), 0, st, NS_MFMA_ARGS);
+  } else {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, false, KNT>), g, dim3(256), 0, st, NS_MFMA_ARGS);
+  }
+#undef NS_MFMA_ARGS
+}
+
 template <typename T, int D, int G>
 static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
   AttnArgs a = a0;
@@ -751,25 +783,10 @@ static void launch_attn_t(const AttnArgs& a0, hipStream_t st) {
   (const T*)a.q_att, (const T*)a.kc, (const T*)a.vc, a.row_bseq, a.row_pos, a.btab, (T*)a.out, a.part_acc,       \
       a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts, scale_log2, a.row_seq
   if constexpr (std::is_same<T, bf16_t>::value) {
-    const RopeIn ra{a.rope_qkv, a.rope_slice_stride, a.rope_splits, a.cosb, a.sinb, a.slot};
-    if (a.rope_qkv) {  // the fused prologue runs on 8 or 4 wavefronts per item
-      if (a.waves == 8)
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, true>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra,
-                           a.row_order);
-      else
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, true>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra,
-                           a.row_order);
-    } else {
-      if (a.waves == 1)
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 1, false>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS, ra,
-                           a.row_order);
-      else if (a.waves == 8)
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 8, false>), dim3((unsigned)grid), dim3(512), 0, st, NS_ATTN_ARGS, ra,
-                           a.row_order);
-      else
-        hipLaunchKernelGGL((attn_mfma_kernel<D, G, 4, false>), dim3((unsigned)grid), dim3(256), 0, st, NS_ATTN_ARGS, ra,
-                           a.row_order);
-    }
+    if (a.kv_nt)
+      launch_mfma<D, G, true>(a, grid, scale_log2, st);
+    else
+      launch_mfma<D, G, false>(a, grid, scale_log2, st);
   } else {
     if (a.waves == 1)
       hipLaunchKernelGGL((attn_decode_kernel<T, D, G, 1>), dim3((unsigned)grid), dim3(64), 0, st, NS_ATTN_ARGS);

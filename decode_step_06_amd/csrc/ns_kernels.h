@@ -104,6 +104,9 @@ struct AttnArgs {
   // n_rows) a permutation of those row indices (null: index order).  Rows are
   // independent, so the order changes no result.
   const int32_t* row_order = nullptr;
+  // bf16 matrix-core kernel: K/V loads non-temporal (for launches that
+  // stream hundreds of MB; see the kernel)
+  bool kv_nt = false;
 };
 int attention_supported(int dtype, int d, int G);
 // Rows are taken in tiles of 32 from row0; a tile of one sequence at
