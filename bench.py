@@ -698,7 +698,7 @@ def sample_clock(enqueue, stream, seconds=0.8):
     if not vals:
         return None
     return {"mhz_median": float(np.median(vals)), "mhz_min": float(min(vals)), "mhz_max": float(max(vals)),
-            "samples": len(vals), "source": "amd-smi gpu metrics (shader clock), during graph replays"}
+            "samples": len(vals), "source": "amd-smi gpu metrics (shader clock), while the timed launches run"}
 
 
 # ---------------------------------------------------------------- the headline: 80-layer 70B step
@@ -930,6 +930,25 @@ def _leg(fn, *a, **kw):
         return {"error": repr(e)}
 
 
+def dense_rooflines(d):
+    """The 2048-row layer's attention (HBM) and projections (MFMA) as roofline
+    entries of their own, from the dense leg's isolated launches."""
+    if not isinstance(d, dict) or "attention" not in d or "gemm" not in d:
+        return {}
+    a, g = d["attention"], d["gemm"]
+    return {"dense_attention_roofline": {
+                "workload": "llama70b_layer_t2048: 512 decode rows at context 1024", "bound": "hbm",
+                "achieved": a["gbs"], "peak": rf.HBM_PEAK_GBS, "unit": "GB/s", "frac": a["hbm_frac"],
+                "traffic": recorded_traffic("attention_llama70b_b512_ctx1024"), "bytes_per_launch": a["bytes"],
+                "avg_launch_us": a["us"]},
+            "dense_gemm_roofline": {
+                "workload": "llama70b_layer_t2048: QKV, O, gate-up and down projections at 2048 rows", "bound": "mfma",
+                "achieved": d["gemm_tflops"], "peak": rf.BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": d["gemm_mfma_frac"], "gate_up_traffic": recorded_traffic("gemm_gate_up_llama70b_t2048"),
+                "per_projection_us": {k: v["us"] for k, v in g.items()},
+                "clock_during_gate_up_gemm": d.get("clock_during_gate_up_gemm")}}
+
+
 def _small_legs(args, stream, result):
     """The 0.5B-shaped step at 32 rows (then at 1 row with the 'b1' leg), and
     the batch sweep and bucketed capture over its weights."""
@@ -993,6 +1012,7 @@ def main():
         _small_legs(args, stream, result)
         if not args.no_dense:
             result["dense_batch"] = _rounded(_leg(dense_batch, stream))
+        result.update(dense_rooflines(result["dense_batch"]))
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = _rounded(cpu_baseline(args.cpu_baseline_full))
         print(json.dumps(result, default=_jsonable), flush=True)
@@ -1064,6 +1084,7 @@ def main():
     _small_legs(args, stream, result)
     if not args.no_dense:
         result["dense_batch"] = _rounded(_leg(dense_batch, stream))
+        result.update(dense_rooflines(result["dense_batch"]))
     result["torch_copy_rate"] = _rounded(copy_ceiling(stream))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _rounded(cpu_baseline(args.cpu_baseline_full))

@@ -1,6 +1,7 @@
 """Host logic of the benchmark that runs without a GPU: the sizing of the
 co-run interference profile (how many attention launches keep the second
-stream busy as long as the projections keep the first) and its caps."""
+stream busy as long as the projections keep the first) and its caps, and the
+dense-batch roofline entries built from the dense leg's results."""
 import pytest
 
 import bench
@@ -19,3 +20,15 @@ def test_corun_caps_cover_shares_of_the_chip():
     caps = bench.CORUN_CAPS
     assert caps[0] == 16 and caps[-1] == 256 and len(caps) == 16
     assert all(b - a == 16 for a, b in zip(caps, caps[1:]))
+
+
+def test_dense_rooflines_from_the_dense_leg():
+    d = {"attention": {"us": 340.0, "gbs": 6300.0, "hbm_frac": 0.7875, "bytes": 2164260864},
+         "gemm": {"qkv_proj": {"us": 386.0}, "o_proj": {"us": 263.0}}, "gemm_tflops": 1070.0,
+         "gemm_mfma_frac": 0.428, "clock_during_gate_up_gemm": {"mhz_median": 1400.0}}
+    r = bench.dense_rooflines(d)
+    a, g = r["dense_attention_roofline"], r["dense_gemm_roofline"]
+    assert (a["bound"], a["unit"], a["frac"], a["achieved"]) == ("hbm", "GB/s", 0.7875, 6300.0)
+    assert (g["bound"], g["unit"], g["frac"], g["peak"]) == ("mfma", "TFLOP/s", 0.428, 2500.0)
+    assert g["per_projection_us"] == {"qkv_proj": 386.0, "o_proj": 263.0}
+    assert bench.dense_rooflines({"error": "x"}) == {}

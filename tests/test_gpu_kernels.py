@@ -230,6 +230,27 @@ def test_attention_workgroup_cap_is_bit_exact():
     np.testing.assert_array_equal(a, b)
 
 
+def test_attention_kv_load_policy_is_bit_exact():
+    """A layer region of 512 MiB or more takes the cache with non-temporal
+    loads, a smaller one with ordinary loads: the same cache placed in both
+    gives the same bits."""
+    shape = ATTN_SHAPES[1]
+    ctx = [1, 16, 17, 200, 1024, 777, 64, 65, 1500, 3]
+    st = _attn_setup(shape, ctx, seed=6)
+    small = _attn_run(shape, st, ctx)
+    per_block = ns.ns_kv_bytes(st["desc"], 1) // shape.n_layers  # K + V bytes of one block
+    nb_big = -(-(512 << 20) // per_block)
+    assert nb_big > st["nb"] and nb_big * per_block >= 512 << 20 > st["nb"] * per_block
+    half, half_big = st["nb"] * per_block // 2, nb_big * per_block // 2
+    big = torch.zeros(nb_big * per_block, dtype=torch.uint8, device="cuda")
+    big[:half] = st["kv"][:half]                       # K blocks
+    big[half_big:half_big + half] = st["kv"][half:]    # V blocks
+    say(f"attention load policy: {st['nb']} blocks ({st['nb'] * per_block >> 20} MiB) vs {nb_big} blocks")
+    large = _attn_run(shape, dict(st, kv=big, nb=nb_big), ctx)
+    assert np.isfinite(small).all()
+    np.testing.assert_array_equal(small, large)
+
+
 # Launch shapes the engine picks from the batch: 8 wavefronts per work item
 # for few items, 4 up to 4095 items, 1 from 4096, and a split context with
 # the combine launch for a long context at a small batch.
