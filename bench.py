@@ -1012,7 +1012,7 @@ def main():
         _small_legs(args, stream, result)
         if not args.no_dense:
             result["dense_batch"] = _rounded(_leg(dense_batch, stream))
-        result.update(dense_rooflines(result["dense_batch"]))
+            result.update(dense_rooflines(result["dense_batch"]))
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = _rounded(cpu_baseline(args.cpu_baseline_full))
         print(json.dumps(result, default=_jsonable), flush=True)
