@@ -731,27 +731,27 @@ int ns_engine_create(const ns_model_desc* desc, const ns_weights* w, ns_kv* kv, 
 void ns_engine_destroy(ns_engine* e) {
   if (!e) return;
   if (e->s2) {
-    hipStreamSynchronize(e->s2);
-    hipStreamDestroy(e->s2);
+    (void)hipStreamSynchronize(e->s2);
+    (void)hipStreamDestroy(e->s2);
   }
   for (int i = 0; i < kMaxParts; ++i) {
-    if (e->ev_qkv[i]) hipEventDestroy(e->ev_qkv[i]);
-    if (e->ev_att[i]) hipEventDestroy(e->ev_att[i]);
+    if (e->ev_qkv[i]) (void)hipEventDestroy(e->ev_qkv[i]);
+    if (e->ev_att[i]) (void)hipEventDestroy(e->ev_att[i]);
   }
-  if (e->ev_join) hipEventDestroy(e->ev_join);
+  if (e->ev_join) (void)hipEventDestroy(e->ev_join);
   if (e->bad_tok_ev) {
-    hipEventSynchronize(e->bad_tok_ev);
-    hipEventDestroy(e->bad_tok_ev);
+    (void)hipEventSynchronize(e->bad_tok_ev);
+    (void)hipEventDestroy(e->bad_tok_ev);
   }
-  if (e->bad_tok_host) hipHostFree(e->bad_tok_host);
-  for (hipEvent_t ev : e->prof_ev) hipEventDestroy(ev);
-  if (e->prof_start) hipEventDestroy(e->prof_start);
+  if (e->bad_tok_host) (void)hipHostFree(e->bad_tok_host);
+  for (hipEvent_t ev : e->prof_ev) (void)hipEventDestroy(ev);
+  if (e->prof_start) (void)hipEventDestroy(e->prof_start);
   for (int k = 0; k < 2; ++k) {
     if (e->staging_ev[k]) {
-      hipEventSynchronize(e->staging_ev[k]);
-      hipEventDestroy(e->staging_ev[k]);
+      (void)hipEventSynchronize(e->staging_ev[k]);
+      (void)hipEventDestroy(e->staging_ev[k]);
     }
-    if (e->staging[k]) hipHostFree(e->staging[k]);
+    if (e->staging[k]) (void)hipHostFree(e->staging[k]);
   }
   delete e;
 }
@@ -800,19 +800,19 @@ int ns_graph_capture(ns_engine* e, int32_t bucket, void* out, void* stream, ns_g
   if (rc != NS_OK && e->sched.overlap) {
     // a step that failed after forking to the second stream: join that
     // stream back into the capture so that the capture can end
-    hipEventRecord(e->ev_join, e->s2);
-    hipStreamWaitEvent(st, e->ev_join, 0);
+    (void)hipEventRecord(e->ev_join, e->s2);
+    (void)hipStreamWaitEvent(st, e->ev_join, 0);
   }
   he = hipStreamEndCapture(st, &g->graph);
   if (rc != NS_OK || he != hipSuccess) {
-    if (g->graph) hipGraphDestroy(g->graph);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
     delete g;
     if (rc != NS_OK) return rc;
     NS_FAIL(NS_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(he));
   }
   he = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
   if (he != hipSuccess) {
-    hipGraphDestroy(g->graph);
+    (void)hipGraphDestroy(g->graph);
     delete g;
     NS_FAIL(NS_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(he));
   }
@@ -885,8 +885,8 @@ int ns_sample_greedy(const float* logits, int32_t n_rows, int32_t vocab, int32_t
 
 void ns_graph_destroy(ns_graph* g) {
   if (!g) return;
-  if (g->exec) hipGraphExecDestroy(g->exec);
-  if (g->graph) hipGraphDestroy(g->graph);
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
   delete g;
 }
 
