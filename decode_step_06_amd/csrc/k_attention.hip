@@ -343,17 +343,13 @@ struct MfmaPass {
   u32x4_t v[D / 16][2];
 };
 
+// A 16-byte load, non-temporal when NT.
 template <bool NT, typename V>
 __device__ __forceinline__ V ld(const V* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
 
-// Issue every K and V load of the pass (tokens past the context end are
-// masked by the math).  NT: non-temporal loads, for launches that stream
-// hundreds of MB (each K/V byte is read once per step; measured on MI355X,
-// random 4 KB reads stream at 6.8-6.9 TB/s with the hint and 6.1-6.2 TB/s
-// without).  Smaller launches, latency-bound, run faster with ordinary loads.
 // Block ids of the pass's 4 blocks, wave-uniform scalars (never an indexed
 // array: a lane-dependent pick between two entries of one made the compiler
 // keep the array in LDS, a store and a load between the block ids and every
@@ -372,6 +368,11 @@ __device__ __forceinline__ Blk4 pass_blocks(const int32_t* __restrict__ bt, int 
   return r;
 }
 
+// Issue every K and V load of the pass (tokens past the context end are
+// masked by the math).  NT: non-temporal loads, for launches that stream
+// hundreds of MB (each K/V byte is read once per step; measured on MI355X,
+// random 4 KB reads stream at 6.8-6.9 TB/s with the hint and 6.1-6.2 TB/s
+// without).  Smaller launches, latency-bound, run faster with ordinary loads.
 template <int D, bool NT>
 __device__ __forceinline__ void mfma_issue(MfmaPass<D>& r, const bf16_t* __restrict__ kc,
                                            const bf16_t* __restrict__ vc, const Blk4& blk, int g, int nkv, int hc,
