@@ -254,29 +254,36 @@ constexpr unsigned BUF_RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit dwords, n
 
 // BNT: the B operand streams with non-temporal loads (set when one row tile
 // covers all M rows, so that each B slab is read by one workgroup only).
-template <int EPI, typename OutT, int BM = 256, int BNT = 0>
-__global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
-                                                       const bf16_t* __restrict__ B, int ldb, int M, int N, int K,
-                                                       void* __restrict__ Cv, int ldc, int splits, long slice_stride,
-                                                       int bpk) {
+// NWV: 4 wavefronts (one per SIMD, 128 x 128 outputs each) or 8 (two per
+// SIMD, 128 x 64 each); PP (8 only): the two groups of 4 alternate between
+// MFMAs and memory work (see the main loop).  Every variant accumulates each
+// output over the same k-steps in the same order: the same bits.
+template <int EPI, typename OutT, int BM = 256, int BNT = 0, int NWV = 4, int PP = 0>
+__global__ void __launch_bounds__(64 * NWV) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
+                                                            const bf16_t* __restrict__ B, int ldb, int M, int N,
+                                                            int K, void* __restrict__ Cv, int ldc, int splits,
+                                                            long slice_stride, int bpk) {
   static_assert(BM == 256 || BM == 128, "tile rows");
+  static_assert(NWV == 4 || (NWV == 8 && BM == 256), "wavefronts");
+  static_assert(PP == 0 || NWV == 8, "ping-pong takes two wavefronts per SIMD");
   constexpr int BN = 256, BK = 32, NSTAGE = 4;
-  constexpr int TM = BM / 2, TN = 128, FM = TM / 32, FN = 4;  // 32 x 32 fragments
+  // wavefronts in 2 rows of NWV / 2; each owns TM x TN outputs
+  constexpr int TM = BM / 2, TN = 2 * BN / NWV, FM = TM / 32, FN = TN / 32;  // 32 x 32 fragments
   constexpr int ROWB = BK * 2;                  // bytes per LDS row
   constexpr int STAGE = (BM + BN) * ROWB;       // bytes per slab buffer (A rows, then B rows)
   constexpr int AG = BM / 16;                   // 16-row load groups of A (then BN / 16 of B)
-  constexpr int LOADS = (BM + BN) / 16 / 4;     // load instructions per wavefront per slab (8 or 6)
+  constexpr int LOADS = (BM + BN) / 16 / NWV;   // load instructions per wavefront per slab (8, 6 or 4)
   constexpr int NMF = 2 * FM * FN;              // MFMAs per wavefront per slab (32 or 16)
   constexpr int NREAD = 2 * (FM + FN);          // fragment reads per wavefront per slab (16 or 12)
   constexpr int PRE = NMF / 4;                  // MFMAs of a slab before its barrier
-  constexpr int LPRE = BM == 256 ? LOADS / 2 : LOADS;  // loads issued before the barrier
+  constexpr int LPRE = (BM == 256 && NWV == 4) ? LOADS / 2 : LOADS;  // loads issued before the barrier
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? BN / 2 : BN;
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];  // 128 or 96 KB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NWV / 2), wn = wave % (NWV / 2);
   const int m_tiles = (M + BM - 1) / BM;
   const int n_tiles = (N + OUT_BN - 1) / OUT_BN;
   const int tiles = m_tiles * n_tiles;
@@ -296,11 +303,11 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
   // are never stored).
   // (sized for the largest tile: a value-dependent array size captured by
   // the nested lambdas below stops the host pass from emitting the kernel)
-  static_assert(LOADS <= 8, "load slots");
+  static_assert(LOADS <= 8 && AG % NWV == 0, "load slots");
   unsigned voff[8];
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
-    const int g = wave + 4 * j;
+    const int g = wave + NWV * j;
     const int r = (g < AG ? g : g - AG) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz(r);
     if (g < AG) {
@@ -332,12 +339,11 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
     // packed B: slab ks is a contiguous [rows][32] block
     const unsigned soff_b = bpk ? (unsigned)ks * (unsigned)ldb * (BK * 2) : soff;
     char* base = lds + (kt % NSTAGE) * STAGE;
-    // load slots j < AG / 4 carry A rows, the rest B rows (wave < 4)
-    static_assert(AG % 4 == 0, "A load slots");
+    // load slots j < AG / NWV carry A rows, the rest B rows (wave < NWV)
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
-      const int g = wave + 4 * j;
-      if (j < AG / 4)
+      const int g = wave + NWV * j;
+      if (j < AG / NWV)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j], soff, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j], soff_b, 0,
@@ -446,15 +452,42 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const bf16_t* __restrict_
   for (int p = 0; p < NSTAGE - 1; ++p) issue(p, 0, LOADS);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LOADS, 0));  // slab 0 landed
   barrier();
-  read_frags(0, 0);
-  // Two slabs per trip so the register sets are compile-time constants.
-  // Past the last slab, read_frags reads a buffer whose fragments go unused.
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    slab(kt, 0);
-    slab(kt + 1, 1);
+  if constexpr (PP) {
+    // Ping-pong: wavefronts 0..3 and 4..7 (one of each per SIMD) run one
+    // barrier interval apart.  In each interval one group issues its MFMAs on
+    // the slab whose fragments it read in the previous interval, while the
+    // other reads its fragments of a slab and issues its loads of the slab
+    // three ahead.  Before every barrier a wavefront waits until its loads
+    // of all but the two newest slabs have landed and its LDS reads are done:
+    // a slab's loads then land before any group reads it, and a buffer is
+    // refilled only after both groups read it.
+    const bool late = wave >= NWV / 2;
+    auto sync = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LOADS, 0));
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (late) sync();
+    for (int kt = 0; kt < nk; ++kt) {
+      read_frags(kt, 0);
+      issue(kt + 3, 0, LOADS);
+      sync();
+      mfmas(0, 0, NMF);
+      sync();
+    }
+    if (!late) sync();
+  } else {
+    read_frags(0, 0);
+    // Two slabs per trip so the register sets are compile-time constants.
+    // Past the last slab, read_frags reads a buffer whose fragments go unused.
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      slab(kt, 0);
+      slab(kt + 1, 1);
+    }
+    if (kt < nk) mfmas(0, 0, NMF);  // odd slab count: the last slab is in set 0
   }
-  if (kt < nk) mfmas(0, 0, NMF);  // odd slab count: the last slab is in set 0
   // Drain the trailing loads before the workgroup's LDS is released.
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
@@ -682,12 +715,21 @@ static void run_big(int M, int N, int K, const void* A, int lda, const void* B, 
                     hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
-  if (M <= BM)  // one row tile: each weight slab is read once
-    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 1>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0,
-                       st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
-  else
-    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 0>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0,
-                       st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+  const dim3 grid((unsigned)tiles, (unsigned)splits);
+  if (M <= BM) {  // one row tile: each weight slab is read once
+    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 1>), grid, dim3(256), 0, st, (const bf16_t*)A, lda,
+                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+  } else if constexpr (BM == 256) {
+    // several row tiles: 8 wavefronts in two ping-pong groups (measured on
+    // MI355X at 2048 rows of the 70B shape: QKV 383.6 -> 369.5, O 261 ->
+    // 230.5, gate-up 1693 -> 1665, down 868 -> 847 us, the same bits; at one
+    // row tile of 256 rows the gate-up projection lost 7%)
+    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 0, 8, 1>), grid, dim3(512), 0, st, (const bf16_t*)A, lda,
+                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+  } else {
+    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 0>), grid, dim3(256), 0, st, (const bf16_t*)A, lda,
+                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+  }
 }
 
 template <int MF, int NF, int NW, int EPI>
