@@ -17,9 +17,11 @@ def _bf16_grid(a):
     return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
 
 
+# (2000, 8100, 512): 256 x 256 tiles over 8 row tiles, the ping-pong kernel,
+# with ragged last row and column tiles
 GEMM_SHAPES = [(1, 64, 64), (5, 130, 96), (16, 896, 896), (17, 1152, 896), (32, 300, 128), (33, 256, 4864),
                (64, 64, 256), (100, 520, 160), (130, 384, 512), (257, 640, 1024), (32, 896, 4864),
-               (1, 896, 4864), (32, 4864, 896), (8, 1000, 1024), (192, 1300, 1056)]
+               (1, 896, 4864), (32, 4864, 896), (8, 1000, 1024), (192, 1300, 1056), (2000, 8100, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
