@@ -3,7 +3,8 @@ bucket, a batch replayed on the smallest bucket that holds it with the rest
 as padding rows.  The real rows equal an eager step of the same padded batch
 bit for bit, and the oracle within the bf16 bound; also with RoPE fused into
 attention (padding rows belong to no sequence, so the fused schedule accepts
-them)."""
+them), and with buckets large enough (1024 attention work items and more)
+that the attention takes its rows longest context first, padding last."""
 import numpy as np
 import pytest
 import torch
@@ -20,13 +21,25 @@ pytestmark = pytest.mark.gpu
 
 SMALL = ModelShape("small", 2, 256, 8, 2, 64, 512, 1000, True, "bf16")
 BUCKETS = (1, 2, 4, 8, 16, 24)
+# 8 KV heads: 128 rows make 1024 attention work items
+KV8 = ModelShape("kv8", 1, 512, 8, 8, 64, 512, 1000, True, "bf16")
+KV8_BUCKETS = (64, 128, 192, 200)
 
 
 @pytest.mark.parametrize("fuse", [False, True], ids=["separate-rope", "rope-fused"])
 def test_bucketed_replay_pads_to_the_next_bucket(fuse):
-    shape, S = SMALL, 24
+    _bucketed(SMALL, 24, BUCKETS, (1, 3, 5, 8, 13, 24), 90, fuse)
+
+
+@pytest.mark.parametrize("fuse", [False, True], ids=["separate-rope", "rope-fused"])
+def test_bucketed_replay_rows_longest_context_first(fuse):
+    _bucketed(KV8, 200, KV8_BUCKETS, (50, 100, 150, 200), 300, fuse)
+
+
+def _bucketed(shape, S, buckets, sizes, ctx_hi, fuse):
+    say(f"buckets {shape.name}: {S} sequences, buckets {buckets}, fused RoPE {fuse}")
     rng = np.random.default_rng(3)
-    ctx = rng.integers(1, 90, size=S)
+    ctx = rng.integers(1, ctx_hi, size=S)
     tokens = rng.integers(0, shape.vocab, size=S).astype(np.int32)
     weights = gen_weights(shape, seed=0)
     maxb = blocks_for(ctx)
@@ -46,14 +59,14 @@ def test_bucketed_replay_pads_to_the_next_bucket(fuse):
         alloc_sequences(h, ctx)
         fill_past(h, past_seq, past_pos, past_k, past_v)
         out = torch.full((S, shape.vocab), float("nan"), device="cuda")
-        gs = ns.ns_graph_set_capture(h.eng, BUCKETS, out.data_ptr(), stream)
+        gs = ns.ns_graph_set_capture(h.eng, buckets, out.data_ptr(), stream)
         try:
-            for n in (1, 3, 5, 8, 13, 24):
+            for n in sizes:
                 seq = np.arange(n, dtype=np.int32)
                 pos = (ctx[:n] - 1).astype(np.int32)
                 used = ns.ns_graph_set_replay(gs, ns.Batch(seq, pos, tokens[:n]), stream)
                 stream.synchronize()
-                want_bucket = min(b for b in BUCKETS if b >= n)
+                want_bucket = min(b for b in buckets if b >= n)
                 assert used == want_bucket, (n, used)
                 got = out[:n].cpu().numpy()
                 # the same batch padded by hand, eager
@@ -65,7 +78,7 @@ def test_bucketed_replay_pads_to_the_next_bucket(fuse):
                 ns.ns_decode_step(h.eng, ns.Batch(pseq, ppos, ptok), ref.data_ptr(), stream)
                 stream.synchronize()
                 np.testing.assert_array_equal(got, ref[:n].cpu().numpy(), err_msg=f"n_tok {n} bucket {used}")
-                say(f"  n_tok {n:2d} -> bucket {used:2d}: equal to the eager padded step")
+                say(f"  n_tok {n:3d} -> bucket {used:3d}: equal to the eager padded step")
             # the largest case against the oracle
             ib = InBatch(seq_lens=ctx.astype(np.int32), row_seq=np.arange(S, dtype=np.int32),
                          row_pos=(ctx - 1).astype(np.int32), tokens=tokens, x=None, num_blocks=nblk,
