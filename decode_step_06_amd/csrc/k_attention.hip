@@ -484,22 +484,68 @@ __device__ __forceinline__ void mfma_compute(MfmaPass<D>& r, const bf16x8_t (&qf
 // paged cache at its slot (rows of other sequences never read that slot; this
 // row's own passes take the token from LDS).  Same arithmetic as the separate
 // RoPE / cache-write kernel, so the results are the same bits.
+// The staging of one work item's q heads, k and v: a thread's chunks of
+// every slice are all in flight before the first add (slice order kept).
+template <int D, int G, int NT, int S>
+__device__ __forceinline__ void rope_stage(const float* __restrict__ row, long slice_stride, int g, int nq, int nkv,
+                                           float* rbuf) {
+  constexpr int N4 = (G + 2) * D / 4, CPT = (N4 + NT - 1) / NT;
+  f32x4_t p[CPT][S];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int e = 4 * (threadIdx.x + c * NT);
+    if (e < 4 * N4) {
+      const int src = e < G * D ? g * G * D + e
+                                : (e < (G + 1) * D ? nq * D + g * D + (e - G * D)
+                                                   : (nq + nkv) * D + g * D + (e - (G + 1) * D));
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        p[c][s] = __builtin_nontemporal_load((const f32x4_t*)(row + src + s * slice_stride));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int e = 4 * (threadIdx.x + c * NT);
+    if (e < 4 * N4) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < S; ++s) a += p[c][s];
+      *(f32x4_t*)(rbuf + e) = a;
+    }
+  }
+}
+
 template <int D, int G, int NWAVE>
 __device__ __forceinline__ void rope_prologue(const RopeIn& ra, int t, int g, int nq, int nkv, int ctx, int start,
                                               int end, bf16_t* kcw, bf16_t* vcw, bf16_t* rq, bf16_t* rv) {
-  constexpr int HALF = D / 2, NCH = D / 8;
-  __shared__ __attribute__((aligned(16))) float rbuf[(G + 2) * D];
+  constexpr int HALF = D / 2, NCH = D / 8, NT = 64 * NWAVE;
+  // the item's rows of the projection, then the row's cos and sin
+  __shared__ __attribute__((aligned(16))) float rbuf[(G + 2) * D + D];
+  float* cr = rbuf + (G + 2) * D;
+  float* sr = cr + HALF;
   const int width = (nq + 2 * nkv) * D;
   const float* row = ra.qkv + (long)t * width;
-  for (int i4 = threadIdx.x; i4 < (G + 2) * D / 4; i4 += 64 * NWAVE) {
-    const int e = 4 * i4;
-    const int src = e < G * D ? g * G * D + e
-                              : (e < (G + 1) * D ? nq * D + g * D + (e - G * D) : (nq + nkv) * D + g * D + (e - (G + 1) * D));
-    *(f32x4_t*)(rbuf + e) = slice_sum4(row + src, ra.slice_stride, ra.splits);
+  // the table entries are loaded with the row's slices: one round of loads
+  float cv = 0.f, sv = 0.f;
+  if ((int)threadIdx.x < HALF) {
+    cv = ra.cosb[(long)t * HALF + threadIdx.x];
+    sv = ra.sinb[(long)t * HALF + threadIdx.x];
+  }
+  switch (ra.splits) {  // uniform
+    case 1: rope_stage<D, G, NT, 1>(row, ra.slice_stride, g, nq, nkv, rbuf); break;
+    case 2: rope_stage<D, G, NT, 2>(row, ra.slice_stride, g, nq, nkv, rbuf); break;
+    case 3: rope_stage<D, G, NT, 3>(row, ra.slice_stride, g, nq, nkv, rbuf); break;
+    case 4: rope_stage<D, G, NT, 4>(row, ra.slice_stride, g, nq, nkv, rbuf); break;
+    case 5: rope_stage<D, G, NT, 5>(row, ra.slice_stride, g, nq, nkv, rbuf); break;
+    case 6: rope_stage<D, G, NT, 6>(row, ra.slice_stride, g, nq, nkv, rbuf); break;
+    case 7: rope_stage<D, G, NT, 7>(row, ra.slice_stride, g, nq, nkv, rbuf); break;
+    default: rope_stage<D, G, NT, kMaxSplits>(row, ra.slice_stride, g, nq, nkv, rbuf); break;
+  }
+  if ((int)threadIdx.x < HALF) {
+    cr[threadIdx.x] = cv;
+    sr[threadIdx.x] = sv;
   }
   __syncthreads();
-  const float* cr = ra.cosb + (long)t * HALF;
-  const float* sr = ra.sinb + (long)t * HALF;
   for (int i = threadIdx.x; i < (G + 1) * HALF + D; i += 64 * NWAVE) {
     if (i < (G + 1) * HALF) {
       const int hh = i / HALF, j = i % HALF;

@@ -75,15 +75,96 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
 
 // The split-K residual add fused in front of the norm: x[t] += the slices
 // of the previous projection (slice order), written back, then the norm.
-// 16-byte chunks, CH per thread held in registers between the two passes;
-// all of a chunk's slice loads are in flight together (a chain of
-// dependent loads would cost one memory latency per slice).  NT threads per
-// row: 256 up to 2048 elements, 1024 above (a thread's chunks are rounds of
-// dependent loads, so wide rows take more threads rather than more rounds).
+// 16-byte chunks, CH per thread held in registers between the two passes.
+// Every load of the row -- all S slices of all CH chunks, x and the norm
+// weights -- is issued before the first add, so the row costs one memory
+// round trip before the reduction (a chunk at a time, or the weights loaded
+// after the reduction, would each add one).  NT threads per row: 256 up to
+// 2048 elements, 1024 above.
+template <typename T> struct Gain4;
+template <> struct Gain4<float> {
+  __device__ static __forceinline__ f32x4_t load(const float* p) { return *(const f32x4_t*)p; }
+};
+template <> struct Gain4<bf16_t> {
+  __device__ static __forceinline__ f32x4_t load(const bf16_t* p) {
+    const uint2 w = *(const uint2*)p;
+    return f32x4_t{lo_bf16(w.x), hi_bf16(w.x), lo_bf16(w.y), hi_bf16(w.y)};
+  }
+};
+
+template <typename T, int CH, int NT, int S>
+__device__ __forceinline__ void rmsnorm_reduce_row(float* __restrict__ xr, const float* __restrict__ pr,
+                                                   long slice_stride, const T* __restrict__ g, T* __restrict__ hr,
+                                                   int H, float eps) {
+  const int H4 = H >> 2;
+  f32x4_t p[CH][S], v[CH], gv[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i4 = threadIdx.x + c * NT;
+    if (i4 < H4) {
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        p[c][s] = __builtin_nontemporal_load((const f32x4_t*)(pr + 4 * i4 + s * slice_stride));
+      v[c] = *(const f32x4_t*)(xr + 4 * i4);
+      gv[c] = Gain4<T>::load(g + 4 * i4);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i4 = threadIdx.x + c * NT;
+    if (i4 < H4) {
+      f32x4_t add = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < S; ++s) add += p[c][s];
+      v[c] += add;
+      *(f32x4_t*)(xr + 4 * i4) = v[c];
+      ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+    }
+  }
+  constexpr int NW = NT / 64;
+  __shared__ float red[NW];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) tot += red[i];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i4 = threadIdx.x + c * NT;
+    if (i4 < H4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Elem<T>::store(hr, 4 * i4 + e, v[c][e] * r * gv[c][e]);
+    }
+  }
+}
+
 template <typename T, int CH, int NT>
 __global__ void __launch_bounds__(NT) rmsnorm_reduce_kernel(float* __restrict__ x, const float* __restrict__ P,
                                                             long slice_stride, int splits, const T* __restrict__ g,
                                                             T* __restrict__ h, int H, float eps) {
+  const long o = (long)blockIdx.x * H;
+  switch (splits) {  // uniform: straight-line code for each slice count
+    case 1: return rmsnorm_reduce_row<T, CH, NT, 1>(x + o, P + o, slice_stride, g, h + o, H, eps);
+    case 2: return rmsnorm_reduce_row<T, CH, NT, 2>(x + o, P + o, slice_stride, g, h + o, H, eps);
+    case 3: return rmsnorm_reduce_row<T, CH, NT, 3>(x + o, P + o, slice_stride, g, h + o, H, eps);
+    case 4: return rmsnorm_reduce_row<T, CH, NT, 4>(x + o, P + o, slice_stride, g, h + o, H, eps);
+    case 5: return rmsnorm_reduce_row<T, CH, NT, 5>(x + o, P + o, slice_stride, g, h + o, H, eps);
+    case 6: return rmsnorm_reduce_row<T, CH, NT, 6>(x + o, P + o, slice_stride, g, h + o, H, eps);
+    case 7: return rmsnorm_reduce_row<T, CH, NT, 7>(x + o, P + o, slice_stride, g, h + o, H, eps);
+    default: return rmsnorm_reduce_row<T, CH, NT, kMaxSplits>(x + o, P + o, slice_stride, g, h + o, H, eps);
+  }
+}
+
+// Rows of more than 8192 elements: a chunk's slices at a time (all of a
+// row's would not fit the registers of 1024 threads).
+template <typename T, int CH, int NT>
+__global__ void __launch_bounds__(NT) rmsnorm_reduce_wide_kernel(float* __restrict__ x, const float* __restrict__ P,
+                                                                 long slice_stride, int splits,
+                                                                 const T* __restrict__ g, T* __restrict__ h, int H,
+                                                                 float eps) {
   const int t = blockIdx.x, H4 = H >> 2;
   float* xr = x + (long)t * H;
   const float* pr = P + (long)t * H;
@@ -314,10 +395,57 @@ __device__ __forceinline__ long v_index(long blk, int g, int tok, int j, int nkv
 // rows, slot < 0, write no K/V).
 //
 // The row is first staged in LDS -- summed in slice order when the projection
-// arrives as split-K slices, every slice's load of a chunk in flight at once.
+// arrives as split-K slices -- together with its cos/sin, in one round of
+// loads: a thread's CPT chunks of every slice are all in flight before the
+// first add (CPT = 0: rows too wide for that, a chunk's slices at a time).
 // Then each thread produces whole 16-byte chunks: E consecutive elements j of
 // one head and, for q and k, their rotation partners j + d/2.
-template <typename T, int NT>
+template <int S, int CPT, int NT>
+__device__ __forceinline__ void stage_slices(const float* __restrict__ row, long slice_stride, float* rowbuf,
+                                             int n4) {
+  f32x4_t p[CPT][S];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int i4 = threadIdx.x + c * NT;
+    if (i4 < n4) {
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        p[c][s] = __builtin_nontemporal_load((const f32x4_t*)(row + 4 * i4 + s * slice_stride));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int i4 = threadIdx.x + c * NT;
+    if (i4 < n4) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < S; ++s) a += p[c][s];
+      *(f32x4_t*)(rowbuf + 4 * i4) = a;
+    }
+  }
+}
+
+template <int CPT, int NT>
+__device__ __forceinline__ void stage_row(const float* __restrict__ row, long slice_stride, int splits, float* rowbuf,
+                                          int n4) {
+  if constexpr (CPT == 0) {
+    for (int i4 = threadIdx.x; i4 < n4; i4 += NT)
+      *(f32x4_t*)(rowbuf + 4 * i4) = slice_sum4(row + 4 * i4, slice_stride, splits);
+  } else {
+    switch (splits) {  // uniform
+      case 1: return stage_slices<1, CPT, NT>(row, slice_stride, rowbuf, n4);
+      case 2: return stage_slices<2, CPT, NT>(row, slice_stride, rowbuf, n4);
+      case 3: return stage_slices<3, CPT, NT>(row, slice_stride, rowbuf, n4);
+      case 4: return stage_slices<4, CPT, NT>(row, slice_stride, rowbuf, n4);
+      case 5: return stage_slices<5, CPT, NT>(row, slice_stride, rowbuf, n4);
+      case 6: return stage_slices<6, CPT, NT>(row, slice_stride, rowbuf, n4);
+      case 7: return stage_slices<7, CPT, NT>(row, slice_stride, rowbuf, n4);
+      default: return stage_slices<kMaxSplits, CPT, NT>(row, slice_stride, rowbuf, n4);
+    }
+  }
+}
+
+template <typename T, int NT, int CPT>
 __global__ void __launch_bounds__(NT) rope_kv_kernel(const float* __restrict__ qkv, long slice_stride, int splits,
                                                       const float* __restrict__ cosb,
                                                       const float* __restrict__ sinb, const int32_t* __restrict__ slot,
@@ -329,12 +457,22 @@ __global__ void __launch_bounds__(NT) rope_kv_kernel(const float* __restrict__ q
   const int half = d >> 1, G = nq / nkv, nch = d / E, hch = half / E;
   const int width = (nq + 2 * nkv) * d;
   const float* row = qkv + (long)t * width;
-  for (int i4 = threadIdx.x; i4 < (width >> 2); i4 += NT)
-    *(f32x4_t*)(rowbuf + 4 * i4) = slice_sum4(row + 4 * i4, slice_stride, splits);
-  __syncthreads();
-  const float* cr = cosb + (long)t * half;
-  const float* sr = sinb + (long)t * half;
   const int s = slot[t];
+  // the row's cos/sin after the row in LDS (half / 4 chunks each)
+  float* cr = rowbuf + width;
+  float* sr = cr + half;
+  f32x4_t cv, sv;
+  const bool trig = (int)threadIdx.x < (half >> 2);
+  if (trig) {
+    cv = *(const f32x4_t*)(cosb + (long)t * half + 4 * threadIdx.x);
+    sv = *(const f32x4_t*)(sinb + (long)t * half + 4 * threadIdx.x);
+  }
+  stage_row<CPT, NT>(row, slice_stride, splits, rowbuf, width >> 2);
+  if (trig) {
+    *(f32x4_t*)(cr + 4 * threadIdx.x) = cv;
+    *(f32x4_t*)(sr + 4 * threadIdx.x) = sv;
+  }
+  __syncthreads();
   const long blk = s >= 0 ? (long)(s / NS_BLOCK) : 0;
   const int tok = s >= 0 ? s % NS_BLOCK : 0;
   const int n_q = nq * hch, n_k = s >= 0 ? nkv * hch : 0, n_v = s >= 0 ? nkv * nch : 0;
@@ -467,30 +605,45 @@ void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, 
                     const float* sinb, const int32_t* slot, void* q_att, void* kc, void* vc, int T, int nq, int nkv,
                     int d, hipStream_t st) {
   if (T <= 0) return;
-  // rows wider than 2048 floats take 1024 threads: each thread's 16-byte
-  // chunks are rounds of dependent slice loads
-  const size_t lds = (size_t)(nq + 2 * nkv) * d * sizeof(float);
-  const bool wide = (nq + 2 * nkv) * d > 2048;
+  // rows wider than 2048 floats take 1024 threads; a thread's chunks of
+  // every slice are loaded in one round where they fit its registers
+  const int width = (nq + 2 * nkv) * d;
+  const size_t lds = (size_t)(width + d) * sizeof(float);  // the row, then its cos and sin
+  const int nt = width > 2048 ? 1024 : 256;
+  const int cpt = (width / 4 + nt - 1) / nt;
+#define NS_ROPE_KV(TT, NT, CPT)                                                                                  \
+  hipLaunchKernelGGL((rope_kv_kernel<TT, NT, CPT>), dim3(T), dim3(NT), lds, st, qkv, slice_stride, splits, cosb, \
+                     sinb, slot, (TT*)q_att, (TT*)kc, (TT*)vc, nq, nkv, d)
   if (dtype == NS_DT_BF16) {
-    if (wide)
-      hipLaunchKernelGGL((rope_kv_kernel<bf16_t, 1024>), dim3(T), dim3(1024), lds, st, qkv, slice_stride, splits, cosb,
-                         sinb, slot, (bf16_t*)q_att, (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
-    else
-      hipLaunchKernelGGL((rope_kv_kernel<bf16_t, 256>), dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb,
-                         sinb, slot, (bf16_t*)q_att, (bf16_t*)kc, (bf16_t*)vc, nq, nkv, d);
+    if (nt == 1024) {
+      if (cpt == 1) NS_ROPE_KV(bf16_t, 1024, 1);
+      else if (cpt == 2) NS_ROPE_KV(bf16_t, 1024, 2);
+      else if (cpt == 3) NS_ROPE_KV(bf16_t, 1024, 3);
+      else NS_ROPE_KV(bf16_t, 1024, 0);
+    } else {
+      if (cpt == 1) NS_ROPE_KV(bf16_t, 256, 1);
+      else NS_ROPE_KV(bf16_t, 256, 2);
+    }
   } else {
-    hipLaunchKernelGGL((rope_kv_kernel<float, 256>), dim3(T), dim3(256), lds, st, qkv, slice_stride, splits, cosb,
-                       sinb, slot, (float*)q_att, (float*)kc, (float*)vc, nq, nkv, d);
+    if (cpt == 1) NS_ROPE_KV(float, 256, 1);
+    else NS_ROPE_KV(float, 256, 2);
   }
+#undef NS_ROPE_KV
 }
 
 template <typename T>
 static void run_rmsnorm_reduce(float* x, const float* P, long slice_stride, int splits, const T* g, T* h, int T_,
                                int H, float eps, hipStream_t st) {
   const int ch = (H / 4 + 255) / 256;
+  // the one-round kernel reads the gains 4 at a time and holds a row's
+  // slices in registers: rows of up to 8192 elements
+  const bool aligned = ((uintptr_t)g % (4 * sizeof(T))) == 0;
   if (H % 4 != 0 || ch > 32)
     hipLaunchKernelGGL(rmsnorm_reduce_any_kernel<T>, dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
                        H, eps);
+  else if (ch > 8 || !aligned)
+    hipLaunchKernelGGL((rmsnorm_reduce_wide_kernel<T, 8, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride,
+                       splits, g, h, H, eps);
   else if (ch == 1)
     hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 1, 256>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g,
                        h, H, eps);
@@ -500,11 +653,8 @@ static void run_rmsnorm_reduce(float* x, const float* P, long slice_stride, int 
   else if (ch <= 4)
     hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 1, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
                        g, h, H, eps);
-  else if (ch <= 8)
-    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 2, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
-                       g, h, H, eps);
   else
-    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 8, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
+    hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 2, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
                        g, h, H, eps);
 }
 
