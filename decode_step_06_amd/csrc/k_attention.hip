@@ -644,6 +644,7 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
     }
     const int32_t* __restrict__ bt;
     bool pad;
+    const int pos_t = row_pos[t];  // loaded with the row's sequence: one round
     if (row_bseq) {
       const int bs = row_bseq[t];
       pad = bs < 0;
@@ -667,7 +668,7 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
         for (int i = threadIdx.x; i < G * D; i += 64 * NWAVE) outp[i] = 0;
       continue;
     }
-    const int ctx = row_pos[t] + 1;
+    const int ctx = pos_t + 1;
     const int start = part * P;
     if (start >= ctx) continue;
     const int end = min(start + P, ctx);

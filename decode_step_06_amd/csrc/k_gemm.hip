@@ -614,16 +614,15 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
   };
   int s = s0;
   for (; s + U <= s1; s += U) round(std::integral_constant<int, U>{}, s);
+#define NS_GEMV_TAIL(R) \
+  case R: if constexpr (U > R) round(std::integral_constant<int, (U > R ? R : 1)>{}, s); break;
   switch (s1 - s) {  // 0 .. U-1 steps left
-    case 1: round(std::integral_constant<int, 1>{}, s); break;
-    case 2: round(std::integral_constant<int, 2>{}, s); break;
-    case 3: round(std::integral_constant<int, 3>{}, s); break;
-    case 4: if constexpr (U > 4) round(std::integral_constant<int, (U > 4 ? 4 : 1)>{}, s); break;
-    case 5: if constexpr (U > 5) round(std::integral_constant<int, (U > 5 ? 5 : 1)>{}, s); break;
-    case 6: if constexpr (U > 6) round(std::integral_constant<int, (U > 6 ? 6 : 1)>{}, s); break;
-    case 7: if constexpr (U > 7) round(std::integral_constant<int, (U > 7 ? 7 : 1)>{}, s); break;
+    NS_GEMV_TAIL(1) NS_GEMV_TAIL(2) NS_GEMV_TAIL(3) NS_GEMV_TAIL(4) NS_GEMV_TAIL(5)
+    NS_GEMV_TAIL(6) NS_GEMV_TAIL(7) NS_GEMV_TAIL(8) NS_GEMV_TAIL(9) NS_GEMV_TAIL(10)
+    NS_GEMV_TAIL(11) NS_GEMV_TAIL(12) NS_GEMV_TAIL(13) NS_GEMV_TAIL(14) NS_GEMV_TAIL(15)
     default: break;
   }
+#undef NS_GEMV_TAIL
 
 #pragma unroll
   for (int i = 0; i < MF; ++i)
@@ -737,8 +736,10 @@ static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B,
                      hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
   constexpr int NB = NF * (EPI == EPI_SILU_MUL ? 2 : 1);
   // k-steps in flight, as registers allow (1024-thread workgroups get 128
-  // VGPRs per lane)
-  constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 4 ? 8 : 4);
+  // VGPRs per lane); with at most 3 fragments per k-step, 16 (192 VGPRs),
+  // so a wavefront's share of a split (the down projection at 32 rows: 10
+  // k-steps) is one round of loads
+  constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 3 ? 16 : ((MF + NB) <= 4 ? 8 : 4));
   const unsigned grid = (unsigned)((N + 16 * NF - 1) / (16 * NF) * splits);
   hipLaunchKernelGGL((gemv_bf16_kernel<MF, NF, NW, U, EPI, bf16_t>), dim3(grid), dim3(64 * NW), 0, st,
                      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
