@@ -3,25 +3,33 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Prints ONE JSON line.  The timed workload is the Qwen2.5-0.5B-shaped 24-layer
-decode step at batch 32, context 512 (KV blocks of 16, tied LM head), bf16,
-replayed as one captured hipGraph per step: ``value`` is decode tokens/s
-(batch x steps / seconds) with every input already resident in HBM.
+Prints ONE JSON line.  The timed workload is the LLaMA-2-70B-shaped 80-layer
+decode step with 256 sequences (contexts 512..1536, KV blocks of 16, untied
+LM head of 32,000), bf16, replayed as one captured hipGraph per step:
+``value`` is decode tokens/s (256 x steps / seconds) with every input
+already resident in HBM.
 
 Also reported (each kernel timed live with HIP events on the stream it runs
 on, behind a queued busy-wait kernel so host launch gaps do not count):
-  * ``roofline``: the step's dominant kernel (the gate-up projection) against
-    the HBM peak; ``attention_roofline``: the paged decode attention alike;
-  * ``kernels``: per-kernel achieved GB/s or TFLOP/s for the step's kernels;
-  * ``dense_batch``: the LLaMA-2-70B-shaped layer at the 2048-token dense
-    batch -- decode attention (512 rows x context 1024) against the HBM peak,
-    the four projections against the bf16 MFMA peak, and the layer step with
-    and without the nano-batch overlap;
-  * ``batch_sweep``: the same model under the continuous-batching mix
-    (batch 1..256, contexts 128..2048, fragmented tables, a graph per batch
-    size): tokens/s against the step's HBM floor, attention GB/s;
-  * ``llama70b_80l_b256``: the LLaMA-2-70B-shaped 80-layer step with 256
-    sequences (contexts 512..1536), with and without the nano-batch overlap;
+  * ``roofline``: the step's dominant kernel (the paged decode attention)
+    against the HBM peak, with its calibrated counter traffic and its share
+    of the measured read ceiling; ``gemm_roofline``: the step's gate-up
+    projection at 256 rows against the bf16 MFMA peak;
+  * ``step``, ``kernels``, ``clock``: the step's runs, eager time, HBM floor,
+    the nano-batch overlap against the unsplit step, per-kernel rates, and
+    the shader clock while it replays; ``corun_interference``: the co-run
+    profile P(R) of its gate-up projection beside its attention;
+  * ``qwen05b_b32_ctx512``, ``qwen05b_b1_ctx512``, ``batch_sweep``,
+    ``bucketed_capture``: the Qwen2.5-0.5B-shaped 24-layer step at batch 32
+    and 1 (context 512) and under the continuous-batching mix (batch 1..256,
+    contexts 128..2048, fragmented tables, a graph per batch size);
+  * ``dense_batch``, ``dense_attention_roofline``, ``dense_gemm_roofline``:
+    the LLaMA-2-70B-shaped layer at the 2048-token dense batch -- decode
+    attention (512 rows x context 1024) against the HBM peak, the four
+    projections against the bf16 MFMA peak, the layer step serial and under
+    the nano-batch schedules, and the co-run profile;
+  * ``hbm_read_ceiling``: the library's streaming read over 4 GiB (the read
+    rate a kernel reaches here); ``torch_copy_rate``: a plain device copy;
   * ``cpu_baseline``: the CPU oracle timed on the host (bounded sample).
 """
 from __future__ import annotations
@@ -81,6 +89,27 @@ def time_launches(fn, n, stream, reps=3):
         e1.synchronize()
         out.append(e0.elapsed_time(e1) / n * 1e-3)
     return statistics.median(out)
+
+
+def read_ceiling(stream, nbytes=4 << 30, n=10):
+    """Achievable HBM read rate: the library's streaming read (ns_read_stream:
+    every byte once, 16-byte non-temporal loads) over a 4 GiB buffer, beside
+    the 8 TB/s datasheet figure and the attention's bytes per second."""
+    src = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(ns.NS_READ_STREAM_WORDS, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()  # the buffers were written on torch's stream
+
+    def launch(i):
+        ns.ns_read_stream(src.data_ptr(), nbytes, sink.data_ptr(), ns.NS_READ_STREAM_WORDS, stream)
+
+    for i in range(3):
+        launch(i)
+    t = time_launches(launch, n, stream)
+    del src, sink
+    torch.cuda.synchronize()
+    gbs = nbytes / t / 1e9
+    return {"kernel": "read_stream_kernel (ns_read_stream)", "bytes_per_launch": nbytes, "avg_launch_us": t * 1e6,
+            "gbs": gbs, "frac_of_peak": gbs / rf.HBM_PEAK_GBS}
 
 
 def copy_ceiling(stream, nbytes=1 << 30, n=10):
@@ -1086,6 +1115,11 @@ def main():
         result["dense_batch"] = _rounded(_leg(dense_batch, stream))
         result.update(dense_rooflines(result["dense_batch"]))
     result["torch_copy_rate"] = _rounded(copy_ceiling(stream))
+    result["hbm_read_ceiling"] = _rounded(read_ceiling(stream))
+    rc = result["hbm_read_ceiling"]["gbs"]
+    for key in ("roofline", "dense_attention_roofline"):
+        if key in result:
+            result[key]["frac_of_read_ceiling"] = round(result[key]["achieved"] / rc, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _rounded(cpu_baseline(args.cpu_baseline_full))
     print(json.dumps(result, default=_jsonable), flush=True)

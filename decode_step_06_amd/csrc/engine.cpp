@@ -883,6 +883,18 @@ int ns_sample_greedy(const float* logits, int32_t n_rows, int32_t vocab, int32_t
   return NS_OK;
 }
 
+int ns_read_stream(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+  static_assert(ns::kReadStreamGrid == NS_READ_STREAM_WORDS, "one sink word per workgroup");
+  if (!src || !sink) NS_FAIL(NS_EINVAL, "null argument");
+  if (bytes == 0 || bytes % 16 != 0 || (uintptr_t)src % 16 != 0)
+    NS_FAIL(NS_EINVAL, "src must be 16-byte aligned and bytes a positive multiple of 16 (got %zu)", bytes);
+  if (sink_words < NS_READ_STREAM_WORDS)
+    NS_FAIL(NS_EINVAL, "sink holds %zu words, needs %d", sink_words, NS_READ_STREAM_WORDS);
+  ns::launch_read_stream(src, (long)(bytes / 16), sink, (hipStream_t)stream);
+  HIP_TRY(hipGetLastError());
+  return NS_OK;
+}
+
 void ns_graph_destroy(ns_graph* g) {
   if (!g) return;
   if (g->exec) (void)hipGraphExecDestroy(g->exec);

@@ -557,6 +557,28 @@ __global__ void __launch_bounds__(256) kv_gather_kernel(const int32_t* __restric
   }
 }
 
+// ---------------------------------------------------------------- read ceiling
+// Streams a buffer once: each lane reads 16-byte chunks (non-temporal) in a
+// grid-stride loop and XORs them; each workgroup stores the XOR of its
+// lanes.  Its rate is the HBM read rate a kernel can reach on this chip, the
+// ceiling the attention's bytes per second are compared against.  One load
+// in flight per lane over 2048 workgroups of 256 was the fastest of the
+// shapes measured on MI355X (7.0 TB/s; 4 or 8 loads per round at 4096-16384
+// workgroups 6.5-6.9 TB/s).
+__global__ void __launch_bounds__(256) read_stream_kernel(const u32x4_t* __restrict__ p, long n16,
+                                                          uint32_t* __restrict__ sink) {
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  const long stride = (long)gridDim.x * 256;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+  uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) r ^= __shfl_xor(r, o, 64);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = r;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
 // ---------------------------------------------------------------- launchers
 static inline int nblocks(long n, int per) {
   long b = (n + per - 1) / per;
@@ -599,6 +621,10 @@ void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, in
     hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(T), dim3(256), 0, st, x, (const bf16_t*)g, (bf16_t*)h, H, eps);
   else
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, st, x, (const float*)g, (float*)h, H, eps);
+}
+
+void launch_read_stream(const void* src, long n16, uint32_t* sink, hipStream_t st) {
+  hipLaunchKernelGGL(read_stream_kernel, dim3(kReadStreamGrid), dim3(256), 0, st, (const u32x4_t*)src, n16, sink);
 }
 
 void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, const float* cosb,

@@ -47,6 +47,8 @@ void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, in
 // tokens out[r] = argmax of row r of fp32 logits [n_rows, V] (lowest index
 // among equal maxima, NaN never wins, a row of NaN only gives 0)
 void launch_argmax_rows(const float* logits, int n_rows, int V, int32_t* out, hipStream_t st);
+constexpr int kReadStreamGrid = 2048;  // workgroups of the streaming read (= NS_READ_STREAM_WORDS)
+void launch_read_stream(const void* src, long n16, uint32_t* sink, hipStream_t st);
 // x[t] += sum_s P[s][t] (slice order; the split-K residual add of the
 // previous projection), written back to x, then RMSNorm into h.
 void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_stride, int splits, const void* g,

@@ -81,6 +81,7 @@ SIGNATURES = {
     "ns_graph_replay": (C.c_int, [_P, C.POINTER(ns_batch), _P]),
     "ns_graph_destroy": (None, [_P]),
     "ns_sample_greedy": (C.c_int, [_P, _I, _I, _P, _P]),
+    "ns_read_stream": (C.c_int, [_P, C.c_size_t, _P, C.c_size_t, _P]),
     "ns_graph_set_capture": (C.c_int, [_P, _PI, _I, _P, _P, C.POINTER(_P)]),
     "ns_graph_set_replay": (C.c_int, [_P, C.POINTER(ns_batch), _P, _PI]),
     "ns_graph_set_destroy": (None, [_P]),
@@ -275,6 +276,13 @@ def ns_graph_set_destroy(gs) -> None:
 
 def ns_sample_greedy(logits_dev: int, n_rows: int, vocab: int, tokens_dev: int, stream=None) -> None:
     _check(lib().ns_sample_greedy(logits_dev, n_rows, vocab, tokens_dev, _stream_ptr(stream)))
+
+
+NS_READ_STREAM_WORDS = 2048
+
+
+def ns_read_stream(src_dev: int, nbytes: int, sink_dev: int, sink_words: int, stream=None) -> None:
+    _check(lib().ns_read_stream(src_dev, nbytes, sink_dev, sink_words, _stream_ptr(stream)))
 
 
 def ns_graph_capture(eng, bucket: int, out_dev: int, stream) -> C.c_void_p:

@@ -208,10 +208,10 @@ int ns_slot_map(const ns_kv* kv, int32_t n_tok, const int32_t* seq, const int32_
  *     a step must then belong to distinct sequences (a decode batch): a row
  *     reads no K/V that another row of the same step writes.  Steps and
  *     replays of graphs captured with it reject a batch that repeats a
- *     sequence (NS_EINVAL).  Excludes prefill_tiles.  Steps whose attention
- *     runs one wavefront per (row, KV head) item (2048 or more items) keep
- *     the separate kernel: there the prologue would serialise in front of
- *     every item.  Results are bit-identical either way. */
+ *     sequence (NS_EINVAL).  Excludes prefill_tiles.  Steps of 2048 or more
+ *     (row, KV head) attention items keep the separate kernel: there the
+ *     items alone fill the chip and the prologue would serialise in front of
+ *     every item's K/V stream.  Results are bit-identical either way. */
 typedef struct {
   int32_t n_nano;
   int32_t nano_rows[4];
@@ -325,6 +325,20 @@ void ns_graph_set_destroy(ns_graph_set* set);
  * to the host.  Errors: NS_EINVAL (null pointer, n_rows or vocab < 1),
  * NS_EHIP. */
 int ns_sample_greedy(const float* logits, int32_t n_rows, int32_t vocab, int32_t* tokens_out, void* stream);
+
+/* Streaming read, for measuring the memory ceiling of the roofline: the
+ * pages take the ceiling as the datasheet bandwidth and note that real
+ * kernels reach only part of it (roofline page, "The roofline flips", section
+ * "The bare mechanism: what the roofline says"); timing this call gives the
+ * read rate a kernel reaches on this chip, beside which the attention's
+ * bytes per second are read.  Reads every byte of src (device, 16-byte
+ * aligned; bytes a positive multiple of 16) once and writes
+ * NS_READ_STREAM_WORDS words to sink (device uint32, sink_words of room):
+ * their XOR equals the XOR of all 32-bit words of src.  Enqueued on
+ * `stream`.  Errors: NS_EINVAL (null pointer, misaligned src, bytes not a
+ * positive multiple of 16, sink too small), NS_EHIP. */
+#define NS_READ_STREAM_WORDS 2048
+int ns_read_stream(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
 
 /* ------------------------------------------------------------ helpers */
 
