@@ -190,7 +190,8 @@ def run_step_bench(h, b, steps, warmup, warm_seconds, stream):
 
 # ---------------------------------------------------------------- greedy decoding
 def greedy_loop(h, b, stream, steps=100):
-    """Greedy decoding at the headline batch: the device argmax alone, and a
+    """Greedy decoding at the step's batch (the 0.5B-shaped step at 32 rows):
+    the device argmax alone, and a
     loop of steps whose tokens come from the previous step's argmax, either
     on the device (graph replay + ns_sample_greedy, token ids fed back
     through token_ids_dev: no host round trip) or through the host (replay,
@@ -1055,12 +1056,12 @@ def main():
     kern = r["kernels"]
     tot = sum(v["us_per_step"] for v in kern.values())
     att, gu = r["att"], r["gu"]
-    # dominant kernel: the paged decode attention (the split kernel and its
-    # combine: each row's context in two parts), the class with the largest
-    # share of the step's device time in the kernel trace of this command;
-    # HBM-bound.  Its average launch duration from back-to-back launches over
-    # the layers' caches (events on the launching stream).
-    roof = {"kernel": "paged decode attention (attn_mfma_kernel + attn_combine_kernel)", "bound": "hbm",
+    # dominant kernel: the paged decode attention (4 wavefronts per (row, KV
+    # head) item over whole contexts, no combine launch), the kernel with the
+    # largest share of the step's device time in the kernel trace of this
+    # command; HBM-bound.  Its average launch duration from back-to-back
+    # launches over the layers' caches (events on the launching stream).
+    roof = {"kernel": "paged decode attention (attn_mfma_kernel, whole contexts)", "bound": "hbm",
             "achieved": round(att["gbs"], 1), "peak": rf.HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(att["gbs"] / rf.HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("attention_llama70b_80l_b256"),
