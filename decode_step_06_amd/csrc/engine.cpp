@@ -166,6 +166,7 @@ struct ns_engine {
   int num_blocks = 0;
   int max_tokens = 0;
   int maxb = 0;
+  int ncu = 256;  // compute units: workgroups of one dispatch round
   char* ws = nullptr;
   Plan plan{};
   ns_sched sched{};
@@ -294,6 +295,23 @@ std::vector<std::pair<int, int>> attn_row_parts(const ns_sched& sc, int n_tok) {
 // Pack the step metadata for `rows` rows (rows >= n_tok are padding) of a
 // step run under schedule sc into pinned staging and copy it to the device
 // with one transfer.
+// How an attention launch of n_rows rows (per_row work items each) orders
+// its rows.  From kOrderItems items: longest context first (more items than
+// the chip holds at once; the dispatch hands the short ones to the CUs that
+// free up first: 256 rows of the 70B shape with contexts 512..1536, 202 ->
+// 192 us in isolation).  Between one and two dispatch rounds (more items
+// than CUs, all resident at once, two workgroups on the busiest CUs):
+// zig-zag, so the workgroups that share a CU pair a long row with a short
+// one.  Fewer items: none (one round, each item on a CU of its own; the order
+// would only add a dependent load in front of each).
+enum { kOrderNone = 0, kOrderLongest = 1, kOrderZigzag = 2 };
+int attn_row_order(const ns_engine* e, long n_rows, long per_row) {
+  const long items = n_rows * per_row;
+  if (items >= kOrderItems) return kOrderLongest;
+  if (items > e->ncu && items <= 2L * e->ncu) return kOrderZigzag;
+  return kOrderNone;
+}
+
 int upload_meta(ns_engine* e, const ns_batch* b, int rows, const ns_sched& sc, hipStream_t st) {
   const int k = e->staging_next;
   e->staging_next ^= 1;
@@ -327,13 +345,23 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, const ns_sched& sc, h
     slot[i] = tab[p / NS_BLOCK_SIZE] * NS_BLOCK_SIZE + p % NS_BLOCK_SIZE;
   }
   // longest context first within each attention part (padding rows last);
-  // ties in row order
+  // ties in row order.  Parts whose work items fill two dispatch rounds are
+  // zig-zagged instead: the rows of the first round longest first, the rest
+  // shortest first, so each CU's second workgroup (a short row) joins a long
+  // one (attn_row_order says which parts use the order at all).
+  int pt = 0, np = 0, wv = 0;
+  attn_partition(rows, e->d.n_kv_heads, e->maxb * NS_BLOCK_SIZE, &pt, &np, &wv);
   for (const auto& pr : attn_row_parts(sc, rows)) {
     for (int i = pr.first; i < pr.second; ++i) order[i] = i;
     std::stable_sort(order + pr.first, order + pr.second, [&](int32_t a, int32_t c) {
       const int32_t ka = rowb[a] < 0 ? -1 : pos[a], kc = rowb[c] < 0 ? -1 : pos[c];
       return ka > kc;
     });
+    const long per_row = (long)e->d.n_kv_heads * np;
+    if (attn_row_order(e, pr.second - pr.first, per_row) == kOrderZigzag) {
+      const long first = (e->ncu + per_row - 1) / per_row;  // rows of the first round
+      if (first < pr.second - pr.first) std::reverse(order + pr.first + first, order + pr.second);
+    }
   }
   const size_t head = 5 * (size_t)T * sizeof(int32_t);
   const size_t bytes = head + (size_t)rows * e->maxb * sizeof(int32_t);
@@ -369,12 +397,7 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
   a->wg_cap = e->sched.attn_wg_cap;
   a->row_seq = e->sched.prefill_tiles ? e->m_seq() : nullptr;
   a->kv_nt = e->kv_layer >= kKvStreamBytes;
-  // Longest rows first once the work items outnumber what the chip holds at
-  // once (the dispatch then hands the short ones to the CUs that free up
-  // first: 256 rows of the 70B shape with contexts 512..1536, 202 -> 192 us
-  // in isolation).  Below that every item starts at once and the order
-  // would only add a dependent load in front of each.
-  if ((long)(r1 - r0) * a->nkv * a->n_parts >= kOrderItems) a->row_order = e->m_order();
+  if (attn_row_order(e, r1 - r0, (long)a->nkv * a->n_parts) != kOrderNone) a->row_order = e->m_order();
 }
 
 // The kernel sequence of one step over n_tok rows (metadata already on the
@@ -670,6 +693,7 @@ int ns_engine_create(const ns_model_desc* desc, const ns_weights* w, ns_kv* kv, 
 
   ns_engine* e = new ns_engine;
   e->d = *desc;
+  e->ncu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   e->es = elem_size(desc->dtype);
   e->G = G;
   for (int l = 0; l < desc->n_layers; ++l) {

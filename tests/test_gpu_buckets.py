@@ -3,8 +3,10 @@ bucket, a batch replayed on the smallest bucket that holds it with the rest
 as padding rows.  The real rows equal an eager step of the same padded batch
 bit for bit, and the oracle within the bf16 bound; also with RoPE fused into
 attention (padding rows belong to no sequence, so the fused schedule accepts
-them), and with buckets large enough (1024 attention work items and more)
-that the attention takes its rows longest context first, padding last."""
+them), and with buckets large enough that the attention orders its rows:
+zig-zag between one and two dispatch rounds of work items (bucket 64 of 8 KV
+heads: 512 items, padding rows in the shortest-first half) and longest
+context first from 1024 items (buckets 128..200), padding last."""
 import numpy as np
 import pytest
 import torch
