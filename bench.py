@@ -860,15 +860,18 @@ def small_step(stream, wname, steps, warm_seconds, detail):
 
 
 # ---------------------------------------------------------------- CPU oracle
-def oracle_step_seconds(shape, b, maxb, gen):
+def oracle_step_seconds(shape, b, maxb, gen, min_seconds=0.0):
     """Wall time of the oracle in its float32 mode for one decode step of a
     workload: one layer over all of the batch's rows (its attention over each
     row's cached context through the block tables), times the layer count,
-    plus the final norm and LM head.  The oracle gets inputs of its own, of
-    the workload's shapes and distributions, drawn with torch's generator
-    `gen` on the device and copied to the host (nothing read back from the
-    library).  Returns (seconds, seconds of the one layer, seconds of the
-    head)."""
+    plus the final norm and LM head.  The layer runs at least 3 times and
+    until `min_seconds` of it have passed (at most 50), and its median counts
+    (each run writes the same cache slots, so the work is the same).  The
+    oracle gets inputs of its own, of the workload's shapes and
+    distributions, drawn with torch's generator `gen` on the device and copied
+    to the host (nothing read back from the library).  Returns (seconds,
+    seconds of the one layer, seconds of the head, layer runs, seconds of all
+    layer runs)."""
     from dataclasses import replace
 
     from decode_step_06_amd.inputs import GAIN_STD, WEIGHT_STD, weight_names
@@ -890,9 +893,12 @@ def oracle_step_seconds(shape, b, maxb, gen):
                  [draw((P, shape.n_kv_heads, shape.head_dim))])
     x = draw((b.n_rows, shape.hidden))
     one = od.Oracle(replace(shape, n_layers=1, vocab=0, tied=False), {"layers": [lw]}, precision="f32")
-    t0 = time.perf_counter()
-    y = one.step(cache, tables, b.row_seq, b.row_pos, x=x)
-    t_layer = time.perf_counter() - t0
+    runs = []
+    while len(runs) < 3 or (sum(runs) < min_seconds and len(runs) < 50):
+        t0 = time.perf_counter()
+        y = one.step(cache, tables, b.row_seq, b.row_pos, x=x)
+        runs.append(time.perf_counter() - t0)
+    t_layer = statistics.median(runs)
     t_head = 0.0
     if shape.vocab:
         head = od.Oracle(shape, {"final_norm": draw((shape.hidden,), GAIN_STD, 1.0),
@@ -900,7 +906,7 @@ def oracle_step_seconds(shape, b, maxb, gen):
         t0 = time.perf_counter()
         head.head(y)
         t_head = time.perf_counter() - t0
-    return t_layer * shape.n_layers + t_head, t_layer, t_head
+    return t_layer * shape.n_layers + t_head, t_layer, t_head, len(runs), sum(runs)
 
 
 def cpu_baseline(full=False):
@@ -914,18 +920,19 @@ def cpu_baseline(full=False):
     cores = len(os.sched_getaffinity(0))
     w = WORKLOADS[HEADLINE]
     b = gen_batch(w, with_past=False, pool_slack=1.02)
-    t, tl, th = oracle_step_seconds(w.model, b, blocks_for(b.seq_lens), gen)
+    t, tl, th, nr, tr = oracle_step_seconds(w.model, b, blocks_for(b.seq_lens), gen, min_seconds=8.0)
     out = {"value": b.n_rows / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-           "sample": f"one of the 80 layers of {HEADLINE} over all {b.n_rows} rows ({tl:.1f} s) plus the final norm "
-                     f"and LM head ({th:.1f} s), float32 numpy; the step time is 80 x the layer + the head",
+           "sample": f"one of the 80 layers of {HEADLINE} over all {b.n_rows} rows, run {nr} times ({tr:.1f} s; "
+                     f"median {tl:.2f} s), plus the final norm and LM head ({th:.1f} s), float32 numpy; the step "
+                     f"time is 80 x the layer's median + the head",
            "threads_env": os.environ.get("OMP_NUM_THREADS")}
     other = [SMALL] + ([f"qwen05b_mix_b{B}" for B in SWEEP] + ["llama70b_layer_t2048"] if full else [])
     extra = {}
     for name in other:
         wo = WORKLOADS[name]
         bo = gen_batch(wo, with_past=False)
-        t, tl, th = oracle_step_seconds(wo.model, bo, blocks_for(bo.seq_lens), gen)
-        extra[name] = {"tokens_per_s": bo.n_rows / t, "step_s": t, "layer_s": tl, "head_s": th}
+        t, tl, th, nr, _ = oracle_step_seconds(wo.model, bo, blocks_for(bo.seq_lens), gen, min_seconds=1.0)
+        extra[name] = {"tokens_per_s": bo.n_rows / t, "step_s": t, "layer_s": tl, "head_s": th, "layer_runs": nr}
     out["other_workloads"] = extra
     return out
 
