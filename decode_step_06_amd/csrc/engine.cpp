@@ -16,9 +16,11 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "ns_internal.h"
@@ -646,6 +648,21 @@ int copy_bad_tokens(ns_engine* e, const ns_batch* b, hipStream_t st) {
   return NS_OK;
 }
 
+constexpr double kDrainSeconds = 30.0;  // longest wait for the engine's work at teardown
+
+// Poll `query` (a stream or event query) until it stops reporting work in
+// flight or kDrainSeconds pass; true when it drained (or reported an error,
+// which leaves nothing to wait for).
+template <typename Q>
+bool wait_drained(Q query) {
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    if (query() != hipErrorNotReady) return true;
+    if (std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() > kDrainSeconds) return false;
+    std::this_thread::sleep_for(std::chrono::milliseconds(1));
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -717,7 +734,7 @@ int ns_engine_create(const ns_model_desc* desc, const ns_weights* w, ns_kv* kv, 
   e->plan = plan;
   if (sched) e->sched = *sched;
   auto fail = [&](int code) {
-    ns_engine_destroy(e);
+    (void)ns_engine_destroy(e);
     return code;
   };
   if ((rc = make_second_stream(e, e->sched.cu_mask_frac))) return fail(rc);
@@ -752,32 +769,32 @@ int ns_engine_create(const ns_model_desc* desc, const ns_weights* w, ns_kv* kv, 
   return NS_OK;
 }
 
-void ns_engine_destroy(ns_engine* e) {
-  if (!e) return;
-  if (e->s2) {
-    (void)hipStreamSynchronize(e->s2);
-    (void)hipStreamDestroy(e->s2);
-  }
+int ns_engine_destroy(ns_engine* e) {
+  if (!e) return NS_OK;
+  // work that may still use the engine's stream, events and pinned staging
+  bool drained = !e->s2 || wait_drained([&] { return hipStreamQuery(e->s2); });
+  if (drained && e->bad_tok_ev) drained = wait_drained([&] { return hipEventQuery(e->bad_tok_ev); });
+  for (int k = 0; k < 2 && drained; ++k)
+    if (e->staging_ev[k]) drained = wait_drained([&] { return hipEventQuery(e->staging_ev[k]); });
+  if (!drained)  // leave everything allocated: the work in flight still uses it
+    NS_FAIL(NS_EHIP, "engine work still in flight after %.0f s; its stream, events and staging stay allocated",
+            kDrainSeconds);
+  if (e->s2) (void)hipStreamDestroy(e->s2);
   for (int i = 0; i < kMaxParts; ++i) {
     if (e->ev_qkv[i]) (void)hipEventDestroy(e->ev_qkv[i]);
     if (e->ev_att[i]) (void)hipEventDestroy(e->ev_att[i]);
   }
   if (e->ev_join) (void)hipEventDestroy(e->ev_join);
-  if (e->bad_tok_ev) {
-    (void)hipEventSynchronize(e->bad_tok_ev);
-    (void)hipEventDestroy(e->bad_tok_ev);
-  }
+  if (e->bad_tok_ev) (void)hipEventDestroy(e->bad_tok_ev);
   if (e->bad_tok_host) (void)hipHostFree(e->bad_tok_host);
   for (hipEvent_t ev : e->prof_ev) (void)hipEventDestroy(ev);
   if (e->prof_start) (void)hipEventDestroy(e->prof_start);
   for (int k = 0; k < 2; ++k) {
-    if (e->staging_ev[k]) {
-      (void)hipEventSynchronize(e->staging_ev[k]);
-      (void)hipEventDestroy(e->staging_ev[k]);
-    }
+    if (e->staging_ev[k]) (void)hipEventDestroy(e->staging_ev[k]);
     if (e->staging[k]) (void)hipHostFree(e->staging[k]);
   }
   delete e;
+  return NS_OK;
 }
 
 int ns_engine_set_sched(ns_engine* e, const ns_sched* sched) {

@@ -74,7 +74,7 @@ SIGNATURES = {
     "ns_workspace_bytes": (C.c_size_t, [C.POINTER(ns_model_desc), _I, _I]),
     "ns_engine_create": (C.c_int, [C.POINTER(ns_model_desc), C.POINTER(ns_weights), _P, _P, C.c_size_t, _P,
                                    C.c_size_t, _I, C.POINTER(ns_sched), C.POINTER(_P)]),
-    "ns_engine_destroy": (None, [_P]),
+    "ns_engine_destroy": (C.c_int, [_P]),
     "ns_engine_set_sched": (C.c_int, [_P, C.POINTER(ns_sched)]),
     "ns_decode_step": (C.c_int, [_P, C.POINTER(ns_batch), _P, _P]),
     "ns_graph_capture": (C.c_int, [_P, _I, _P, _P, C.POINTER(_P)]),
@@ -246,7 +246,7 @@ def ns_engine_create(desc, weights: ns_weights, kv, kv_dev: int, kv_bytes: int, 
 
 
 def ns_engine_destroy(eng) -> None:
-    lib().ns_engine_destroy(eng)
+    _check(lib().ns_engine_destroy(eng))
 
 
 def ns_engine_set_sched(eng, sched: ns_sched) -> None:

@@ -268,7 +268,13 @@ size_t ns_workspace_bytes(const ns_model_desc* desc, int32_t max_tokens,
 int ns_engine_create(const ns_model_desc* desc, const ns_weights* weights, ns_kv* kv,
                      void* kv_dev, size_t kv_bytes, void* workspace, size_t ws_bytes,
                      int32_t max_tokens, const ns_sched* sched, ns_engine** out);
-void ns_engine_destroy(ns_engine* eng);
+/* Release an engine: waits (at most 30 s) for the work it enqueued on its
+ * second stream and for its event-guarded copies, then frees its stream,
+ * events and pinned staging.  NULL is a no-op.  Errors: NS_EHIP when that
+ * work has not finished within the wait; the engine's resources then stay
+ * allocated (the work in flight still uses them) and the handle must not be
+ * used again. */
+int ns_engine_destroy(ns_engine* eng);
 
 /* Replace the engine's schedule (not the CU mask).  Graphs captured earlier
  * keep the schedule they were captured with. */

@@ -162,6 +162,7 @@ def test_engine_create_rejects_bad_arguments_without_a_gpu():
         assert "null" in ns.lib().ns_last_error().decode()
     finally:
         ns.ns_kv_destroy(kv)
+    assert ns.lib().ns_engine_destroy(None) == ns.NS_OK   # releasing no engine is a no-op
     rc = ns.lib().ns_op_gemm(ns.NS_BF16, 0, 4, 4, 30, None, None, None, None)
     assert rc == ns.NS_EINVAL  # null matrices are checked first
     bad = ns.model_desc(TINY)
