@@ -305,7 +305,6 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;
   const long item0 = ((long)t * a.nkv + g) * a.n_parts;
-  T* outp = (T*)a.out + (long)t * a.nq * D + (long)g * G * D;
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
     const int h = idx / D;
     float M = -INFINITY;
@@ -316,7 +315,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
       L += a.part_ml[(item0 + p) * G * 2 + 2 * h + 1] * wgt;
       o += a.part_acc[(item0 + p) * G * D + idx] * wgt;
     }
-    Elem<T>::store(outp, idx, o / L);
+    Elem<T>::store((T*)a.out, act_idx(t, g * G * D + idx, a.nq * D, a.out_slab_rows), o / L);
   }
 }
 
@@ -622,7 +621,7 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
     const int32_t* __restrict__ row_bseq, const int32_t* __restrict__ row_pos, const int32_t* __restrict__ btab,
     bf16_t* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml, int maxb, int row0,
     int n_rows, int nq, int nkv, int P, int n_parts, float scale_log2, const int32_t* __restrict__ skip_seq,
-    RopeIn ra, const int32_t* __restrict__ row_order) {
+    RopeIn ra, const int32_t* __restrict__ row_order, int osr) {
   static_assert(G <= 16 && D % 32 == 0, "heads must fit the 16 MFMA columns, d whole k-steps");
   constexpr int NCH = D / 8;  // 16-byte chunks per head row
   constexpr int KS = D / 32, DT = D / 16;
@@ -662,10 +661,11 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
     const int f2 = __builtin_amdgcn_readfirstlane(bt[min((cf >> 4) + 2, maxb - 1)]);
     const int f3 = __builtin_amdgcn_readfirstlane(bt[min((cf >> 4) + 3, maxb - 1)]);
     asm volatile("" : : "s"(f0), "s"(f1), "s"(f2), "s"(f3));
-    bf16_t* outp = out + (long)t * nq * D + (long)g * G * D;
+    // output column c of this item's heads (row-major or slab-major out)
+    auto oix = [&](int c) { return act_idx(t, g * G * D + c, nq * D, osr); };
     if (pad) {  // padding row: zero output
       if (part == 0)
-        for (int i = threadIdx.x; i < G * D; i += 64 * NWAVE) outp[i] = 0;
+        for (int i = threadIdx.x; i < G * D; i += 64 * NWAVE) out[oix(i)] = 0;
       continue;
     }
     const int ctx = pos_t + 1;
@@ -732,13 +732,13 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
       if (hc < G) {
         if (nparts_row == 1) {
           const float inv = 1.f / l;
-          bf16_t* op = outp + (long)hc * D + 4 * grp;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
             uint2 o2;
             o2.x = pack_bf16(acc[dt][0] * inv, acc[dt][1] * inv);
             o2.y = pack_bf16(acc[dt][2] * inv, acc[dt][3] * inv);
-            *(uint2*)(op + 16 * dt) = o2;
+            // 4 consecutive columns from a multiple of 4: one slab piece
+            *(uint2*)(out + oix(hc * D + 16 * dt + 4 * grp)) = o2;
           }
         } else {
           float* pa = part_acc + (item * G + hc) * D + 4 * grp;
@@ -778,7 +778,7 @@ __global__ void __launch_bounds__(64 * NWAVE) attn_mfma_kernel(
           o += macc[v][h][dd] * wgt;
         }
         if (nparts_row == 1) {
-          outp[(long)h * D + dd] = f32_to_bf16(o / L);
+          out[oix(h * D + dd)] = f32_to_bf16(o / L);
         } else {
           part_acc[item * G * D + idx] = o;
           if (dd == 0) {
@@ -800,7 +800,7 @@ static void launch_mfma(const AttnArgs& a, long grid, float scale_log2, hipStrea
 #define NS_MFMA_ARGS                                                                                           \
   (const bf16_t*)a.q_att, (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.row_bseq, a.row_pos, a.btab,             \
       (bf16_t*)a.out, a.part_acc, a.part_ml, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, a.part_tokens, a.n_parts,  \
-      scale_log2, a.row_seq, ra, a.row_order
+      scale_log2, a.row_seq, ra, a.row_order, a.out_slab_rows
   const dim3 g((unsigned)grid);
   if (a.rope_qkv) {  // the fused prologue runs on 8 or 4 wavefronts per item
     if (a.waves == 8)

@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(256) rope_table_kernel(const int32_t* __restri
 // projection's epilogue, so x already holds the updated residual stream.
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x, const T* __restrict__ g,
-                                                      T* __restrict__ h, int H, float eps) {
+                                                      T* __restrict__ h, int H, float eps, int hs) {
   const int t = blockIdx.x;
   const float* xr = x + (long)t * H;
   float ss = 0.f;
@@ -69,8 +69,7 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
-  T* hr = h + (long)t * H;
-  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(hr, i, xr[i] * r * Elem<T>::load(g, i));
+  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(h, act_idx(t, i, H, hs), xr[i] * r * Elem<T>::load(g, i));
 }
 
 // The split-K residual add fused in front of the norm: x[t] += the slices
@@ -94,8 +93,8 @@ template <> struct Gain4<bf16_t> {
 
 template <typename T, int CH, int NT, int S>
 __device__ __forceinline__ void rmsnorm_reduce_row(float* __restrict__ xr, const float* __restrict__ pr,
-                                                   long slice_stride, const T* __restrict__ g, T* __restrict__ hr,
-                                                   int H, float eps) {
+                                                   long slice_stride, const T* __restrict__ g, T* __restrict__ h,
+                                                   int t, int hs, int H, float eps) {
   const int H4 = H >> 2;
   f32x4_t p[CH][S], v[CH], gv[CH];
 #pragma unroll
@@ -136,7 +135,7 @@ __device__ __forceinline__ void rmsnorm_reduce_row(float* __restrict__ xr, const
     const int i4 = threadIdx.x + c * NT;
     if (i4 < H4) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Elem<T>::store(hr, 4 * i4 + e, v[c][e] * r * gv[c][e]);
+      for (int e = 0; e < 4; ++e) Elem<T>::store(h, act_idx(t, 4 * i4 + e, H, hs), v[c][e] * r * gv[c][e]);
     }
   }
 }
@@ -144,17 +143,18 @@ __device__ __forceinline__ void rmsnorm_reduce_row(float* __restrict__ xr, const
 template <typename T, int CH, int NT>
 __global__ void __launch_bounds__(NT) rmsnorm_reduce_kernel(float* __restrict__ x, const float* __restrict__ P,
                                                             long slice_stride, int splits, const T* __restrict__ g,
-                                                            T* __restrict__ h, int H, float eps) {
-  const long o = (long)blockIdx.x * H;
+                                                            T* __restrict__ h, int H, float eps, int hs) {
+  const int t = blockIdx.x;
+  const long o = (long)t * H;
   switch (splits) {  // uniform: straight-line code for each slice count
-    case 1: return rmsnorm_reduce_row<T, CH, NT, 1>(x + o, P + o, slice_stride, g, h + o, H, eps);
-    case 2: return rmsnorm_reduce_row<T, CH, NT, 2>(x + o, P + o, slice_stride, g, h + o, H, eps);
-    case 3: return rmsnorm_reduce_row<T, CH, NT, 3>(x + o, P + o, slice_stride, g, h + o, H, eps);
-    case 4: return rmsnorm_reduce_row<T, CH, NT, 4>(x + o, P + o, slice_stride, g, h + o, H, eps);
-    case 5: return rmsnorm_reduce_row<T, CH, NT, 5>(x + o, P + o, slice_stride, g, h + o, H, eps);
-    case 6: return rmsnorm_reduce_row<T, CH, NT, 6>(x + o, P + o, slice_stride, g, h + o, H, eps);
-    case 7: return rmsnorm_reduce_row<T, CH, NT, 7>(x + o, P + o, slice_stride, g, h + o, H, eps);
-    default: return rmsnorm_reduce_row<T, CH, NT, kMaxSplits>(x + o, P + o, slice_stride, g, h + o, H, eps);
+    case 1: return rmsnorm_reduce_row<T, CH, NT, 1>(x + o, P + o, slice_stride, g, h, t, hs, H, eps);
+    case 2: return rmsnorm_reduce_row<T, CH, NT, 2>(x + o, P + o, slice_stride, g, h, t, hs, H, eps);
+    case 3: return rmsnorm_reduce_row<T, CH, NT, 3>(x + o, P + o, slice_stride, g, h, t, hs, H, eps);
+    case 4: return rmsnorm_reduce_row<T, CH, NT, 4>(x + o, P + o, slice_stride, g, h, t, hs, H, eps);
+    case 5: return rmsnorm_reduce_row<T, CH, NT, 5>(x + o, P + o, slice_stride, g, h, t, hs, H, eps);
+    case 6: return rmsnorm_reduce_row<T, CH, NT, 6>(x + o, P + o, slice_stride, g, h, t, hs, H, eps);
+    case 7: return rmsnorm_reduce_row<T, CH, NT, 7>(x + o, P + o, slice_stride, g, h, t, hs, H, eps);
+    default: return rmsnorm_reduce_row<T, CH, NT, kMaxSplits>(x + o, P + o, slice_stride, g, h, t, hs, H, eps);
   }
 }
 
@@ -164,7 +164,7 @@ template <typename T, int CH, int NT>
 __global__ void __launch_bounds__(NT) rmsnorm_reduce_wide_kernel(float* __restrict__ x, const float* __restrict__ P,
                                                                  long slice_stride, int splits,
                                                                  const T* __restrict__ g, T* __restrict__ h, int H,
-                                                                 float eps) {
+                                                                 float eps, int hs) {
   const int t = blockIdx.x, H4 = H >> 2;
   float* xr = x + (long)t * H;
   const float* pr = P + (long)t * H;
@@ -191,13 +191,13 @@ __global__ void __launch_bounds__(NT) rmsnorm_reduce_wide_kernel(float* __restri
 #pragma unroll
   for (int i = 0; i < NW; ++i) tot += red[i];
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
-  T* hr = h + (long)t * H;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int i4 = threadIdx.x + c * NT;
     if (i4 < H4) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Elem<T>::store(hr, 4 * i4 + e, v[c][e] * r * Elem<T>::load(g, 4 * i4 + e));
+      for (int e = 0; e < 4; ++e)
+        Elem<T>::store(h, act_idx(t, 4 * i4 + e, H, hs), v[c][e] * r * Elem<T>::load(g, 4 * i4 + e));
     }
   }
 }
@@ -207,7 +207,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_reduce_any_kernel(float* __restrict__ x, const float* __restrict__ P,
                                                                  long slice_stride, int splits,
                                                                  const T* __restrict__ g, T* __restrict__ h, int H,
-                                                                 float eps) {
+                                                                 float eps, int hs) {
   const int t = blockIdx.x;
   float* xr = x + (long)t * H;
   const float* pr = P + (long)t * H;
@@ -225,8 +225,7 @@ __global__ void __launch_bounds__(256) rmsnorm_reduce_any_kernel(float* __restri
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
-  T* hr = h + (long)t * H;
-  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(hr, i, xr[i] * r * Elem<T>::load(g, i));
+  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(h, act_idx(t, i, H, hs), xr[i] * r * Elem<T>::load(g, i));
 }
 
 __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ x, const float* __restrict__ P,
@@ -260,7 +259,7 @@ __global__ void __launch_bounds__(256) step_prologue_kernel(const T* __restrict_
                                                             float* __restrict__ cosb, float* __restrict__ sinb,
                                                             const T* __restrict__ g0, T* __restrict__ h, int H, int V,
                                                             int half, double log2_base, float eps,
-                                                            int32_t* __restrict__ bad_tok) {
+                                                            int32_t* __restrict__ bad_tok, int hs) {
   const int t = blockIdx.x;
   float* xr = x + (long)t * H;
   float ss = 0.f;
@@ -295,8 +294,7 @@ __global__ void __launch_bounds__(256) step_prologue_kernel(const T* __restrict_
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
-  T* hr = h + (long)t * H;
-  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(hr, i, xr[i] * r * Elem<T>::load(g0, i));
+  for (int i = threadIdx.x; i < H; i += 256) Elem<T>::store(h, act_idx(t, i, H, hs), xr[i] * r * Elem<T>::load(g0, i));
 }
 
 // ---------------------------------------------------------------- greedy sampling
@@ -604,23 +602,25 @@ void launch_rope_table(const int32_t* pos, float* cosb, float* sinb, int T, int 
 
 void launch_step_prologue(int dtype, const void* E, const int32_t* tok, float* x, const int32_t* pos, float* cosb,
                           float* sinb, const void* g0, void* h, int T, int H, int V, int d, float base, float eps,
-                          int32_t* bad_tok, hipStream_t st) {
+                          int32_t* bad_tok, hipStream_t st, int h_slab_rows) {
   if (T <= 0) return;
   const double lb = log2((double)base);
   if (dtype == NS_DT_BF16)
     hipLaunchKernelGGL(step_prologue_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)E, tok, x, pos, cosb,
-                       sinb, (const bf16_t*)g0, (bf16_t*)h, H, V, d / 2, lb, eps, bad_tok);
+                       sinb, (const bf16_t*)g0, (bf16_t*)h, H, V, d / 2, lb, eps, bad_tok, h_slab_rows);
   else
     hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)E, tok, x, pos, cosb,
-                       sinb, (const float*)g0, (float*)h, H, V, d / 2, lb, eps, bad_tok);
+                       sinb, (const float*)g0, (float*)h, H, V, d / 2, lb, eps, bad_tok, 0);
 }
 
-void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st) {
+void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st,
+                    int h_slab_rows) {
   if (T <= 0) return;
   if (dtype == NS_DT_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(T), dim3(256), 0, st, x, (const bf16_t*)g, (bf16_t*)h, H, eps);
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(T), dim3(256), 0, st, x, (const bf16_t*)g, (bf16_t*)h, H, eps,
+                       h_slab_rows);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, st, x, (const float*)g, (float*)h, H, eps);
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, st, x, (const float*)g, (float*)h, H, eps, 0);
 }
 
 void launch_read_stream(const void* src, long n16, uint32_t* sink, hipStream_t st) {
@@ -659,38 +659,38 @@ void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, 
 
 template <typename T>
 static void run_rmsnorm_reduce(float* x, const float* P, long slice_stride, int splits, const T* g, T* h, int T_,
-                               int H, float eps, hipStream_t st) {
+                               int H, float eps, hipStream_t st, int hs) {
   const int ch = (H / 4 + 255) / 256;
   // the one-round kernel reads the gains 4 at a time and holds a row's
   // slices in registers: rows of up to 8192 elements
   const bool aligned = ((uintptr_t)g % (4 * sizeof(T))) == 0;
   if (H % 4 != 0 || ch > 32)
     hipLaunchKernelGGL(rmsnorm_reduce_any_kernel<T>, dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g, h,
-                       H, eps);
+                       H, eps, hs);
   else if (ch > 8 || !aligned)
     hipLaunchKernelGGL((rmsnorm_reduce_wide_kernel<T, 8, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride,
-                       splits, g, h, H, eps);
+                       splits, g, h, H, eps, hs);
   else if (ch == 1)
     hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 1, 256>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g,
-                       h, H, eps);
+                       h, H, eps, hs);
   else if (ch == 2)
     hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 2, 256>), dim3(T_), dim3(256), 0, st, x, P, slice_stride, splits, g,
-                       h, H, eps);
+                       h, H, eps, hs);
   else if (ch <= 4)
     hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 1, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
-                       g, h, H, eps);
+                       g, h, H, eps, hs);
   else
     hipLaunchKernelGGL((rmsnorm_reduce_kernel<T, 2, 1024>), dim3(T_), dim3(1024), 0, st, x, P, slice_stride, splits,
-                       g, h, H, eps);
+                       g, h, H, eps, hs);
 }
 
 void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_stride, int splits, const void* g,
-                           void* h, int T, int H, float eps, hipStream_t st) {
+                           void* h, int T, int H, float eps, hipStream_t st, int h_slab_rows) {
   if (T <= 0) return;
   if (dtype == NS_DT_BF16)
-    run_rmsnorm_reduce<bf16_t>(x, P, slice_stride, splits, (const bf16_t*)g, (bf16_t*)h, T, H, eps, st);
+    run_rmsnorm_reduce<bf16_t>(x, P, slice_stride, splits, (const bf16_t*)g, (bf16_t*)h, T, H, eps, st, h_slab_rows);
   else
-    run_rmsnorm_reduce<float>(x, P, slice_stride, splits, (const float*)g, (float*)h, T, H, eps, st);
+    run_rmsnorm_reduce<float>(x, P, slice_stride, splits, (const float*)g, (float*)h, T, H, eps, st, 0);
 }
 
 void launch_reduce_rows(const float* x, const float* P, long slice_stride, int splits, float* out, int T, int H,

@@ -53,7 +53,7 @@ template <int BM, int BN, int BK, int WM, int WN, int EPI, typename OutT, int BN
 __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                                  const bf16_t* __restrict__ B, int ldb, int M, int N,
                                                                  int K, void* __restrict__ Cv, int ldc, int splits,
-                                                                 long slice_stride, int bpk) {
+                                                                 long slice_stride, int pk) {
   using C = GemmCfg<BM, BN, BK, WM, WN, EPI>;
   constexpr int LDK = C::LDK;
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDK];
@@ -90,8 +90,9 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
     for (int i = 0; i < C::A_PT; ++i) {
       const int c = tid + i * C::NT;
       if (c < C::A_CH) {
-        const int r = c / (BK / 8), k8 = c % (BK / 8);
-        ra[i] = *(const u32x4_t*)(A + (long)a_row(r) * lda + k0 + k8 * 8);
+        const int r = c / (BK / 8), k = k0 + (c % (BK / 8)) * 8;
+        ra[i] = *(const u32x4_t*)(A + ((pk & PK_A) ? ((long)(k >> 5) * lda + a_row(r)) * 32 + (k & 31)
+                                                   : (long)a_row(r) * lda + k));
       }
     }
 #pragma unroll
@@ -99,7 +100,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
       const int c = tid + i * C::NT;
       if (c < C::B_CH) {
         const int r = c / (BK / 8), k = k0 + (c % (BK / 8)) * 8;
-        const u32x4_t* src = bpk ? (const u32x4_t*)(B + ((long)(k >> 5) * ldb + b_row(r)) * 32 + (k & 31))
+        const u32x4_t* src = (pk & PK_B) ? (const u32x4_t*)(B + ((long)(k >> 5) * ldb + b_row(r)) * 32 + (k & 31))
                                  : (const u32x4_t*)(B + (long)b_row(r) * ldb + k);
         rb[i] = BNT ? __builtin_nontemporal_load(src) : *src;
       }
@@ -183,7 +184,9 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = m0 + wm * C::TM + 16 * i + er + r;
-          if (row < M) Elem<OutT>::store(Cp, (long)row * ldc + col, silu_f(acc[i][j][r]) * acc[i][j + HF][r]);
+          if (row < M)
+            Elem<OutT>::store(Cp, act_idx(row, col, ldc, (pk & PK_C) ? ldc : 0),
+                              silu_f(acc[i][j][r]) * acc[i][j + HF][r]);
         }
       }
   } else {
@@ -262,7 +265,7 @@ template <int EPI, typename OutT, int BM = 256, int BNT = 0, int NWV = 4, int PP
 __global__ void __launch_bounds__(64 * NWV) gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
                                                             const bf16_t* __restrict__ B, int ldb, int M, int N,
                                                             int K, void* __restrict__ Cv, int ldc, int splits,
-                                                            long slice_stride, int bpk) {
+                                                            long slice_stride, int pk) {
   static_assert(BM == 256 || BM == 128, "tile rows");
   static_assert(NWV == 4 || (NWV == 8 && BM == 256), "wavefronts");
   static_assert(PP == 0 || NWV == 8, "ping-pong takes two wavefronts per SIMD");
@@ -292,8 +295,12 @@ __global__ void __launch_bounds__(64 * NWV) gemm_big_kernel(const bf16_t* __rest
   const int tile_m = tile % m_tiles, tile_n = tile / m_tiles;
   const int m0 = tile_m * BM, n0 = tile_n * OUT_BN;
 
-  const unsigned a_bytes = (unsigned)((long)M * lda * 2);
-  const unsigned b_bytes = (unsigned)(bpk ? (long)K * ldb * 2 : (long)((EPI == EPI_SILU_MUL) ? 2 * N : N) * ldb * 2);
+  // A's byte span: M rows, or (slab-major) K / 32 - 1 whole slab blocks of
+  // lda rows then M rows of the last slab
+  const unsigned a_bytes =
+      (unsigned)((pk & PK_A) ? ((long)(K / 32 - 1) * lda + M) * 64 : (long)M * lda * 2);
+  const unsigned b_bytes =
+      (unsigned)((pk & PK_B) ? (long)K * ldb * 2 : (long)((EPI == EPI_SILU_MUL) ? 2 * N : N) * ldb * 2);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)a_bytes, BUF_RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)b_bytes, BUF_RSRC_WORD3);
   // Load instruction j of wavefront w fills the 16 LDS rows of group
@@ -313,7 +320,7 @@ __global__ void __launch_bounds__(64 * NWV) gemm_big_kernel(const bf16_t* __rest
     if (g < AG) {
       int m = m0 + r;
       m = m < M ? m : M - 1;
-      voff[j] = (unsigned)(((long)m * lda + c * 8) * 2);
+      voff[j] = (pk & PK_A) ? (unsigned)(m * 64 + c * 16) : (unsigned)(((long)m * lda + c * 8) * 2);
     } else {
       int brow;
       if constexpr (EPI == EPI_SILU_MUL) {
@@ -324,7 +331,7 @@ __global__ void __launch_bounds__(64 * NWV) gemm_big_kernel(const bf16_t* __rest
         int n = n0 + r;
         brow = n < N ? n : N - 1;
       }
-      voff[j] = bpk ? (unsigned)(brow * 64 + c * 16) : (unsigned)(((long)brow * ldb + c * 8) * 2);
+      voff[j] = (pk & PK_B) ? (unsigned)(brow * 64 + c * 16) : (unsigned)(((long)brow * ldb + c * 8) * 2);
     }
   }
   // K slabs [sb, sb + nk) of split blockIdx.y (all of K unless EPI_PARTIAL);
@@ -336,15 +343,16 @@ __global__ void __launch_bounds__(64 * NWV) gemm_big_kernel(const bf16_t* __rest
   auto issue = [&](int kt, int j0, int j1) {
     const int ks = sb + (kt < nk ? kt : nk - 1);
     const unsigned soff = (unsigned)ks * (BK * 2);
-    // packed B: slab ks is a contiguous [rows][32] block
-    const unsigned soff_b = bpk ? (unsigned)ks * (unsigned)ldb * (BK * 2) : soff;
+    // slab-major operands: slab ks is a contiguous [rows][32] block
+    const unsigned soff_a = (pk & PK_A) ? (unsigned)ks * (unsigned)lda * (BK * 2) : soff;
+    const unsigned soff_b = (pk & PK_B) ? (unsigned)ks * (unsigned)ldb * (BK * 2) : soff;
     char* base = lds + (kt % NSTAGE) * STAGE;
     // load slots j < AG / NWV carry A rows, the rest B rows (wave < NWV)
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       const int g = wave + NWV * j;
       if (j < AG / NWV)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j], soff_a, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(base + g * 16 * ROWB), 16, voff[j], soff_b, 0,
                                                  BNT ? 2 : 0);  // cache policy: 2 = nt
@@ -506,7 +514,8 @@ __global__ void __launch_bounds__(64 * NWV) gemm_big_kernel(const bf16_t* __rest
         for (int e = 0; e < 16; ++e) {
           const int row = m0 + wm * TM + 32 * i + 8 * (e >> 2) + eq + (e & 3);
           if (row < M)
-            Elem<OutT>::store((OutT*)Cv, (long)row * ldc + col, silu_f(acc[i][j][e]) * acc[i][j + HF][e]);
+            Elem<OutT>::store((OutT*)Cv, act_idx(row, col, ldc, (pk & PK_C) ? ldc : 0),
+                              silu_f(acc[i][j][e]) * acc[i][j + HF][e]);
         }
       }
   } else {
@@ -549,7 +558,7 @@ template <int MF, int NF, int NW, int U, int EPI, typename OutT>
 __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                             const bf16_t* __restrict__ B, int ldb, int M, int N,
                                                             int K, void* __restrict__ Cv, int ldc, int splits,
-                                                            long slice_stride, int bpk) {
+                                                            long slice_stride, int pk) {
   constexpr int DUAL = (EPI == EPI_SILU_MUL) ? 2 : 1;
   constexpr int NB = NF * DUAL;  // B fragments per k-step (U k-steps in flight)
   __shared__ f32x4_t red[NW][MF * NB][64];
@@ -564,16 +573,17 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
     int n = n0 + 16 * f + fr;
     n = n < N ? n : N - 1;
 #pragma unroll
-    for (int dd = 0; dd < DUAL; ++dd) brow[f * DUAL + dd] = B + (long)(dd ? N + n : n) * (bpk ? 32 : ldb) + fk;
+    for (int dd = 0; dd < DUAL; ++dd) brow[f * DUAL + dd] = B + (long)(dd ? N + n : n) * ((pk & PK_B) ? 32 : ldb) + fk;
   }
   // elements between k-steps of 32: row-major, or one packed slab of ldb rows
-  const long bstep = bpk ? (long)ldb * 32 : 32;
+  const long bstep = (pk & PK_B) ? (long)ldb * 32 : 32;
+  const long astep = (pk & PK_A) ? (long)lda * 32 : 32;
   const bf16_t* arow[MF];
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
     int m = 16 * i + fr;
     m = m < M ? m : M - 1;
-    arow[i] = A + (long)m * lda + fk;
+    arow[i] = A + (long)m * ((pk & PK_A) ? 32 : lda) + fk;
   }
   const int steps = K / 32;
   const int sper = (steps + splits - 1) / splits;       // k-steps of this workgroup's split
@@ -600,7 +610,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
       for (int j = 0; j < NB; ++j)
         bv[u][j] = __builtin_nontemporal_load((const bf16x8_t*)(brow[j] + (s + u) * bstep));
 #pragma unroll
-      for (int i = 0; i < MF; ++i) av[u][i] = *(const bf16x8_t*)(arow[i] + (s + u) * 32);
+      for (int i = 0; i < MF; ++i) av[u][i] = *(const bf16x8_t*)(arow[i] + (s + u) * astep);
     }
     // keep the scheduler from trading loads in flight for registers
     __builtin_amdgcn_sched_barrier(0);
@@ -652,7 +662,8 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
         const int row = 16 * i + er + r;
         if (row >= M) continue;
         if constexpr (EPI == EPI_SILU_MUL) {
-          Elem<OutT>::store((OutT*)Cv, (long)row * ldc + col, silu_f(acc[i][2 * f][r]) * acc[i][2 * f + 1][r]);
+          Elem<OutT>::store((OutT*)Cv, act_idx(row, col, ldc, (pk & PK_C) ? ldc : 0),
+                            silu_f(acc[i][2 * f][r]) * acc[i][2 * f + 1][r]);
         } else if constexpr (EPI == EPI_PARTIAL) {
           ((float*)Cv)[split * slice_stride + (long)row * ldc + col] = acc[i][f][r];
         } else {
@@ -696,44 +707,44 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
 
 template <int BM, int BN, int BK, int WM, int WN, int EPI>
 static void run_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
-                     hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
+                     hipStream_t st, int pk, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? BN / 2 : BN;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
   if (M <= BM)  // one row tile: each weight element is read once
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t, 1>), dim3((unsigned)tiles,
                        (unsigned)splits), dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M,
-                       N, K, Cv, ldc, splits, slice_stride, bpk);
+                       N, K, Cv, ldc, splits, slice_stride, pk);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t, 0>), dim3((unsigned)tiles,
                        (unsigned)splits), dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M,
-                       N, K, Cv, ldc, splits, slice_stride, bpk);
+                       N, K, Cv, ldc, splits, slice_stride, pk);
 }
 
 template <int EPI, int BM = 256>
 static void run_big(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
-                    hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
+                    hipStream_t st, int pk, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
   const dim3 grid((unsigned)tiles, (unsigned)splits);
   if (M <= BM) {  // one row tile: each weight slab is read once
     hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 1>), grid, dim3(256), 0, st, (const bf16_t*)A, lda,
-                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk);
   } else if constexpr (BM == 256) {
     // several row tiles: 8 wavefronts in two ping-pong groups (measured on
     // MI355X at 2048 rows of the 70B shape: QKV 383.6 -> 369.5, O 261 ->
     // 230.5, gate-up 1693 -> 1665, down 868 -> 847 us, the same bits; at one
     // row tile of 256 rows the gate-up projection lost 7%)
     hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 0, 8, 1>), grid, dim3(512), 0, st, (const bf16_t*)A, lda,
-                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk);
   } else {
     hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 0>), grid, dim3(256), 0, st, (const bf16_t*)A, lda,
-                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk);
   }
 }
 
 template <int MF, int NF, int NW, int EPI>
 static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* Cv, int ldc,
-                     hipStream_t st, int bpk, int splits = 1, long slice_stride = 0) {
+                     hipStream_t st, int pk, int splits = 1, long slice_stride = 0) {
   constexpr int NB = NF * (EPI == EPI_SILU_MUL ? 2 : 1);
   // k-steps in flight, as registers allow (1024-thread workgroups get 128
   // VGPRs per lane); with at most 3 fragments per k-step, 16 (192 VGPRs),
@@ -742,7 +753,7 @@ static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B,
   constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 3 ? 16 : ((MF + NB) <= 4 ? 8 : 4));
   const unsigned grid = (unsigned)((N + 16 * NF - 1) / (16 * NF) * splits);
   hipLaunchKernelGGL((gemv_bf16_kernel<MF, NF, NW, U, EPI, bf16_t>), dim3(grid), dim3(64 * NW), 0, st,
-                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, bpk);
+                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk);
 }
 
 // Tile shapes for M > 64 rows, largest first: 256 x 256 and 128 x 256 (the
@@ -753,8 +764,9 @@ constexpr int kTileCols[4] = {256, 256, 128, 64};
 constexpr int kFillTarget = 256;  // workgroups that fill the chip (one per CU)
 
 // The big kernel addresses its operands with 32-bit buffer offsets.
-static bool big_fits(int M, int lda, long b_rows, int ldb, int K, int bpk) {
-  return (long)M * lda * 2 < (1L << 32) && (bpk ? (long)K * ldb : b_rows * ldb) * 2 < (1L << 32);
+static bool big_fits(int M, int lda, long b_rows, int ldb, int K, int pk) {
+  const long a_span = (pk & PK_A) ? ((long)(K / 32 - 1) * lda + M) * 64 : (long)M * lda * 2;
+  return a_span < (1L << 32) && ((pk & PK_B) ? (long)K * ldb : b_rows * ldb) * 2 < (1L << 32);
 }
 
 // Output tiles of a launch; SwiGLU tiles hold gate and up columns, so they
@@ -809,8 +821,8 @@ int gemm_partial_splits(int M, int N, int K) {
 }
 
 int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* P, int ldp,
-                        long slice_stride, int splits, hipStream_t st, int b_packed) {
-  const int bpk = b_packed ? 1 : 0;
+                        long slice_stride, int splits, hipStream_t st, int pack) {
+  const int pk = pack & (PK_A | PK_B);  // the slices are fp32 row-major
   if (M <= 0 || N <= 0) return 0;
   if (K % 32 != 0 || splits < 1 || splits > K / 32) return -1;
   if (M <= 64) {
@@ -820,8 +832,8 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
     const bool nf2 = (long)((N + 31) / 32) * splits >= 256;
 #define NS_GEMV_PART(MF)                                                                             \
   do {                                                                                               \
-    if (nf2) run_gemv<MF, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride); \
-    else run_gemv<MF, 1, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);     \
+    if (nf2) run_gemv<MF, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, pk, splits, slice_stride); \
+    else run_gemv<MF, 1, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, pk, splits, slice_stride);     \
   } while (0)
     if (M <= 16) NS_GEMV_PART(1);
     else if (M <= 32) NS_GEMV_PART(2);
@@ -829,20 +841,20 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
 #undef NS_GEMV_PART
   } else {
     int kind = partial_plan(M, N, K).kind;
-    if ((kind == TILE_BIG || kind == TILE_BIG128) && !big_fits(M, lda, N, ldb, K, bpk)) kind = TILE_128;
-    if (kind == TILE_BIG) run_big<EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
+    if ((kind == TILE_BIG || kind == TILE_BIG128) && !big_fits(M, lda, N, ldb, K, pk)) kind = TILE_128;
+    if (kind == TILE_BIG) run_big<EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, pk, splits, slice_stride);
     else if (kind == TILE_BIG128)
-      run_big<EPI_PARTIAL, 128>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
+      run_big<EPI_PARTIAL, 128>(M, N, K, A, lda, B, ldb, P, ldp, st, pk, splits, slice_stride);
     else if (kind == TILE_128)
-      run_bf16<128, 128, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
+      run_bf16<128, 128, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, pk, splits, slice_stride);
     // Wide K slabs where every split still gets one: fewer slab syncs
     // (0.5B-shaped mix, down projection at 128 rows: 32-wide 18.5 us, 64-wide
     // 14.6 us, 128-wide 12.2 us)
     else if (K % 128 == 0 && K / 128 >= splits)
-      run_bf16<64, 64, 128, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
+      run_bf16<64, 64, 128, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, pk, splits, slice_stride);
     else if (K % 64 == 0 && K / 64 >= splits)
-      run_bf16<64, 64, 64, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
-    else run_bf16<64, 64, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, bpk, splits, slice_stride);
+      run_bf16<64, 64, 64, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, pk, splits, slice_stride);
+    else run_bf16<64, 64, 32, 2, 2, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, P, ldp, st, pk, splits, slice_stride);
   }
   return 0;
 }
@@ -855,28 +867,28 @@ int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void*
 // K-splitting wavefronts as the LDS for their partial sums allows (<= 64 KB).
 template <int MF, int EPI>
 static void dispatch_gemv_m(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C, int ldc,
-                            hipStream_t st, int bpk) {
+                            hipStream_t st, int pk) {
   constexpr int NB1 = EPI == EPI_SILU_MUL ? 2 : 1;
   constexpr int NW_LONG = (64 / (MF * NB1)) < 16 ? (64 / (MF * NB1)) : 16;
   const bool wide = (long)N / 64 >= 1024;
   if constexpr (EPI != EPI_SILU_MUL) {
     // measured on MI355X (LM head, N 151936, K 896; isolated and in the step)
     if (wide) {
-      if constexpr (MF == 1) return run_gemv<MF, 4, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-      else if constexpr (MF == 2) return run_gemv<MF, 8, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-      else return run_gemv<MF, 4, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+      if constexpr (MF == 1) return run_gemv<MF, 4, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+      else if constexpr (MF == 2) return run_gemv<MF, 8, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+      else return run_gemv<MF, 4, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
     }
   }
-  if (K > 2048) run_gemv<MF, 1, NW_LONG, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-  else run_gemv<MF, 1, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+  if (K > 2048) run_gemv<MF, 1, NW_LONG, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+  else run_gemv<MF, 1, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
 }
 
 template <int EPI>
 static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C, int ldc,
-                          hipStream_t st, int bpk) {
-  if (M <= 16) return dispatch_gemv_m<1, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-  if (M <= 32) return dispatch_gemv_m<2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-  if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+                          hipStream_t st, int pk) {
+  if (M <= 16) return dispatch_gemv_m<1, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+  if (M <= 32) return dispatch_gemv_m<2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+  if (M <= 64) return dispatch_gemv_m<4, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
   // M > 64: the tile shape with the best estimated throughput -- its
   // relative per-CU rate (measured on MI355X: the 256 x 256 kernel 1.0,
   // 128 x 256 about 0.72, 128 x 128 about 0.55, 64 x 64 about 0.35) times the
@@ -887,7 +899,7 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
   const long b_rows = (EPI == EPI_SILU_MUL) ? 2L * N : (long)N;
   constexpr double kRate[4] = {1.0, 0.72, 0.55, 0.35};
   constexpr long kSlots[4] = {256, 256, 512, 1024};
-  const bool fits = big_fits(M, lda, b_rows, ldb, K, bpk);
+  const bool fits = big_fits(M, lda, b_rows, ldb, K, pk);
   int kind = TILE_64;
   double best = -1.0;
   for (int k = (fits ? (M > 128 ? TILE_BIG : TILE_BIG128) : TILE_128); k <= TILE_64; ++k) {
@@ -901,11 +913,11 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
       kind = k;
     }
   }
-  if (kind == TILE_BIG) return run_big<EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-  if (kind == TILE_BIG128) return run_big<EPI, 128>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+  if (kind == TILE_BIG) return run_big<EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+  if (kind == TILE_BIG128) return run_big<EPI, 128>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
   if (kind == TILE_128) {
-    if (k64) run_bf16<128, 128, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-    else run_bf16<128, 128, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+    if (k64) run_bf16<128, 128, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+    else run_bf16<128, 128, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
   } else {
     constexpr int BN64 = (EPI == EPI_SILU_MUL) ? 128 : 64;
     // SwiGLU tiles that fit one wave of workgroups take 128-wide K slabs
@@ -913,9 +925,9 @@ static void dispatch_bf16(int M, int N, int K, const void* A, int lda, const voi
     // 0.5B shape 20.8 -> 16.8 us; with more tiles than CUs the second wave
     // costs more than that saves (256 rows: 21 -> 27 us)
     if (EPI == EPI_SILU_MUL && K % 128 == 0 && tile_count(TILE_64, M, N, false) <= kFillTarget)
-      run_bf16<64, BN64, 128, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-    else if (k64) run_bf16<64, BN64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
-    else run_bf16<64, BN64, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk);
+      run_bf16<64, BN64, 128, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+    else if (k64) run_bf16<64, BN64, 64, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
+    else run_bf16<64, BN64, 32, 2, 2, EPI>(M, N, K, A, lda, B, ldb, C, ldc, st, pk);
   }
 }
 
@@ -939,10 +951,12 @@ void launch_pack_kslab(const void* src, void* dst, int rows, int cols, hipStream
 }
 
 int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C,
-                int ldc, hipStream_t st, int b_packed) {
+                int ldc, hipStream_t st, int pack) {
   if (M <= 0 || N <= 0) return 0;
-  if (!gemm_supported(dtype, K) || (b_packed && dtype != NS_DT_BF16)) return -1;
-  const int bpk = b_packed ? 1 : 0;
+  if (!gemm_supported(dtype, K) || (pack && dtype != NS_DT_BF16)) return -1;
+  // a slab-major C needs whole 32-column slabs and only the SwiGLU epilogue writes bf16
+  if ((pack & PK_C) && (epi != EPI_SILU_MUL || N % 32 != 0)) return -1;
+  const int pk = pack;
   if (dtype == NS_DT_F32) {
     dim3 grid((N + 15) / 16, (M + 15) / 16);
     const float* a = (const float*)A;
@@ -956,9 +970,9 @@ int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda,
     return 0;
   }
   switch (epi) {
-    case EPI_STORE_F32: dispatch_bf16<EPI_STORE_F32>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk); break;
-    case EPI_RESID_F32: dispatch_bf16<EPI_RESID_F32>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk); break;
-    default: dispatch_bf16<EPI_SILU_MUL>(M, N, K, A, lda, B, ldb, C, ldc, st, bpk); break;
+    case EPI_STORE_F32: dispatch_bf16<EPI_STORE_F32>(M, N, K, A, lda, B, ldb, C, ldc, st, pk); break;
+    case EPI_RESID_F32: dispatch_bf16<EPI_RESID_F32>(M, N, K, A, lda, B, ldb, C, ldc, st, pk); break;
+    default: dispatch_bf16<EPI_SILU_MUL>(M, N, K, A, lda, B, ldb, C, ldc, st, pk); break;
   }
   return 0;
 }

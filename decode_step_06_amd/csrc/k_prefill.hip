@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(64 * G) attn_prefill_kernel(
     const bf16_t* __restrict__ qatt, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_bseq, const int32_t* __restrict__ row_pos,
     const int32_t* __restrict__ btab, bf16_t* __restrict__ out, int maxb, int row0, int n_rows, int nq, int nkv,
-    float scale_log2) {
+    float scale_log2, int osr) {
   constexpr int NCH = D / 8;   // 16-byte chunks per head row
   constexpr int KS = D / 16;   // MFMA steps over d
   constexpr int DT = D / 32;   // 32-wide d tiles of the output
@@ -157,7 +157,6 @@ __global__ void __launch_bounds__(64 * G) attn_prefill_kernel(
   }
   // lane: query q, d = 32 j + 8 (e / 4) + 4 hl + e % 4
   const float inv = 1.f / l;
-  bf16_t* op = out + (long)(t0 + q) * nq * D + (long)(g * G + hh) * D;
 #pragma unroll
   for (int j = 0; j < DT; ++j)
 #pragma unroll
@@ -166,7 +165,8 @@ __global__ void __launch_bounds__(64 * G) attn_prefill_kernel(
       uint2 w;
       w.x = pack_bf16(o[j][4 * e4] * inv, o[j][4 * e4 + 1] * inv);
       w.y = pack_bf16(o[j][4 * e4 + 2] * inv, o[j][4 * e4 + 3] * inv);
-      *(uint2*)(op + d0) = w;
+      // 4 consecutive columns from a multiple of 4: one slab piece
+      *(uint2*)(out + act_idx(t0 + q, (g * G + hh) * D + d0, nq * D, osr)) = w;
     }
 }
 
@@ -183,7 +183,7 @@ void launch_attention_prefill(const AttnArgs& a, hipStream_t st) {
   if (a.d == DD && G == GG) {                                                                                   \
     hipLaunchKernelGGL((attn_prefill_kernel<DD, GG>), grid, dim3(64 * GG), 0, st, (const bf16_t*)a.q_att,      \
                        (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.row_seq, a.row_bseq, a.row_pos, a.btab,     \
-                       (bf16_t*)a.out, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, scale_log2);                     \
+                       (bf16_t*)a.out, a.maxb, a.row0, a.n_rows, a.nq, a.nkv, scale_log2, a.out_slab_rows);                     \
     return;                                                                                                     \
   }
   NS_PF(64, 1) NS_PF(64, 2) NS_PF(64, 4) NS_PF(64, 7) NS_PF(64, 8)

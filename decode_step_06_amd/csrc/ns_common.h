@@ -48,6 +48,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 // Element storage type helpers: T is float or bf16_t.
+// Element (row, col) of a bf16 activation matrix: row-major with row stride
+// ld when slab_rows == 0; otherwise K-slab-major, the layout of the
+// projection weights: each 32-wide column slab is a contiguous [slab_rows][32]
+// block, so that a GEMM's load of 16 rows of one slab reads 1 KB contiguous.
+__device__ __forceinline__ long act_idx(int row, int col, int ld, int slab_rows) {
+  return slab_rows ? ((long)(col >> 5) * slab_rows + row) * 32 + (col & 31) : (long)row * ld + col;
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int per16 = 4;  // elements per 16-byte chunk

@@ -19,13 +19,20 @@ enum GemmEpi {
   EPI_PARTIAL = 3,    // C fp32 slice s [M, N] = acc over the s-th K range (split K, decode batches)
 };
 
+// Operand layouts (bf16 only), a bit mask:
+//  PK_B: B is stored K-slab-major, element (n, k) at ((k / 32) * ldb + n) * 32
+//        + k % 32 with ldb = B's row count (N, or 2N for SwiGLU), so each
+//        32-wide K slab of every row is one 64-byte piece of a contiguous
+//        [rows][32] block; otherwise row-major with row stride ldb.
+//  PK_A: A is K-slab-major the same way, lda = the rows of each slab block
+//        (at least M; A may point at a row inside the block).
+//  PK_C: the SwiGLU epilogue's bf16 C is written K-slab-major, ldc = the
+//        rows of each slab block (N % 32 == 0).
+enum GemmPack { PK_B = 1, PK_A = 2, PK_C = 4 };
+
 // Returns 0, or -1 when the shape is unsupported (K % 32 != 0 for bf16).
-// b_packed (bf16 only): B is stored K-slab-major, element (n, k) at
-// ((k / 32) * ldb + n) * 32 + k % 32 with ldb = B's row count (N, or 2N for
-// SwiGLU), so each 32-wide K slab of every row is one 64-byte piece of a
-// contiguous [rows][32] block; otherwise row-major with row stride ldb.
 int launch_gemm(int dtype, int epi, int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C,
-                int ldc, hipStream_t st, int b_packed = 0);
+                int ldc, hipStream_t st, int pack = 0);
 int gemm_supported(int dtype, int K);
 
 // Split-K projection (bf16): slice s of the result (P + s * slice_stride,
@@ -36,14 +43,17 @@ int gemm_supported(int dtype, int K);
 // is accepted.  Returns -1 for unsupported shapes.
 int gemm_partial_splits(int M, int N, int K);
 int launch_gemm_partial(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* P, int ldp,
-                        long slice_stride, int splits, hipStream_t st, int b_packed = 0);
+                        long slice_stride, int splits, hipStream_t st, int pack = 0);
 // Row-major bf16 [rows, cols] -> K-slab-major (cols % 32 == 0).
 void launch_pack_kslab(const void* src, void* dst, int rows, int cols, hipStream_t st);
 
 void launch_embed(int dtype, const void* E, const int32_t* tok, float* x, int T, int H, int V, hipStream_t st);
 void launch_copy_rows(const float* src, float* dst, long n, hipStream_t st);
 void launch_rope_table(const int32_t* pos, float* cosb, float* sinb, int T, int d, float base, hipStream_t st);
-void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st);
+// h_slab_rows: 0 = h row-major [T, H]; otherwise h is K-slab-major with that
+// many rows per slab block (see act_idx), h pointing at the first row.
+void launch_rmsnorm(int dtype, const float* x, const void* g, void* h, int T, int H, float eps, hipStream_t st,
+                    int h_slab_rows = 0);
 // tokens out[r] = argmax of row r of fp32 logits [n_rows, V] (lowest index
 // among equal maxima, NaN never wins, a row of NaN only gives 0)
 void launch_argmax_rows(const float* logits, int n_rows, int V, int32_t* out, hipStream_t st);
@@ -52,7 +62,7 @@ void launch_read_stream(const void* src, long n16, uint32_t* sink, hipStream_t s
 // x[t] += sum_s P[s][t] (slice order; the split-K residual add of the
 // previous projection), written back to x, then RMSNorm into h.
 void launch_rmsnorm_reduce(int dtype, float* x, const float* P, long slice_stride, int splits, const void* g,
-                           void* h, int T, int H, float eps, hipStream_t st);
+                           void* h, int T, int H, float eps, hipStream_t st, int h_slab_rows = 0);
 // out[t] = x[t] + sum_s P[s][t]  (the last layer's residual add, fp32 out)
 void launch_reduce_rows(const float* x, const float* P, long slice_stride, int splits, float* out, int T, int H,
                         hipStream_t st);
@@ -62,7 +72,7 @@ void launch_reduce_rows(const float* x, const float* P, long slice_stride, int s
 // null).
 void launch_step_prologue(int dtype, const void* E, const int32_t* tok, float* x, const int32_t* pos, float* cosb,
                           float* sinb, const void* g0, void* h, int T, int H, int V, int d, float base, float eps,
-                          int32_t* bad_tok, hipStream_t st);
+                          int32_t* bad_tok, hipStream_t st, int h_slab_rows = 0);
 // qkv holds `splits` fp32 slices (slice_stride apart) that are summed first.
 void launch_rope_kv(int dtype, const float* qkv, long slice_stride, int splits, const float* cosb,
                     const float* sinb, const int32_t* slot, void* q_att, void* kc, void* vc, int T, int nq, int nkv,
@@ -83,7 +93,7 @@ struct AttnArgs {
   const int32_t* row_pos;   // [T]
   const int32_t* btab;      // [n_bseq][maxb]
   int maxb;
-  void* out;                // [T][nq * d] (dtype)
+  void* out;                // [T][nq * d] (dtype), or K-slab-major when out_slab_rows > 0 (bf16)
   float* part_acc;          // [T * nkv * n_parts][G][d]
   float* part_ml;           // [T * nkv * n_parts][G][2]
   int row0, n_rows;
@@ -109,6 +119,9 @@ struct AttnArgs {
   // bf16 matrix-core kernel: K/V loads non-temporal (for launches that
   // stream hundreds of MB; see the kernel)
   bool kv_nt = false;
+  // bf16 kernels: out is K-slab-major with this many rows per slab block
+  // (see act_idx), indexed by absolute row; 0 = row-major
+  int out_slab_rows = 0;
 };
 int attention_supported(int dtype, int d, int G);
 // Rows are taken in tiles of 32 from row0; a tile of one sequence at
