@@ -35,9 +35,11 @@ on, behind a queued busy-wait kernel so host launch gaps do not count):
 from __future__ import annotations
 
 import argparse
+import faulthandler
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -986,6 +988,32 @@ def dense_rooflines(d):
                 "clock_during_gate_up_gemm": d.get("clock_during_gate_up_gemm")}}
 
 
+def dense_leg_isolated():
+    """The dense-batch leg in a child process of its own.  Once, in a run of
+    several legs, the leg ended the process with a host segmentation fault
+    (no GPU fault reported, cause not found); run apart, such a crash costs
+    this leg's entries instead of the whole line.  The child's log and any
+    fault trace go to this process's stderr; its JSON comes back on stdout."""
+    return run_child_leg([sys.executable, os.path.abspath(__file__), "--child-leg", "dense"], "dense-batch")
+
+
+def run_child_leg(cmd, name, timeout=1200):
+    """Run `cmd` as a child process and return the JSON object on the last
+    line of its stdout, or {"error": ...} when it times out, exits with a
+    nonzero status (a signal shows as a negative one) or prints no JSON."""
+    try:
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=timeout)
+    except subprocess.TimeoutExpired:
+        return {"error": f"{name} child process timed out after {timeout} s"}
+    if r.returncode != 0:
+        return {"error": f"{name} child process exited with status {r.returncode}"}
+    try:
+        out = json.loads(r.stdout.strip().splitlines()[-1])
+    except (IndexError, ValueError) as e:
+        return {"error": f"{name} child process printed no result: {e!r}"}
+    return out if isinstance(out, dict) else {"error": f"{name} child process printed a non-object"}
+
+
 def _small_legs(args, stream, result):
     """The 0.5B-shaped step at 32 rows (then at 1 row with the 'b1' leg), and
     the batch sweep and bucketed capture over its weights."""
@@ -1020,7 +1048,9 @@ def main():
     ap.add_argument("--legs", default="headline,small,b1,sweep,dense,cpu",
                     help="comma list of legs to run (profiling runs take one); without 'headline' the line "
                          "carries only the legs run and no value")
+    ap.add_argument("--child-leg", choices=["dense"], default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    faulthandler.enable()  # a native crash prints the Python frames it happened under
     legs = set(args.legs.split(","))
     args.no_small = args.no_small or "small" not in legs
     args.no_b1 = "b1" not in legs
@@ -1043,6 +1073,9 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    if args.child_leg == "dense":  # run by dense_leg_isolated
+        print(json.dumps(_rounded(_leg(dense_batch, stream)), default=_jsonable), flush=True)
+        return
     if "headline" not in legs:
         result = {"metric": "decode tokens/s @1 GPU; attn HBM GB/s and GEMM MFMA % of peak", "value": None,
                   "legs": sorted(legs)}
@@ -1120,7 +1153,8 @@ def main():
     del r
     _small_legs(args, stream, result)
     if not args.no_dense:
-        result["dense_batch"] = _rounded(_leg(dense_batch, stream))
+        torch.cuda.empty_cache()
+        result["dense_batch"] = _rounded(dense_leg_isolated())
         result.update(dense_rooflines(result["dense_batch"]))
     result["torch_copy_rate"] = _rounded(copy_ceiling(stream))
     result["hbm_read_ceiling"] = _rounded(read_ceiling(stream))

@@ -1,7 +1,10 @@
 """Host logic of the benchmark that runs without a GPU: the sizing of the
 co-run interference profile (how many attention launches keep the second
-stream busy as long as the projections keep the first) and its caps, and the
-dense-batch roofline entries built from the dense leg's results."""
+stream busy as long as the projections keep the first) and its caps, the
+dense-batch roofline entries built from the dense leg's results, and the
+runner of a leg in a child process."""
+import sys
+
 import pytest
 
 import bench
@@ -32,3 +35,18 @@ def test_dense_rooflines_from_the_dense_leg():
     assert (g["bound"], g["unit"], g["frac"], g["peak"]) == ("mfma", "TFLOP/s", 0.428, 2500.0)
     assert g["per_projection_us"] == {"qkv_proj": 386.0, "o_proj": 263.0}
     assert bench.dense_rooflines({"error": "x"}) == {}
+
+
+def test_child_leg_result_and_failures_are_reported():
+    """The isolated leg's runner: the child's last stdout line is the result;
+    a crash (a signal), a nonzero exit, silence or a time-out become an error
+    entry instead of ending the benchmark (CPU-only child processes)."""
+    py = sys.executable
+    ok = bench.run_child_leg([py, "-c", "print('log line'); print('{\"a\": 1}')"], "t")
+    assert ok == {"a": 1}
+    crash = bench.run_child_leg([py, "-c", "import os, signal; os.kill(os.getpid(), signal.SIGSEGV)"], "t")
+    assert "status -11" in crash["error"]
+    assert "status 3" in bench.run_child_leg([py, "-c", "import sys; sys.exit(3)"], "t")["error"]
+    assert "no result" in bench.run_child_leg([py, "-c", "print('not json')"], "t")["error"]
+    assert "non-object" in bench.run_child_leg([py, "-c", "print('[1, 2]')"], "t")["error"]
+    assert "timed out" in bench.run_child_leg([py, "-c", "import time; time.sleep(5)"], "t", timeout=0.5)["error"]
