@@ -91,6 +91,11 @@ struct Plan {
   size_t meta_ints;  // int32 entries of the metadata block
 };
 
+// Rows of a slab block of the K-slab-major bf16 activations (see
+// act_slab_rows): the capacity rounded up to an odd count, so that
+// consecutive blocks do not start at the same offset modulo a power of two.
+int slab_rows(int max_tokens) { return max_tokens | 1; }
+
 Plan make_plan(const ns_model_desc* d, int T, int maxb) {
   Plan p{};
   const size_t es = elem_size(d->dtype);
@@ -102,11 +107,12 @@ Plan make_plan(const ns_model_desc* d, int T, int maxb) {
     return o;
   };
   p.x = take((size_t)T * d->hidden * 4);
-  p.h = take((size_t)T * d->hidden * es);
+  // the bf16 projections' inputs: slab blocks of slab_rows(T) rows
+  p.h = take((size_t)slab_rows(T) * d->hidden * es);
   p.qkv = take((size_t)T * (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim * 4);
   p.q_att = take((size_t)T * d->n_q_heads * d->head_dim * es);
-  p.o = take((size_t)T * d->n_q_heads * d->head_dim * es);
-  p.act = take((size_t)T * d->ffn * es);
+  p.o = take((size_t)slab_rows(T) * d->n_q_heads * d->head_dim * es);
+  p.act = take((size_t)slab_rows(T) * d->ffn * es);
   p.cosb = take((size_t)T * d->head_dim / 2 * 4);
   p.sinb = take((size_t)T * d->head_dim / 2 * 4);
   p.meta_ints = 5 * (size_t)T + (size_t)T * maxb;
@@ -383,7 +389,13 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, const ns_sched& sc, h
 // 16-row load of one slab reads 1 KB contiguous instead of 16 separate 64-byte
 // pieces (80-layer 70B-shaped step, a timing probe of the GEMMs alone:
 // 54.5 -> 53.3 ms).  fp32 models stay row-major.
-int act_slab_rows(const ns_engine* e) { return e->d.dtype == NS_BF16 ? e->max_tokens : 0; }
+// Steps of at most kPackMinRows rows keep them row-major: their projections
+// load one 16-row fragment per k-step, which the layout cannot widen, and the
+// loads keep their constant offsets.
+constexpr int kPackMinRows = 16;
+int act_slab_rows(const ns_engine* e, int n_tok) {
+  return e->d.dtype == NS_BF16 && n_tok > kPackMinRows ? slab_rows(e->max_tokens) : 0;
+}
 
 void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::AttnArgs* a) {
   a->dtype = e->d.dtype == NS_BF16 ? NS_DT_BF16 : NS_DT_F32;
@@ -407,7 +419,7 @@ void attn_args(const ns_engine* e, int layer, int r0, int r1, int n_tok, ns::Att
   a->wg_cap = e->sched.attn_wg_cap;
   a->row_seq = e->sched.prefill_tiles ? e->m_seq() : nullptr;
   a->kv_nt = e->kv_layer >= kKvStreamBytes;
-  a->out_slab_rows = act_slab_rows(e);
+  a->out_slab_rows = act_slab_rows(e, n_tok);
   if (attn_row_order(e, r1 - r0, (long)a->nkv * a->n_parts) != kOrderNone) a->row_order = e->m_order();
 }
 
@@ -452,7 +464,7 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   // embedding (or the hidden input already in x), RoPE table, layer 0's norm
   ns::launch_step_prologue(dt, d.vocab > 0 ? e->embed : nullptr, e->m_tok(), e->x(), e->m_pos(), e->cosb(),
                            e->sinb(), e->attn_norm[0], e->h(), n_tok, H, d.vocab, hd, d.rope_base, d.rms_eps,
-                           e->bad_tok(), st, act_slab_rows(e));
+                           e->bad_tok(), st, act_slab_rows(e, n_tok));
   ++launches;
   MARK(K_EMBED);
 
@@ -461,7 +473,7 @@ int enqueue_step(ns_engine* e, const ns_sched& sc, int n_tok, void* out, hipStre
   char* act = (char*)e->act();
   // activation rows from r0 of a `width`-column matrix, its leading
   // dimension for the GEMMs, and their layout flag
-  const int ar = act_slab_rows(e);
+  const int ar = act_slab_rows(e, n_tok);
   auto arow = [&](char* buf, int r0, int width) { return buf + (ar ? (size_t)r0 * 32 : (size_t)r0 * width) * es; };
   auto ald = [&](int width) { return ar ? ar : width; };
   const int apk = ar ? ns::PK_A : 0;

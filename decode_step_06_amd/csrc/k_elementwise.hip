@@ -134,8 +134,10 @@ __device__ __forceinline__ void rmsnorm_reduce_row(float* __restrict__ xr, const
   for (int c = 0; c < CH; ++c) {
     const int i4 = threadIdx.x + c * NT;
     if (i4 < H4) {
+      // 4 consecutive columns from a multiple of 4: consecutive in either layout
+      const long o = act_idx(t, 4 * i4, H, hs);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Elem<T>::store(h, act_idx(t, 4 * i4 + e, H, hs), v[c][e] * r * gv[c][e]);
+      for (int e = 0; e < 4; ++e) Elem<T>::store(h, o + e, v[c][e] * r * gv[c][e]);
     }
   }
 }
@@ -195,9 +197,9 @@ __global__ void __launch_bounds__(NT) rmsnorm_reduce_wide_kernel(float* __restri
   for (int c = 0; c < CH; ++c) {
     const int i4 = threadIdx.x + c * NT;
     if (i4 < H4) {
+      const long o = act_idx(t, 4 * i4, H, hs);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Elem<T>::store(h, act_idx(t, 4 * i4 + e, H, hs), v[c][e] * r * Elem<T>::load(g, 4 * i4 + e));
+      for (int e = 0; e < 4; ++e) Elem<T>::store(h, o + e, v[c][e] * r * Elem<T>::load(g, 4 * i4 + e));
     }
   }
 }

@@ -48,8 +48,10 @@ struct GemmCfg {
 }  // namespace
 
 // BNT: B loads are non-temporal (one row tile covers all M rows, so each B
-// element is read by one workgroup).
-template <int BM, int BN, int BK, int WM, int WN, int EPI, typename OutT, int BNT = 0>
+// element is read by one workgroup).  LAY: bit 0, A is K-slab-major (PK_A);
+// bit 1, the SwiGLU output is (PK_C) -- template parameters so that the
+// row-major addresses stay the plain ones.
+template <int BM, int BN, int BK, int WM, int WN, int EPI, typename OutT, int BNT = 0, int LAY = 0>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                                  const bf16_t* __restrict__ B, int ldb, int M, int N,
                                                                  int K, void* __restrict__ Cv, int ldc, int splits,
@@ -91,8 +93,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
       const int c = tid + i * C::NT;
       if (c < C::A_CH) {
         const int r = c / (BK / 8), k = k0 + (c % (BK / 8)) * 8;
-        ra[i] = *(const u32x4_t*)(A + ((pk & PK_A) ? ((long)(k >> 5) * lda + a_row(r)) * 32 + (k & 31)
-                                                   : (long)a_row(r) * lda + k));
+        ra[i] = *(const u32x4_t*)(A + ((LAY & 1) ? ((long)(k >> 5) * lda + a_row(r)) * 32 + (k & 31)
+                                                 : (long)a_row(r) * lda + k));
       }
     }
 #pragma unroll
@@ -185,7 +187,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_bf16_kernel(const bf16_t* _
         for (int r = 0; r < 4; ++r) {
           const int row = m0 + wm * C::TM + 16 * i + er + r;
           if (row < M)
-            Elem<OutT>::store(Cp, act_idx(row, col, ldc, (pk & PK_C) ? ldc : 0),
+            Elem<OutT>::store(Cp, act_idx(row, col, ldc, (LAY & 2) ? ldc : 0),
                               silu_f(acc[i][j][r]) * acc[i][j + HF][r]);
         }
       }
@@ -554,7 +556,7 @@ __global__ void __launch_bounds__(64 * NWV) gemm_big_kernel(const bf16_t* __rest
 // `splits` contiguous K ranges and stores its fp32 partial tile to slice s
 // (C + s * slice_stride); the kernel that next reads these rows sums the
 // slices in slice order, so no workgroups ever wait on each other.
-template <int MF, int NF, int NW, int U, int EPI, typename OutT>
+template <int MF, int NF, int NW, int U, int EPI, typename OutT, int LAY = 0>
 __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                             const bf16_t* __restrict__ B, int ldb, int M, int N,
                                                             int K, void* __restrict__ Cv, int ldc, int splits,
@@ -577,13 +579,15 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
   }
   // elements between k-steps of 32: row-major, or one packed slab of ldb rows
   const long bstep = (pk & PK_B) ? (long)ldb * 32 : 32;
-  const long astep = (pk & PK_A) ? (long)lda * 32 : 32;
+  // A K-slab-major (LAY bit 0): a k-step moves one slab block; row-major:
+  // 32 elements (a constant, so the loads keep immediate offsets)
+  const long astep = (LAY & 1) ? (long)lda * 32 : 32;
   const bf16_t* arow[MF];
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
     int m = 16 * i + fr;
     m = m < M ? m : M - 1;
-    arow[i] = A + (long)m * ((pk & PK_A) ? 32 : lda) + fk;
+    arow[i] = A + (long)m * ((LAY & 1) ? 32 : lda) + fk;
   }
   const int steps = K / 32;
   const int sper = (steps + splits - 1) / splits;       // k-steps of this workgroup's split
@@ -662,7 +666,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_bf16_kernel(const bf16_t* __rest
         const int row = 16 * i + er + r;
         if (row >= M) continue;
         if constexpr (EPI == EPI_SILU_MUL) {
-          Elem<OutT>::store((OutT*)Cv, act_idx(row, col, ldc, (pk & PK_C) ? ldc : 0),
+          Elem<OutT>::store((OutT*)Cv, act_idx(row, col, ldc, (LAY & 2) ? ldc : 0),
                             silu_f(acc[i][2 * f][r]) * acc[i][2 * f + 1][r]);
         } else if constexpr (EPI == EPI_PARTIAL) {
           ((float*)Cv)[split * slice_stride + (long)row * ldc + col] = acc[i][f][r];
@@ -710,14 +714,35 @@ static void run_bf16(int M, int N, int K, const void* A, int lda, const void* B,
                      hipStream_t st, int pk, int splits = 1, long slice_stride = 0) {
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? BN / 2 : BN;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
-  if (M <= BM)  // one row tile: each weight element is read once
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t, 1>), dim3((unsigned)tiles,
-                       (unsigned)splits), dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M,
-                       N, K, Cv, ldc, splits, slice_stride, pk);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t, 0>), dim3((unsigned)tiles,
-                       (unsigned)splits), dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M,
-                       N, K, Cv, ldc, splits, slice_stride, pk);
+#define NS_TILE_LAUNCH(BNT_, LAY_)                                                                             \
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, EPI, bf16_t, BNT_, LAY_>),                           \
+                     dim3((unsigned)tiles, (unsigned)splits), dim3(64 * WM * WN), 0, st, (const bf16_t*)A, lda, \
+                     (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk)
+  // one row tile: each weight element is read once (non-temporal B); the
+  // SwiGLU output's layout only exists for that epilogue
+  const int lay = ((pk & PK_A) ? 1 : 0) | ((EPI == EPI_SILU_MUL && (pk & PK_C)) ? 2 : 0);
+  if (M <= BM) {
+    if constexpr (EPI == EPI_SILU_MUL) {
+      if (lay == 3) NS_TILE_LAUNCH(1, 3);
+      else if (lay == 2) NS_TILE_LAUNCH(1, 2);
+      else if (lay == 1) NS_TILE_LAUNCH(1, 1);
+      else NS_TILE_LAUNCH(1, 0);
+    } else {
+      if (lay & 1) NS_TILE_LAUNCH(1, 1);
+      else NS_TILE_LAUNCH(1, 0);
+    }
+  } else {
+    if constexpr (EPI == EPI_SILU_MUL) {
+      if (lay == 3) NS_TILE_LAUNCH(0, 3);
+      else if (lay == 2) NS_TILE_LAUNCH(0, 2);
+      else if (lay == 1) NS_TILE_LAUNCH(0, 1);
+      else NS_TILE_LAUNCH(0, 0);
+    } else {
+      if (lay & 1) NS_TILE_LAUNCH(0, 1);
+      else NS_TILE_LAUNCH(0, 0);
+    }
+  }
+#undef NS_TILE_LAUNCH
 }
 
 template <int EPI, int BM = 256>
@@ -752,8 +777,21 @@ static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B,
   // k-steps) is one round of loads
   constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 3 ? 16 : ((MF + NB) <= 4 ? 8 : 4));
   const unsigned grid = (unsigned)((N + 16 * NF - 1) / (16 * NF) * splits);
-  hipLaunchKernelGGL((gemv_bf16_kernel<MF, NF, NW, U, EPI, bf16_t>), dim3(grid), dim3(64 * NW), 0, st,
-                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk);
+#define NS_GEMV_LAUNCH(LAY_)                                                                             \
+  hipLaunchKernelGGL((gemv_bf16_kernel<MF, NF, NW, U, EPI, bf16_t, LAY_>), dim3(grid), dim3(64 * NW), 0, st, \
+                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk)
+  // the SwiGLU output's layout only exists for that epilogue
+  const int lay = ((pk & PK_A) ? 1 : 0) | ((EPI == EPI_SILU_MUL && (pk & PK_C)) ? 2 : 0);
+  if constexpr (EPI == EPI_SILU_MUL) {
+    if (lay == 3) NS_GEMV_LAUNCH(3);
+    else if (lay == 2) NS_GEMV_LAUNCH(2);
+    else if (lay == 1) NS_GEMV_LAUNCH(1);
+    else NS_GEMV_LAUNCH(0);
+  } else {
+    if (lay & 1) NS_GEMV_LAUNCH(1);
+    else NS_GEMV_LAUNCH(0);
+  }
+#undef NS_GEMV_LAUNCH
 }
 
 // Tile shapes for M > 64 rows, largest first: 256 x 256 and 128 x 256 (the
