@@ -319,23 +319,61 @@ def attention_isolated(h, b, maxb, stream, n=400):
     return {"us": t * 1e6, "bytes": nbytes, "gbs": nbytes / t / 1e9, "launches": n * 3 + 20}
 
 
+def step_slab_rows(rows):
+    """Rows of a slab block of a bf16 step's activations for an engine of
+    `rows` rows (odd, at least rows), and whether a step of that many rows
+    keeps them K-slab-major (more than 16 rows) -- the engine's choices."""
+    return rows | 1, rows > 16
+
+
+def slab_input(A):
+    """A [M, K] bf16 input in the layout a step of M rows gives its
+    projections: (tensor, rows per slab block), K-slab-major with an odd block
+    of rows above 16 rows, else row-major (rows per block 0)."""
+    M, K = A.shape
+    r, packed = step_slab_rows(M)
+    if not packed:
+        return A.contiguous(), 0
+    pad = torch.cat([A, torch.zeros((r - M, K), dtype=A.dtype, device=A.device)])
+    out = torch.empty_like(pad)
+    ns.ns_pack_weight(pad.data_ptr(), out.data_ptr(), r, K)
+    return out, r
+
+
+def step_gemm(epi, M, N, K, A_in, B, C, stream):
+    """One projection launch in the step's layouts: A_in from slab_input, B
+    the engine's K-slab-major weights, C fp32 [M, N] (store / residual) or,
+    for SwiGLU, a bf16 buffer of slab_output's size."""
+    A, a_rows = A_in
+    if a_rows:
+        ns.ns_op_gemm_slab(epi, M, N, K, A.data_ptr(), a_rows, B, C.data_ptr(), a_rows, stream)
+    else:
+        ns.ns_op_gemm_packed(ns.NS_BF16, epi, M, N, K, A.data_ptr(), B, C.data_ptr(), stream)
+
+
+def slab_output(M, N):
+    """A bf16 SwiGLU output buffer large enough for step_gemm's layout."""
+    r, packed = step_slab_rows(M)
+    return torch.empty(((N + 31) // 32 * 32 * (r if packed else M),), device="cuda", dtype=torch.bfloat16)
+
+
 def gate_up_isolated(h, b, stream, n=400):
     """The step's gate-up projection (the layers' K-slab-major weights in
-    turn, a [rows, H] bf16 input, the SwiGLU epilogue: the same kernel and
-    launch shape as in the step) launched n times back to back on `stream`."""
+    turn, a [rows, H] bf16 input and the SwiGLU output in the layouts the step
+    keeps them in: the same kernel and launch shape as in the step) launched
+    n times back to back on `stream`."""
     s = h.shape
     T, H, F = b.n_rows, s.hidden, s.ffn
     g = torch.Generator(device="cuda")
     g.manual_seed(6)
-    A = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
-    C = torch.empty((T, F), device="cuda", dtype=torch.bfloat16)
+    A = slab_input(torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16))
+    C = slab_output(T, F)
     # the launches cycle through the layers' weights (as the step does), so
     # they stream from HBM rather than from the last-level cache
     wgu = [lw["wgu"].data_ptr() for lw in h.weights.t["layers"]]
 
     def launch(i):
-        ns.ns_op_gemm_packed(ns.NS_BF16, ns.NS_EPI_SILU, T, F, H, A.data_ptr(), wgu[i % len(wgu)], C.data_ptr(),
-                             stream)
+        step_gemm(ns.NS_EPI_SILU, T, F, H, A, wgu[i % len(wgu)], C, stream)
 
     for i in range(20):
         launch(i)
@@ -537,10 +575,11 @@ def dense_batch(stream, steps=10):
                                        ("o_proj", ns.NS_EPI_RESID, H, DQ, lw["wo"], C32),
                                        ("gate_up_proj", ns.NS_EPI_SILU, F, H, lw["wgu"], Cb),
                                        ("down_proj", ns.NS_EPI_RESID, H, F, lw["wdown"], C32)):
-            Ak = A[:, :K].contiguous()
-            # the engine's weights (K-slab-major), as the step reads them
-            t = time_launches(lambda i: ns.ns_op_gemm_packed(ns.NS_BF16, epi, T, N, K, Ak.data_ptr(), Bw.data_ptr(),
-                                                             C.data_ptr(), stream), 5, stream)
+            # the engine's weights (K-slab-major) and the step's layouts of
+            # the input and the SwiGLU output, as the step runs them
+            Ak = slab_input(A[:, :K])
+            Ck = slab_output(T, N) if epi == ns.NS_EPI_SILU else C
+            t = time_launches(lambda i: step_gemm(epi, T, N, K, Ak, Bw.data_ptr(), Ck, stream), 5, stream)
             fl = rf.gemm_flops(T, N, K, epi == ns.NS_EPI_SILU)
             gem[name] = dict(us=t * 1e6, tflops=fl / t / 1e12, frac=fl / t / 1e12 / rf.BF16_PEAK_TFLOPS)
         tot_fl = sum(rf.gemm_flops(T, N, K, sw) for N, K, sw in ((s.qkv_dim, H, False), (H, DQ, False),
@@ -1117,6 +1156,11 @@ def main():
                  "hbm_gbs": round(gu["gbs"], 1), "hbm_frac": round(gu["gbs"] / rf.HBM_PEAK_GBS, 4),
                  "flops_per_launch": gfl, "bytes_per_launch": gu["bytes"], "avg_launch_us": round(gu["us"], 3),
                  "isolated_launches": gu["launches"],
+                 # back-to-back launches hold the matrix cores busy without a
+                 # pause and run at a lower clock than the step's, where the
+                 # memory-bound kernels come between them
+                 "in_step_event_interval_us": round(kern["gate_up_proj"]["us_per_launch"], 3),
+                 "in_step_tflops": round(gfl / (kern["gate_up_proj"]["us_per_launch"] * 1e-6) / 1e12, 1),
                  "share_of_step": round(kern["gate_up_proj"]["us_per_step"] / tot, 3)}
     result = {
         "metric": "decode tokens/s @1 GPU; attn HBM GB/s and GEMM MFMA % of peak",

@@ -1045,6 +1045,25 @@ int ns_op_gemm_packed(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t 
   return op_gemm(dtype, epi, M, N, K, A, B, C, stream, true);
 }
 
+int ns_op_gemm_slab(int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, int32_t a_rows, const void* B,
+                    void* C, int32_t c_rows, void* stream) {
+  if (epi < 0 || epi > 2) NS_FAIL(NS_EINVAL, "bad epilogue");
+  if (M < 0 || N < 0 || K <= 0) NS_FAIL(NS_EINVAL, "bad sizes");
+  if (M == 0 || N == 0) return NS_OK;
+  if (!A || !B || !C) NS_FAIL(NS_EINVAL, "null matrix");
+  if (K % 32 != 0) NS_FAIL(NS_ESHAPE, "K = %d unsupported (the slab layouts need K %% 32 == 0)", K);
+  if (a_rows < M) NS_FAIL(NS_EINVAL, "a_rows %d is less than M %d", a_rows, M);
+  const bool slab_c = epi == NS_EPI_SILU;
+  if (slab_c && (N % 32 != 0 || c_rows < M))
+    NS_FAIL(NS_EINVAL, "a slab-major SwiGLU output needs N %% 32 == 0 and c_rows >= M");
+  const int b_rows = epi == NS_EPI_SILU ? 2 * N : N;
+  if (ns::launch_gemm(NS_DT_BF16, epi, M, N, K, A, a_rows, B, b_rows, C, slab_c ? c_rows : N, (hipStream_t)stream,
+                      ns::PK_A | ns::PK_B | (slab_c ? ns::PK_C : 0)))
+    NS_FAIL(NS_ESHAPE, "unsupported shape");
+  HIP_TRY(hipGetLastError());
+  return NS_OK;
+}
+
 int ns_op_rmsnorm(int32_t dtype, int32_t n_rows, int32_t hidden, const float* x, const void* gain, float eps, void* out,
                   void* stream) {
   if (dtype != NS_F32 && dtype != NS_BF16) NS_FAIL(NS_EINVAL, "bad dtype");

@@ -92,6 +92,7 @@ SIGNATURES = {
     "ns_engine_profile_read": (C.c_int, [_P, _I, _PI, C.POINTER(C.c_float), _PI]),
     "ns_op_gemm": (C.c_int, [_I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "ns_op_gemm_packed": (C.c_int, [_I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "ns_op_gemm_slab": (C.c_int, [_I, _I, _I, _I, _P, _I, _P, _P, _I, _P]),
     "ns_pack_weight": (C.c_int, [_P, _P, _I, _I, _P]),
     "ns_op_rmsnorm": (C.c_int, [_I, _I, _I, _P, _P, C.c_float, _P, _P]),
     "ns_op_attention_ws_bytes": (C.c_size_t, [C.POINTER(ns_model_desc), _I, _I]),
@@ -338,6 +339,11 @@ def ns_op_gemm(dtype: int, epi: int, M: int, N: int, K: int, A: int, B: int, Cp:
 
 def ns_op_gemm_packed(dtype: int, epi: int, M: int, N: int, K: int, A: int, B: int, Cp: int, stream=None) -> None:
     _check(lib().ns_op_gemm_packed(dtype, epi, M, N, K, A, B, Cp, _stream_ptr(stream)))
+
+
+def ns_op_gemm_slab(epi: int, M: int, N: int, K: int, A: int, a_rows: int, B: int, Cp: int, c_rows: int,
+                    stream=None) -> None:
+    _check(lib().ns_op_gemm_slab(epi, M, N, K, A, a_rows, B, Cp, c_rows, _stream_ptr(stream)))
 
 
 def ns_op_rmsnorm(dtype: int, n_rows: int, hidden: int, x: int, gain: int, eps: float, out: int, stream=None) -> None:

@@ -395,6 +395,19 @@ int ns_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, cons
 int ns_op_gemm_packed(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A,
                       const void* B, void* C, void* stream);
 
+/* The same projection (bf16) with every operand in the layout a bf16
+ * engine's step keeps (NanoFlow review, operator table: the dense class):
+ * A K-slab-major with a_rows (>= M) rows per 32-column slab block, element
+ * (m, k) at ((k / 32) * a_rows + m) * 32 + k % 32; B K-slab-major as for
+ * ns_op_gemm_packed; for NS_EPI_SILU, C (bf16) K-slab-major over its N
+ * columns with c_rows (>= M) rows per block (N % 32 == 0); for NS_EPI_STORE
+ * and NS_EPI_RESID, C fp32 [M, N] row-major (c_rows unused).  ns_pack_weight
+ * of a row-major [a_rows, K] matrix gives such an A.  Errors: NS_EINVAL (bad
+ * epilogue or sizes, null pointer, a_rows or c_rows < M), NS_ESHAPE
+ * (K % 32 != 0). */
+int ns_op_gemm_slab(int32_t epi, int32_t M, int32_t N, int32_t K, const void* A, int32_t a_rows, const void* B,
+                    void* C, int32_t c_rows, void* stream);
+
 /* RMSNorm of each row (nanoserve notes, changes table: the fused RMSNorm;
  * the final norm in front of the LM head): out[r] = x[r] / sqrt(mean(x[r]^2)
  * + eps) * gain, computed in fp32 and stored as dtype.  x: device fp32

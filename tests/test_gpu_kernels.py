@@ -86,6 +86,61 @@ def test_gemm_kslab_major_weights_equal_row_major(M, N, K, epi):
     assert torch.equal(C1.cpu(), C2.cpu())
 
 
+SLAB_SHAPES = [(1, 64, 64), (5, 160, 96), (17, 1152, 896), (33, 256, 4864), (64, 64, 256), (100, 512, 160),
+               (130, 384, 512), (256, 896, 4864), (257, 640, 1024), (32, 4864, 896), (300, 512, 1024),
+               (2048, 1024, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", SLAB_SHAPES)
+@pytest.mark.parametrize("epi", [ns.NS_EPI_STORE, ns.NS_EPI_RESID, ns.NS_EPI_SILU])
+def test_gemm_slab_layouts_equal_row_major(M, N, K, epi):
+    """The projections as a bf16 step runs them -- A and the SwiGLU output
+    K-slab-major with slab blocks of more rows than the launch's (an odd
+    count), the weights K-slab-major -- give the row-major result bit for bit
+    in every regime, read only A's first M rows of each block and leave the
+    output blocks' other rows untouched."""
+    from decode_step_06_amd.runner import pack_kslab_host
+    say(f"gemm slab layouts M={M} N={N} K={K} epi={epi}")
+    rng = np.random.default_rng(7 * M + N + K + epi)
+    a_rows, c_rows = M | 1 if M % 2 == 0 else M + 2, M + 3
+    A = _bf16_grid(rng.standard_normal((M, K))).cuda()
+    # rows past M hold values that would change the result if read
+    Apad = torch.cat([A, _bf16_grid(rng.standard_normal((a_rows - M, K)) * 1e3).cuda()])
+    As = torch.empty_like(Apad)
+    ns.ns_pack_weight(Apad.data_ptr(), As.data_ptr(), a_rows, K)
+    Bn = 2 * N if epi == ns.NS_EPI_SILU else N
+    Bp = torch.from_numpy(pack_kslab_host(_bf16_grid(rng.standard_normal((Bn, K)) * 0.05).view(torch.int16).numpy()))
+    Bp = Bp.view(torch.bfloat16).cuda()
+    if epi == ns.NS_EPI_SILU:
+        ref = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+        sentinel = torch.tensor(12345.0, dtype=torch.bfloat16)
+        got = torch.full((N // 32 * c_rows * 32,), float(sentinel), dtype=torch.bfloat16, device="cuda")
+    else:
+        ref = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).cuda()
+        got = ref.clone()
+    ns.ns_op_gemm_packed(ns.NS_BF16, epi, M, N, K, A.data_ptr(), Bp.data_ptr(), ref.data_ptr())
+    ns.ns_op_gemm_slab(epi, M, N, K, As.data_ptr(), a_rows, Bp.data_ptr(), got.data_ptr(), c_rows)
+    torch.cuda.synchronize()
+    if epi == ns.NS_EPI_SILU:
+        blocks = got.cpu().view(N // 32, c_rows, 32)
+        unpacked = blocks[:, :M, :].permute(1, 0, 2).reshape(M, N)
+        assert torch.equal(unpacked.view(torch.int16), ref.cpu().view(torch.int16))
+        assert torch.equal(blocks[:, M:, :], torch.full_like(blocks[:, M:, :], float(sentinel)))
+    else:
+        assert torch.equal(got.cpu(), ref.cpu())
+
+
+def test_gemm_slab_rejects_bad_arguments():
+    x = torch.zeros((64 * 64,), dtype=torch.bfloat16, device="cuda")
+    for args in ((3, 4, 32, 64, 4), (ns.NS_EPI_STORE, 4, 32, 48, 4), (ns.NS_EPI_STORE, 4, 32, 64, 3),
+                 (ns.NS_EPI_SILU, 4, 48, 64, 4)):
+        epi, M, N, K, a_rows = args
+        with pytest.raises(ns.NSError):
+            ns.ns_op_gemm_slab(epi, M, N, K, x.data_ptr(), a_rows, x.data_ptr(), x.data_ptr(), M)
+    with pytest.raises(ns.NSError):  # the SwiGLU output's blocks must hold M rows
+        ns.ns_op_gemm_slab(ns.NS_EPI_SILU, 4, 32, 64, x.data_ptr(), 4, x.data_ptr(), x.data_ptr(), 3)
+
+
 def test_pack_weight_rejects_bad_shapes():
     x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
     y = torch.zeros_like(x)
