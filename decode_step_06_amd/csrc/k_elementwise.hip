@@ -91,6 +91,18 @@ template <> struct Gain4<bf16_t> {
   }
 };
 
+// Four consecutive outputs in one store (8 bytes of bf16, 16 of fp32); p is
+// aligned to four elements.
+template <typename T> struct Store4;
+template <> struct Store4<float> {
+  __device__ static __forceinline__ void store(float* p, f32x4_t v) { *(f32x4_t*)p = v; }
+};
+template <> struct Store4<bf16_t> {
+  __device__ static __forceinline__ void store(bf16_t* p, f32x4_t v) {
+    *(uint2*)p = uint2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  }
+};
+
 template <typename T, int CH, int NT, int S>
 __device__ __forceinline__ void rmsnorm_reduce_row(float* __restrict__ xr, const float* __restrict__ pr,
                                                    long slice_stride, const T* __restrict__ g, T* __restrict__ h,
@@ -134,10 +146,12 @@ __device__ __forceinline__ void rmsnorm_reduce_row(float* __restrict__ xr, const
   for (int c = 0; c < CH; ++c) {
     const int i4 = threadIdx.x + c * NT;
     if (i4 < H4) {
-      // 4 consecutive columns from a multiple of 4: consecutive in either layout
-      const long o = act_idx(t, 4 * i4, H, hs);
+      // 4 consecutive columns from a multiple of 4: consecutive (and aligned
+      // to 4) in either layout
+      f32x4_t y;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Elem<T>::store(h, o + e, v[c][e] * r * gv[c][e]);
+      for (int e = 0; e < 4; ++e) y[e] = v[c][e] * r * gv[c][e];
+      Store4<T>::store(h + act_idx(t, 4 * i4, H, hs), y);
     }
   }
 }
