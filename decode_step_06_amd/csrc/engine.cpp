@@ -385,13 +385,14 @@ int upload_meta(ns_engine* e, const ns_batch* b, int rows, const ns_sched& sc, h
 
 // bf16 models keep the projections' bf16 inputs (h, the attention output o
 // and the SwiGLU activation) K-slab-major, each 32-column slab a contiguous
-// block of max_tokens rows: the layout of the weights, so that a GEMM's
-// 16-row load of one slab reads 1 KB contiguous instead of 16 separate 64-byte
-// pieces (80-layer 70B-shaped step, a timing probe of the GEMMs alone:
-// 54.5 -> 53.3 ms).  fp32 models stay row-major.
-// Steps of at most kPackMinRows rows keep them row-major: their projections
-// load one 16-row fragment per k-step, which the layout cannot widen, and the
-// loads keep their constant offsets.
+// block of slab_rows(max_tokens) rows: the layout of the weights, so that a
+// GEMM's 16-row load of one slab reads 1 KB contiguous instead of 16
+// separate 64-byte pieces (measured on MI355X, one box, same bits: the
+// 80-layer 70B-shaped step 54.1 -> 51.9 ms, the 2048-row layer 3.62 -> 3.55
+// ms, the 0.5B-shaped mix at 64 rows 1.565 -> 1.371 ms).  fp32 models stay
+// row-major.  Steps of at most kPackMinRows rows keep them row-major too:
+// their projections load one 16-row fragment per k-step, which the layout
+// cannot widen, and the row-major loads keep their constant offsets.
 constexpr int kPackMinRows = 16;
 int act_slab_rows(const ns_engine* e, int n_tok) {
   return e->d.dtype == NS_BF16 && n_tok > kPackMinRows ? slab_rows(e->max_tokens) : 0;
