@@ -774,8 +774,9 @@ static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B,
   // k-steps in flight, as registers allow (1024-thread workgroups get 128
   // VGPRs per lane); with at most 3 fragments per k-step, 16 (192 VGPRs),
   // so a wavefront's share of a split (the down projection at 32 rows: 10
-  // k-steps) is one round of loads
-  constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 3 ? 16 : ((MF + NB) <= 4 ? 8 : 4));
+  // k-steps) is one round of loads; up to 6 fragments, 8 (the 33-64-row
+  // projections: the 0.5B-shaped mix at 64 rows 1.367 -> 1.341 ms against 4)
+  constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 3 ? 16 : ((MF + NB) <= 6 ? 8 : 4));
   const unsigned grid = (unsigned)((N + 16 * NF - 1) / (16 * NF) * splits);
 #define NS_GEMV_LAUNCH(LAY_)                                                                             \
   hipLaunchKernelGGL((gemv_bf16_kernel<MF, NF, NW, U, EPI, bf16_t, LAY_>), dim3(grid), dim3(64 * NW), 0, st, \
