@@ -163,6 +163,17 @@ def test_engine_create_rejects_bad_arguments_without_a_gpu():
     finally:
         ns.ns_kv_destroy(kv)
     assert ns.lib().ns_engine_destroy(None) == ns.NS_OK   # releasing no engine is a no-op
+    # the slab-layout projection checks its arguments before any launch (the
+    # pointers below are never dereferenced)
+    L, fake = ns.lib(), 4096
+    assert L.ns_op_gemm_slab(3, 4, 32, 64, fake, 4, fake, fake, 4, None) == ns.NS_EINVAL      # epilogue
+    assert L.ns_op_gemm_slab(ns.NS_EPI_STORE, -1, 32, 64, fake, 4, fake, fake, 4, None) == ns.NS_EINVAL
+    assert L.ns_op_gemm_slab(ns.NS_EPI_STORE, 0, 32, 64, None, 0, None, None, 0, None) == ns.NS_OK  # empty
+    assert L.ns_op_gemm_slab(ns.NS_EPI_STORE, 4, 32, 64, None, 4, fake, fake, 4, None) == ns.NS_EINVAL
+    assert L.ns_op_gemm_slab(ns.NS_EPI_STORE, 4, 32, 48, fake, 4, fake, fake, 4, None) == ns.NS_ESHAPE
+    assert L.ns_op_gemm_slab(ns.NS_EPI_STORE, 4, 32, 64, fake, 3, fake, fake, 4, None) == ns.NS_EINVAL  # a_rows
+    assert L.ns_op_gemm_slab(ns.NS_EPI_SILU, 4, 48, 64, fake, 4, fake, fake, 4, None) == ns.NS_EINVAL   # N % 32
+    assert L.ns_op_gemm_slab(ns.NS_EPI_SILU, 4, 32, 64, fake, 4, fake, fake, 3, None) == ns.NS_EINVAL   # c_rows
     rc = ns.lib().ns_op_gemm(ns.NS_BF16, 0, 4, 4, 30, None, None, None, None)
     assert rc == ns.NS_EINVAL  # null matrices are checked first
     bad = ns.model_desc(TINY)
