@@ -772,11 +772,13 @@ static void run_gemv(int M, int N, int K, const void* A, int lda, const void* B,
                      hipStream_t st, int pk, int splits = 1, long slice_stride = 0) {
   constexpr int NB = NF * (EPI == EPI_SILU_MUL ? 2 : 1);
   // k-steps in flight, as registers allow (1024-thread workgroups get 128
-  // VGPRs per lane); with at most 3 fragments per k-step, 16 (192 VGPRs),
-  // so a wavefront's share of a split (the down projection at 32 rows: 10
-  // k-steps) is one round of loads; up to 6 fragments, 8 (the 33-64-row
-  // projections: the 0.5B-shaped mix at 64 rows 1.367 -> 1.341 ms against 4)
-  constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 3 ? 16 : ((MF + NB) <= 6 ? 8 : 4));
+  // VGPRs per lane); with at most 4 fragments per k-step, 16 (up to 256
+  // VGPRs), so a wavefront's share of a split (the down projection at 32
+  // rows: 10 k-steps) or of the gate-up projection at 17-32 rows (14) is one
+  // round of loads (the 0.5B-shaped mix at 32 rows 1.129 -> 1.118 ms against
+  // 8 for 4 fragments); up to 6 fragments, 8 (the 33-64-row projections: at
+  // 64 rows 1.367 -> 1.341 ms against 4)
+  constexpr int U = NW >= 16 ? ((MF + NB) <= 4 ? 4 : 2) : ((MF + NB) <= 4 ? 16 : ((MF + NB) <= 6 ? 8 : 4));
   const unsigned grid = (unsigned)((N + 16 * NF - 1) / (16 * NF) * splits);
 #define NS_GEMV_LAUNCH(LAY_)                                                                             \
   hipLaunchKernelGGL((gemv_bf16_kernel<MF, NF, NW, U, EPI, bf16_t, LAY_>), dim3(grid), dim3(64 * NW), 0, st, \
