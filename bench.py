@@ -1033,7 +1033,9 @@ def dense_leg_isolated():
     (no GPU fault reported, cause not found); run apart, such a crash costs
     this leg's entries instead of the whole line.  The child's log and any
     fault trace go to this process's stderr; its JSON comes back on stdout."""
-    return run_child_leg([sys.executable, os.path.abspath(__file__), "--child-leg", "dense"], "dense-batch")
+    # the leg takes about a minute; a child that hangs must not hold the line
+    return run_child_leg([sys.executable, os.path.abspath(__file__), "--child-leg", "dense"], "dense-batch",
+                         timeout=600)
 
 
 def run_child_leg(cmd, name, timeout=1200):
