@@ -751,14 +751,18 @@ static void run_big(int M, int N, int K, const void* A, int lda, const void* B, 
   constexpr int OUT_BN = (EPI == EPI_SILU_MUL) ? 128 : 256;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + OUT_BN - 1) / OUT_BN);
   const dim3 grid((unsigned)tiles, (unsigned)splits);
-  if (M <= BM) {  // one row tile: each weight slab is read once
+  // 256-row tiles: 8 wavefronts in two ping-pong groups, the same bits as
+  // 4 (measured on MI355X at 2048 rows of the 70B shape: QKV 383.6 -> 369.5,
+  // O 261 -> 230.5, gate-up 1693 -> 1665, down 868 -> 847 us; at one row tile
+  // of 256 rows, once A is K-slab-major, the 80-layer step 52.0 -> 51.2 ms,
+  // where with a row-major A the gate-up projection had lost 7%)
+  if (BM == 256 && M <= BM) {  // one row tile: each weight slab is read once (non-temporal)
+    hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, 256, 1, 8, 1>), grid, dim3(512), 0, st, (const bf16_t*)A, lda,
+                       (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk);
+  } else if (M <= BM) {
     hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 1>), grid, dim3(256), 0, st, (const bf16_t*)A, lda,
                        (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk);
   } else if constexpr (BM == 256) {
-    // several row tiles: 8 wavefronts in two ping-pong groups (measured on
-    // MI355X at 2048 rows of the 70B shape: QKV 383.6 -> 369.5, O 261 ->
-    // 230.5, gate-up 1693 -> 1665, down 868 -> 847 us, the same bits; at one
-    // row tile of 256 rows the gate-up projection lost 7%)
     hipLaunchKernelGGL((gemm_big_kernel<EPI, bf16_t, BM, 0, 8, 1>), grid, dim3(512), 0, st, (const bf16_t*)A, lda,
                        (const bf16_t*)B, ldb, M, N, K, Cv, ldc, splits, slice_stride, pk);
   } else {
